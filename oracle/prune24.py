@@ -1,0 +1,360 @@
+"""CPU oracle for 2:4 structured-sparse GEMM and tile-vector-wise (TVW) sparsity.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It is plain, slow, numpy-only code
+written from the definitions below; it shares no code, table or helper with the
+HIP library, and it imports neither torch nor the package.
+
+Sources (the method's definition):
+  * "Accelerating Sparse Deep Neural Networks" (Mishra et al.), Abstract: a 2:4
+    pattern keeps 50% of the weights and the sparse matrix unit does twice the
+    dense math rate.
+  * NVIDIA A100 sparsity blog page (nvidia-a100-benchmarks), body text and its
+    (missing) Figure 1: in every run of four consecutive weights at least two
+    are zero; the survivors are stored in a compressed form with a small amount
+    of position metadata.
+  * "Accelerating Sparse DNNs Based on Tiled GEMM", Abstract, TL;DR and
+    Figure 3: tile-wise (TW) sparsity removes whole reduction-axis rows per GEMM
+    tile in global memory, and TVW applies 2:4 on top of it inside the tile.
+
+Readings where the pages are silent (each one is listed in the design notes):
+  * criterion: magnitude; order: key descending, index ascending (ties go to
+    the lower index); key = IEEE bit pattern with the sign bit cleared, read as
+    an unsigned integer (monotone in |w|, -0 == +0, NaN above +Inf).
+  * groups of four run along K (the reduction axis), aligned at k = 0.
+  * fp32 masters are pruned first, then the kept values are rounded to bf16
+    with round-to-nearest-even (NaN -> quiet NaN 0x7FC0 with the input's sign).
+  * canonical metadata: row-major bit stream per row, value s (s = 0..K/2-1)
+    stores the 2-bit in-group position of that value at bits [2s, 2s+2);
+    32-bit words, little endian, ceil(K/32) words per row, unused bits zero.
+  * device metadata/value layout: the operand order of the gfx950 sparse MFMA
+    32x32x32 bf16 instruction (defined in ``to_device_layout``).
+  * TVW: tile t = output rows [t*tile_m, (t+1)*tile_m); column score = fp64
+    sum of |W| over the tile's rows in ascending row order; keep the keep_k
+    columns with the largest score (ties -> lower k), listed ascending; then
+    2:4 along the compacted axis.
+  * GEMM tolerance: |y - y_ref| <= 1e-3 * (|W|.|X|)_ij on the fp32 result; a
+    bf16 result also gets the half-ulp of its final rounding,
+    2^-8 * (|y_ref| + 1e-3 * (|W|.|X|)).
+
+Parity pins for every function here live in ``tests/test_oracle_*.py``.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+BF16_QNAN = 0x7FC0
+TOL_REL = 1e-3          # elementwise bound factor on (|W|.|X|)
+BF16_HALF_ULP = 2.0 ** -8
+
+
+# ----------------------------------------------------------------------------
+# bf16 helpers (bf16 values are carried as uint16 bit patterns)
+# ----------------------------------------------------------------------------
+def bf16_rne(x: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bits, round to nearest, ties to even.
+
+    Written from the rounding definition: add half of the dropped range minus
+    one plus the lowest kept bit, then drop the low 16 bits.  NaN maps to the
+    quiet NaN 0x7FC0 carrying the input's sign.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint32)
+    nan = np.isnan(x)
+    sign = ((u >> 31) & 1).astype(np.uint32) << 15
+    r = np.where(nan, sign | BF16_QNAN, r)
+    return r.astype(np.uint16)
+
+
+def bf16_to_f64(b: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float64 (exact)."""
+    b = np.asarray(b, dtype=np.uint16)
+    with np.errstate(invalid="ignore"):
+        return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_to_f32(b: np.ndarray) -> np.ndarray:
+    b = np.asarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# 2:4 magnitude selection (blog page body text; criterion and tie rule above)
+# ----------------------------------------------------------------------------
+def _as_bits(W: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(W, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    if dtype == "bf16":
+        return np.ascontiguousarray(W, dtype=np.uint16).astype(np.uint64)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+def magnitude_key(W: np.ndarray, dtype: str) -> np.ndarray:
+    """Unsigned magnitude key: the bit pattern with the sign bit cleared."""
+    bits = _as_bits(W, dtype)
+    mask = 0x7FFFFFFF if dtype == "f32" else 0x7FFF
+    return bits & mask
+
+
+def select_24(W: np.ndarray, dtype: str = "f32") -> np.ndarray:
+    """Kept in-group positions, shape (M, K/4, 2), ascending within each group.
+
+    Each group of four along K is ordered by (key descending, index ascending)
+    with a stable sort, and the first two positions are kept.
+    """
+    W = np.asarray(W)
+    if W.ndim != 2:
+        raise ValueError("W must be 2-D (M x K)")
+    M, K = W.shape
+    if K % 4:
+        raise ValueError("K must be a multiple of 4")
+    key = magnitude_key(W, dtype).reshape(M, K // 4, 4).astype(np.int64)
+    order = np.argsort(-key, axis=-1, kind="stable")
+    kept = np.sort(order[..., :2], axis=-1)
+    return kept.astype(np.int64)
+
+
+def prune_24(W: np.ndarray, dtype: str = "f32") -> np.ndarray:
+    """Dense pruned copy: dropped entries become +0 (bit pattern 0), kept entries are unchanged."""
+    W = np.asarray(W)
+    M, K = W.shape
+    kept = select_24(W, dtype)
+    mask = np.zeros((M, K // 4, 4), dtype=bool)
+    np.put_along_axis(mask, kept, True, axis=-1)
+    mask = mask.reshape(M, K)
+    if dtype == "f32":
+        out = np.where(mask, np.asarray(W, dtype=np.float32), np.float32(0.0))
+        return out.astype(np.float32)
+    return np.where(mask, np.asarray(W, dtype=np.uint16), np.uint16(0)).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------
+# Compressed representation (blog page, Figure 1 reference; layout reading above)
+# ----------------------------------------------------------------------------
+def meta_words_per_row(K: int) -> int:
+    return (K + 31) // 32
+
+
+def compress_24(W: np.ndarray, dtype: str = "f32"):
+    """Returns (values uint16 [M, K/2] bf16 bits, meta uint32 [M, ceil(K/32)]).
+
+    values[m, 2g+j] = bf16(W[m, 4g + pos_j]) with pos_0 < pos_1 the kept
+    positions of group g; meta holds pos of value s at bits [2s, 2s+2) of row
+    m's bit stream.
+    """
+    W = np.asarray(W)
+    M, K = W.shape
+    kept = select_24(W, dtype)                      # (M, G, 2)
+    G = K // 4
+    grp = W.reshape(M, G, 4)
+    vals = np.take_along_axis(grp, kept, axis=-1).reshape(M, K // 2)
+    if dtype == "f32":
+        values = bf16_rne(vals.astype(np.float32))
+    else:
+        values = vals.astype(np.uint16)
+    pos = kept.reshape(M, K // 2).astype(np.uint64)  # position of value s
+    nw = meta_words_per_row(K)
+    meta = np.zeros((M, nw), dtype=np.uint64)
+    for s in range(K // 2):
+        bit = 2 * s
+        meta[:, bit // 32] |= pos[:, s] << np.uint64(bit % 32)
+    return values.astype(np.uint16), meta.astype(np.uint32)
+
+
+def meta_positions(meta: np.ndarray, K: int) -> np.ndarray:
+    """Decode canonical metadata into in-group positions, shape (M, K/2)."""
+    meta = np.asarray(meta, dtype=np.uint32).astype(np.uint64)
+    M = meta.shape[0]
+    pos = np.zeros((M, K // 2), dtype=np.int64)
+    for s in range(K // 2):
+        bit = 2 * s
+        pos[:, s] = ((meta[:, bit // 32] >> np.uint64(bit % 32)) & np.uint64(3)).astype(np.int64)
+    return pos
+
+
+def decompress_24(values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:
+    """Dense bf16 bits [M, K]: each value goes back to 4g + pos; zeros elsewhere."""
+    values = np.asarray(values, dtype=np.uint16)
+    M = values.shape[0]
+    pos = meta_positions(meta, K)
+    out = np.zeros((M, K), dtype=np.uint16)
+    s = np.arange(K // 2)
+    cols = 4 * (s // 2)[None, :] + pos
+    rows = np.repeat(np.arange(M)[:, None], K // 2, axis=1)
+    out[rows, cols] = values
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Device layout: operand order of the gfx950 sparse MFMA (32x32x32, bf16)
+# ----------------------------------------------------------------------------
+# The instruction multiplies a 32-row x 32-column (logical) sparse A by a dense
+# 32 x 32 B.  Lane L (0..63) holds, for row r = L mod 32, the 8 compressed
+# values whose logical columns are 16*(L div 32) .. +16, and a 16-bit index
+# with 4 bits per group (position of the group's first kept value in bits
+# [0,2), second in [2,4)); the instruction's abid operand picks the low (0) or
+# high (1) 16 bits of the 32-bit index register.
+#
+# Device values: blocks of 32 rows (rows >= M are zero), K-steps of 32 logical
+# columns.  Block (rb, s) is 64 lanes x 8 bf16 = 1 KiB; lane L's 8 values are
+# values[32*rb + L%32, 16*s + 8*(L//32) .. +8].  Block order: rb-major, s-minor.
+# Device metadata: per 32-row block rb and K-pair t (64 logical columns), 64
+# uint32; lane L's word is (positions of row 32*rb + L%32, logical columns
+# 64t + 16*(L//32) .. +16) in bits [0,16) and the same for columns
+# 64t + 32 + 16*(L//32) .. +16 in bits [16,32).  Within 16 bits, the position
+# of the i-th compressed value sits at bits [2i, 2i+2) -- the same bit-stream
+# order as the canonical layout.  Padded rows get position pattern 0x4444.
+def device_rows(M: int) -> int:
+    return ((M + 31) // 32) * 32
+
+
+def to_device_layout(values: np.ndarray, meta: np.ndarray, K: int):
+    """Canonical (values [M, K/2], meta [M, K/32]) -> device (values flat u16, meta flat u32).
+
+    Requires K % 64 == 0.  Index names: rb row block, r row in block, s K-step
+    of 32 logical columns, t K-pair (64 logical columns), h lane half (L // 32),
+    half = which K-step of the pair (abid), i compressed value within a lane.
+    """
+    if K % 64:
+        raise ValueError("device layout needs K % 64 == 0")
+    values = np.asarray(values, dtype=np.uint16)
+    M = values.shape[0]
+    Mp = device_rows(M)
+    RB, S, T = Mp // 32, K // 32, K // 64
+    vpad = np.zeros((Mp, K // 2), dtype=np.uint16)
+    vpad[:M] = values
+    pos = np.tile(np.array([0, 1], dtype=np.uint64), (Mp, K // 4))   # padded rows: 0x4 per group
+    pos[:M] = meta_positions(meta, K).astype(np.uint64)
+    # values: row = 32*rb + r, compressed column = 16*s + 8*h + i  ->  [rb, s, L = 32*h + r, i]
+    dv = vpad.reshape(RB, 32, S, 2, 8).transpose(0, 2, 3, 1, 4).reshape(RB, S, 64, 8)
+    # meta: compressed column = 32*t + 16*half + 8*h + i  ->  word[rb, t, L] bit 16*half + 2*i
+    p6 = pos.reshape(RB, 32, T, 2, 2, 8).transpose(0, 2, 4, 1, 3, 5)   # rb, t, h, r, half, i
+    shifts = (16 * np.arange(2)[:, None] + 2 * np.arange(8)[None, :]).astype(np.uint64)
+    words = (p6 << shifts).sum(axis=(-2, -1), dtype=np.uint64)           # disjoint bits: sum == or
+    return dv.reshape(-1).copy(), words.reshape(RB, T, 64).astype(np.uint32).reshape(-1)
+
+
+def from_device_layout(dvals: np.ndarray, dmeta: np.ndarray, M: int, K: int):
+    """Inverse of ``to_device_layout`` (drops padded rows)."""
+    Mp = device_rows(M)
+    RB, S, T = Mp // 32, K // 32, K // 64
+    dv = np.asarray(dvals, dtype=np.uint16).reshape(RB, S, 2, 32, 8)          # rb, s, h, r, i
+    values = dv.transpose(0, 3, 1, 2, 4).reshape(Mp, K // 2)
+    w = np.asarray(dmeta, dtype=np.uint32).reshape(RB, T, 2, 32).astype(np.uint64)  # rb, t, h, r
+    shifts = (16 * np.arange(2)[:, None] + 2 * np.arange(8)[None, :]).astype(np.uint64)
+    p6 = (w[..., None, None] >> shifts) & np.uint64(3)                             # rb, t, h, r, half, i
+    pos = p6.transpose(0, 3, 1, 4, 2, 5).reshape(Mp, K // 2)                       # rb, r, t, half, h, i
+    meta = np.zeros((Mp, meta_words_per_row(K)), dtype=np.uint64)
+    for s in range(K // 2):
+        meta[:, (2 * s) // 32] |= pos[:, s] << np.uint64((2 * s) % 32)
+    return values[:M].copy(), meta[:M].astype(np.uint32)
+
+
+# ----------------------------------------------------------------------------
+# Tile-vector-wise sparsity ("Accelerating Sparse DNNs Based on Tiled GEMM",
+# Abstract and Figure 3: TW drop at the tile level, then 2:4 inside the tile)
+# ----------------------------------------------------------------------------
+def tvw_num_tiles(M: int, tile_m: int) -> int:
+    return (M + tile_m - 1) // tile_m
+
+
+def tvw_scores(W: np.ndarray, tile_m: int) -> np.ndarray:
+    """fp64 column L1 score per tile, [T, K]; rows summed one at a time in ascending order."""
+    W = np.asarray(W, dtype=np.float32)
+    M, K = W.shape
+    T = tvw_num_tiles(M, tile_m)
+    out = np.zeros((T, K), dtype=np.float64)
+    for t in range(T):
+        acc = np.zeros(K, dtype=np.float64)
+        for m in range(t * tile_m, min(M, (t + 1) * tile_m)):
+            acc = acc + np.abs(W[m].astype(np.float64))
+        out[t] = acc
+    return out
+
+
+def tvw_select(W: np.ndarray, tile_m: int, keep_k: int) -> np.ndarray:
+    """Kept column indices per tile, int32 [T, keep_k], ascending.
+
+    Order: score descending, then column ascending (stable sort of -score).
+    """
+    M, K = np.asarray(W).shape
+    if not (0 < keep_k <= K) or keep_k % 4:
+        raise ValueError("keep_k must be in (0, K] and a multiple of 4")
+    sc = tvw_scores(W, tile_m)
+    order = np.argsort(-sc, axis=1, kind="stable")
+    kept = np.sort(order[:, :keep_k], axis=1)
+    return kept.astype(np.int32)
+
+
+def tvw_compress(W: np.ndarray, tile_m: int, keep_k: int):
+    """Returns (kept int32 [T, keep_k], values u16 [M, keep_k/2], meta u32 [M, ceil(keep_k/32)])."""
+    W = np.asarray(W, dtype=np.float32)
+    M, K = W.shape
+    kept = tvw_select(W, tile_m, keep_k)
+    Wc = np.zeros((M, keep_k), dtype=np.float32)
+    for t in range(kept.shape[0]):
+        r0, r1 = t * tile_m, min(M, (t + 1) * tile_m)
+        Wc[r0:r1] = W[r0:r1][:, kept[t]]
+    values, meta = compress_24(Wc, "f32")
+    return kept, values, meta
+
+
+def tvw_decompress(kept: np.ndarray, values: np.ndarray, meta: np.ndarray, M: int, K: int,
+                   tile_m: int) -> np.ndarray:
+    """Dense bf16 bits [M, K] with the compacted columns scattered back."""
+    keep_k = kept.shape[1]
+    comp = decompress_24(values, meta, keep_k)          # [M, keep_k]
+    out = np.zeros((M, K), dtype=np.uint16)
+    for t in range(kept.shape[0]):
+        r0, r1 = t * tile_m, min(M, (t + 1) * tile_m)
+        out[r0:r1, kept[t]] = comp[r0:r1]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# GEMM reference and bound (fp64; every bf16 x bf16 product is exact in fp64)
+# ----------------------------------------------------------------------------
+def gemm_ref(Wd: np.ndarray, X: np.ndarray, rows=None):
+    """(y_ref, bound) for Y = W X; Wd, X are bf16 bits; rows optionally selects output rows."""
+    Wf = bf16_to_f64(Wd if rows is None else np.asarray(Wd)[rows])
+    Xf = bf16_to_f64(X)
+    return Wf @ Xf, np.abs(Wf) @ np.abs(Xf)
+
+
+def spmm_ref_sparse(values: np.ndarray, meta: np.ndarray, K: int, X: np.ndarray, rows=None):
+    """Sparse route: y[m, :] = sum_s values[m, s] * X[4*(s//2) + pos[m, s], :] in fp64."""
+    values = np.asarray(values, dtype=np.uint16)
+    if rows is None:
+        rows = np.arange(values.shape[0])
+    rows = np.asarray(rows)
+    pos = meta_positions(np.asarray(meta)[rows], K)
+    Xf = bf16_to_f64(X)
+    s = np.arange(K // 2)
+    y = np.zeros((len(rows), Xf.shape[1]), dtype=np.float64)
+    for i, m in enumerate(rows):
+        ks = 4 * (s // 2) + pos[i]
+        y[i] = bf16_to_f64(values[m]) @ Xf[ks]
+    return y
+
+
+def tolerance(y_ref: np.ndarray, bound: np.ndarray, out_dtype: str) -> np.ndarray:
+    if out_dtype == "f32":
+        return TOL_REL * bound
+    if out_dtype == "bf16":
+        return TOL_REL * bound + BF16_HALF_ULP * (np.abs(y_ref) + TOL_REL * bound)
+    raise ValueError(out_dtype)
+
+
+def check(y: np.ndarray, y_ref: np.ndarray, bound: np.ndarray, out_dtype: str):
+    """(ok, worst err/tol ratio).  Non-finite outputs always fail."""
+    y = np.asarray(y, dtype=np.float64)
+    tol = tolerance(y_ref, bound, out_dtype)
+    err = np.abs(y - y_ref)
+    finite = np.isfinite(y).all()
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tol > 0, err / tol, np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return bool(finite and worst <= 1.0), worst
