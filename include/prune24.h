@@ -1,0 +1,196 @@
+/*
+ * prune24.h -- C ABI of libprune24.so: 2:4 structured-sparse GEMM and
+ * tile-vector-wise (TVW) sparsity on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes
+ *   - 2:4 pattern: in every run of four consecutive weights along the
+ *     reduction axis K, two are zero, so half the weights and half the math
+ *     remain (NVIDIA A100 sparsity blog page, body text; "Accelerating Sparse
+ *     Deep Neural Networks", Abstract).
+ *   - Compressed representation: the kept values plus a small per-value
+ *     position code (same blog page, Figure 1 -- its drawing is not on the
+ *     page, so the bit layout below is this library's own).
+ *   - TVW: per GEMM tile of output rows, whole K columns are dropped at the
+ *     global-memory level and 2:4 is applied to the columns that remain
+ *     ("Accelerating Sparse DNNs Based on Tiled GEMM", Abstract and Figure 3).
+ *
+ * Conventions (all entry points)
+ *   - W is M x K (output features x input features), X is K x N (input
+ *     features x tokens), Y = W X is M x N.  All matrices are row-major with a
+ *     leading dimension (ld*) counted in elements.  2:4 groups run along K,
+ *     aligned at k = 0.
+ *   - Every pointer argument is a DEVICE pointer, except where stated.  The
+ *     caller allocates and owns every buffer; the library allocates nothing and
+ *     keeps no pointer after a call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Every call only
+ *     enqueues work on that stream and never synchronises; the caller keeps
+ *     the buffers alive until the stream has passed the work.
+ *   - Arguments are validated first; on any error the status is returned and
+ *     nothing is enqueued.  P24_ERR_HIP means a launch failed.  M == 0 or
+ *     N == 0 is a valid no-op.
+ *   - The library is stateless and thread-safe.
+ *
+ * Layouts of a compressed matrix (values are bf16, metadata uint32)
+ *   P24_LAYOUT_CANONICAL
+ *     values: M x K/2 row-major bf16; values[m][2g+j] is the j-th kept entry
+ *       (in ascending position order) of group g = k/4.
+ *     meta: M x ceil(K/32) row-major uint32; value s of row m (s = 0..K/2-1)
+ *       stores its position inside its group (0..3) at bits [2s, 2s+2) of the
+ *       row's little-endian bit stream.  Unused high bits are 0.
+ *   P24_LAYOUT_DEVICE (operand order of the gfx950 sparse MFMA
+ *     v_smfmac_f32_32x32x32_bf16; needs K % 64 == 0; Mp = M rounded up to 32)
+ *     values: (Mp/32) x (K/32) blocks of 64 x 8 bf16 (1 KiB), block (rb, s)
+ *       at element offset (rb*(K/32) + s)*512; lane L's 8 values are
+ *       canonical values[32*rb + L%32][16*s + 8*(L/32) .. +8].
+ *     meta: (Mp/32) x (K/64) blocks of 64 uint32, block (rb, t) at word offset
+ *       (rb*(K/64) + t)*64; lane L's word holds, for row 32*rb + L%32, the
+ *       positions of compressed columns 32*t + 8*(L/32) .. +8 in bits [0,16)
+ *       and of 32*t + 16 + 8*(L/32) .. +8 in bits [16,32), 2 bits per value
+ *       in value order.  Rows M..Mp-1 hold zero values and positions 0,1.
+ *
+ * Readings the pages leave open (magnitude criterion, tie order, rounding)
+ *   - Selection keeps the two entries of each group with the largest
+ *     magnitude key = the IEEE bit pattern with the sign cleared, read as an
+ *     unsigned integer; ties go to the lower index (so -0 ties +0, NaN ranks
+ *     above +Inf).
+ *   - fp32 inputs are selected on their fp32 bits, then the kept values are
+ *     rounded to bf16 to nearest-even (NaN -> 0x7FC0 with the input's sign).
+ */
+#ifndef PRUNE24_H
+#define PRUNE24_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define P24_API __attribute__((visibility("default")))
+#define PRUNE24_ABI_VERSION 1
+
+typedef int32_t p24_status;
+
+enum {
+  P24_OK = 0,
+  P24_ERR_NULL = -1,         /* a required pointer is NULL */
+  P24_ERR_SHAPE = -2,        /* negative size, ld too small, K % 4 != 0, bad tile/keep */
+  P24_ERR_ALIGN = -3,        /* pointer or leading dimension not aligned as required */
+  P24_ERR_DTYPE = -4,        /* unknown dtype code */
+  P24_ERR_UNSUPPORTED = -5,  /* valid request this build does not implement (e.g. K % 64) */
+  P24_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
+  P24_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required */
+  P24_ERR_LAYOUT = -8        /* unknown layout code, or layout not accepted here */
+};
+
+enum { P24_F32 = 0, P24_BF16 = 1 };                         /* element dtypes */
+enum { P24_LAYOUT_CANONICAL = 0, P24_LAYOUT_DEVICE = 1 };    /* compressed layouts */
+enum { P24_ALGO_AUTO = 0, P24_ALGO_SMFMAC = 1 };             /* spmm24 algorithms */
+
+/* ABI version of the loaded library (PRUNE24_ABI_VERSION). */
+P24_API int32_t prune24_abi_version(void);
+
+/* Human-readable text for a status code (static storage; never NULL). */
+P24_API const char* prune24_strerror(p24_status s);
+
+/* Bytes of the values / metadata buffers for an M x K matrix in `layout`
+ * (0 for an invalid request).  Host-only helpers; they touch no device. */
+P24_API size_t prune24_values_bytes(int64_t M, int64_t K, int32_t layout);
+P24_API size_t prune24_meta_bytes(int64_t M, int64_t K, int32_t layout);
+
+/*
+ * prune24_compress -- magnitude 2:4 selection + compression of W.
+ *   W        M x K, dtype w_dtype (P24_F32 or P24_BF16), leading dim ldw >= K.
+ *            Alignment: W 16 B aligned and ldw % 4 == 0 (fp32); 8 B and
+ *            ldw % 4 == 0 (bf16).
+ *   values   output, prune24_values_bytes(M, K, layout) bytes, 16 B aligned.
+ *   meta     output, prune24_meta_bytes(M, K, layout) bytes, 16 B aligned.
+ *   layout   P24_LAYOUT_CANONICAL (K % 4 == 0) or P24_LAYOUT_DEVICE (K % 64 == 0).
+ * Result is bit-exact and deterministic.
+ */
+P24_API p24_status prune24_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K,
+                                    int64_t ldw, void* values, void* meta, int32_t layout,
+                                    void* stream);
+
+/*
+ * prune24_decompress -- expand a compressed matrix back to dense bf16:
+ *   W_out[m][k] = the kept value at k, +0 elsewhere.  W_out is M x K bf16 with
+ *   leading dim ldo >= K, 2 B aligned.  Same layout rules as prune24_compress.
+ */
+P24_API p24_status prune24_decompress(const void* values, const void* meta, int32_t layout,
+                                      int64_t M, int64_t K, void* W_out, int64_t ldo,
+                                      void* stream);
+
+/*
+ * spmm24 -- Y = W X with W given compressed (2:4) and X dense bf16.
+ *   values, meta  compressed W in P24_LAYOUT_DEVICE (the layout the sparse MFMA
+ *                 reads directly; other layouts return P24_ERR_LAYOUT).
+ *   M, K          logical shape of W; K % 64 == 0 (else P24_ERR_UNSUPPORTED).
+ *   X             K x N bf16, leading dim ldx >= N, ldx % 8 == 0, 16 B aligned.
+ *   Y             M x N, y_dtype P24_F32 or P24_BF16 (round to nearest even),
+ *                 leading dim ldy >= N, naturally aligned.
+ *   algo          P24_ALGO_AUTO or P24_ALGO_SMFMAC (same kernel family).
+ * Products are exact in fp32 and accumulate in fp32.  The result is
+ * deterministic run to run (no atomics, fixed reduction order).
+ */
+P24_API p24_status spmm24(const void* values, const void* meta, int32_t layout, int64_t M,
+                          int64_t K, const void* X, int64_t ldx, int64_t N, void* Y,
+                          int32_t y_dtype, int64_t ldy, int32_t algo, void* stream);
+
+/*
+ * tvw_compress -- TVW selection and compression of fp32 W.
+ *   Tile t covers output rows [t*tile_m, min(M, (t+1)*tile_m)).  Its column
+ *   score is the fp64 sum over those rows, in ascending row order, of |W[m][k]|;
+ *   the keep_k columns with the largest score (ties -> lower k; scores compare
+ *   by their fp64 bit pattern, so NaN ranks highest) are kept, listed ascending
+ *   in kept[t][0..keep_k).  The tile's rows restricted to those columns are then
+ *   compressed 2:4 exactly as prune24_compress does, along the compacted axis.
+ *   W         M x K fp32 (w_dtype must be P24_F32), ldw % 4 == 0, 16 B aligned.
+ *   tile_m    > 0 and a multiple of 32.  keep_k: 0 < keep_k <= K, keep_k % 4 == 0
+ *             (% 64 for the device layout).
+ *   kept      output int32 [ceil(M/tile_m)][keep_k].
+ *   values, meta   output, sized as for an M x keep_k matrix in `layout`.
+ *   workspace device scratch of at least tvw_workspace_bytes(...) bytes,
+ *             8 B aligned; its contents on entry do not matter.
+ */
+P24_API size_t tvw_workspace_bytes(int64_t M, int64_t K, int64_t tile_m, int64_t keep_k);
+P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K,
+                                int64_t ldw, int64_t tile_m, int64_t keep_k, int32_t* kept,
+                                void* values, void* meta, int32_t layout, void* workspace,
+                                size_t ws_bytes, void* stream);
+
+/*
+ * spmm_tvw -- Y = W X for a TVW-compressed W: for output rows of tile t,
+ *   Y[m][n] = sum_j Wc[m][j] * X[kept[t][j]][n], with Wc the 2:4-compressed
+ *   M x keep_k matrix (P24_LAYOUT_DEVICE).  X rows are gathered by `kept`
+ *   (whole, contiguous N-slices).  Needs tile_m % 128 == 0 and keep_k % 64 == 0.
+ *   kept entries must lie in [0, K); the kernel clamps out-of-range entries
+ *   into that range (the result is then meaningless but no access leaves X).
+ *   Other arguments as for spmm24.
+ */
+P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, const void* meta,
+                            int32_t layout, int64_t M, int64_t K, int64_t tile_m,
+                            int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
+                            int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * Dense bf16 GEMM, the denominator of every speedup ("over the dense model",
+ * "Accelerating Sparse DNNs Based on Tiled GEMM", Abstract).  It runs the same
+ * tile loop as spmm24 with the dense MFMA v_mfma_f32_32x32x16_bf16.
+ *   gemm_bf16_pack: W (M x K bf16, ldw >= K, ldw % 8 == 0, 16 B aligned) ->
+ *     Wp in MFMA operand order: (Mp/32) x (K/16) blocks of 64 x 8 bf16, block
+ *     (rb, s) at element offset (rb*(K/16) + s)*512, lane L's 8 values are
+ *     W[32*rb + L%32][16*s + 8*(L/32) .. +8]; rows >= M are zero.  K % 64 == 0.
+ *   gemm_bf16: Y = W X from the packed Wp; X, Y as for spmm24.
+ */
+P24_API size_t gemm_bf16_packed_bytes(int64_t M, int64_t K);
+P24_API p24_status gemm_bf16_pack(const void* W, int64_t M, int64_t K, int64_t ldw, void* Wp,
+                                  void* stream);
+P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
+                             int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRUNE24_H */

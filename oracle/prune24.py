@@ -278,13 +278,16 @@ def tvw_scores(W: np.ndarray, tile_m: int) -> np.ndarray:
 def tvw_select(W: np.ndarray, tile_m: int, keep_k: int) -> np.ndarray:
     """Kept column indices per tile, int32 [T, keep_k], ascending.
 
-    Order: score descending, then column ascending (stable sort of -score).
+    Order: score descending, then column ascending (stable sort).  Scores are
+    non-negative, so comparing their fp64 bit patterns as unsigned integers is
+    the value order; it also gives NaN (sign cleared) a place above +Inf.
     """
     M, K = np.asarray(W).shape
     if not (0 < keep_k <= K) or keep_k % 4:
         raise ValueError("keep_k must be in (0, K] and a multiple of 4")
     sc = tvw_scores(W, tile_m)
-    order = np.argsort(-sc, axis=1, kind="stable")
+    key = sc.view(np.uint64)
+    order = np.argsort(np.iinfo(np.uint64).max - key, axis=1, kind="stable")
     kept = np.sort(order[:, :keep_k], axis=1)
     return kept.astype(np.int32)
 

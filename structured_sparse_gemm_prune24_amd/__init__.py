@@ -1,0 +1,292 @@
+"""Python binding of libprune24.so: 2:4 structured-sparse GEMM on AMD MI355X (gfx950).
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/prune24.h``; PyTorch provides
+device memory and the current HIP stream, nothing else.  If the library has
+not been built this module raises on first use -- there is no fallback.
+
+    import structured_sparse_gemm_prune24_amd as p24
+    c = p24.compress(W)                 # W: cuda fp32/bf16 [M, K]  (magnitude 2:4)
+    Y = p24.spmm24(c, X)                # X: cuda bf16 [K, N] -> Y bf16 [M, N]
+    t = p24.tvw_compress(W, 128, K // 2)
+    Y = p24.spmm_tvw(t, X)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from dataclasses import dataclass
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libprune24.so")
+HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "prune24.h")
+
+# status codes / enums (mirror include/prune24.h)
+P24_OK = 0
+P24_ERR_NULL = -1
+P24_ERR_SHAPE = -2
+P24_ERR_ALIGN = -3
+P24_ERR_DTYPE = -4
+P24_ERR_UNSUPPORTED = -5
+P24_ERR_HIP = -6
+P24_ERR_WORKSPACE = -7
+P24_ERR_LAYOUT = -8
+P24_F32, P24_BF16 = 0, 1
+P24_LAYOUT_CANONICAL, P24_LAYOUT_DEVICE = 0, 1
+P24_ALGO_AUTO, P24_ALGO_SMFMAC = 0, 1
+
+_c_i32, _c_i64, _c_size, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes)
+_SIGNATURES = {
+    "prune24_abi_version": (_c_i32, []),
+    "prune24_strerror": (ctypes.c_char_p, [_c_i32]),
+    "prune24_values_bytes": (_c_size, [_c_i64, _c_i64, _c_i32]),
+    "prune24_meta_bytes": (_c_size, [_c_i64, _c_i64, _c_i32]),
+    "prune24_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i32, _c_vp]),
+    "prune24_decompress": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
+    "spmm24": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
+                        _c_i64, _c_i32, _c_vp]),
+    "tvw_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64]),
+    "tvw_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp,
+                              _c_i32, _c_vp, _c_size, _c_vp]),
+    "spmm_tvw": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
+                          _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
+    "gemm_bf16_packed_bytes": (_c_size, [_c_i64, _c_i64]),
+    "gemm_bf16_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
+    "gemm_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
+}
+
+_LIB = None
+
+
+class P24Error(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: status {code} ({strerror(code)})")
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "or python structured_sparse_gemm_prune24_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def header_symbols() -> list[str]:
+    """Entry points declared with P24_API in include/prune24.h."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    return re.findall(r"P24_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def strerror(code: int) -> str:
+    return lib().prune24_strerror(code).decode()
+
+
+def _check(code: int, where: str):
+    if code != P24_OK:
+        raise P24Error(code, where)
+
+
+# ----------------------------------------------------------------------------
+# tensor plumbing
+# ----------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(dev):
+    torch = _torch()
+    return _c_vp(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _ptr(t):
+    return _c_vp(t.data_ptr())
+
+
+def _require_cuda(t, name):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a CUDA/HIP device tensor")
+
+
+def _rowmajor(t, name):
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError(f"{name} must be 2-D with unit stride along its last dimension")
+    return t.stride(0)
+
+
+def _out_code(out_dtype):
+    torch = _torch()
+    if out_dtype == torch.float32:
+        return P24_F32
+    if out_dtype == torch.bfloat16:
+        return P24_BF16
+    raise ValueError("out_dtype must be torch.float32 or torch.bfloat16")
+
+
+def _layout_code(layout):
+    if layout in ("device", P24_LAYOUT_DEVICE):
+        return P24_LAYOUT_DEVICE
+    if layout in ("canonical", P24_LAYOUT_CANONICAL):
+        return P24_LAYOUT_CANONICAL
+    raise ValueError("layout must be 'device' or 'canonical'")
+
+
+@dataclass
+class Compressed24:
+    """A 2:4-compressed M x K matrix: bf16 values + int32 words of 2-bit positions."""
+    values: object       # torch.bfloat16, flat
+    meta: object         # torch.int32, flat (bit patterns of the uint32 words)
+    M: int
+    K: int
+    layout: int
+
+
+@dataclass
+class CompressedTVW:
+    """TVW-compressed matrix: kept column lists per tile + 2:4 compression of the compacted rows."""
+    kept: object         # torch.int32 [T, keep_k]
+    values: object
+    meta: object
+    M: int
+    K: int
+    tile_m: int
+    keep_k: int
+    layout: int
+
+
+def compress(W, layout="device") -> Compressed24:
+    """Magnitude 2:4 prune + compress of W (cuda fp32 or bf16, [M, K])."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    ldw = _rowmajor(W, "W")
+    if W.dtype == torch.float32:
+        wd = P24_F32
+    elif W.dtype == torch.bfloat16:
+        wd = P24_BF16
+    else:
+        raise ValueError("W must be float32 or bfloat16")
+    M, K = W.shape
+    lc = _layout_code(layout)
+    L = lib()
+    vb, mb = L.prune24_values_bytes(M, K, lc), L.prune24_meta_bytes(M, K, lc)
+    if (vb == 0 or mb == 0) and M * K:
+        raise P24Error(P24_ERR_SHAPE if K % 4 else P24_ERR_UNSUPPORTED, "prune24_compress")
+    values = torch.empty(max(vb // 2, 1), dtype=torch.bfloat16, device=W.device)
+    meta = torch.empty(max(mb // 4, 1), dtype=torch.int32, device=W.device)
+    _check(L.prune24_compress(_ptr(W), wd, M, K, ldw, _ptr(values), _ptr(meta), lc, _stream(W.device)),
+           "prune24_compress")
+    return Compressed24(values, meta, M, K, lc)
+
+
+def decompress(c: Compressed24):
+    """Dense bf16 [M, K] with the kept values in place and zeros elsewhere."""
+    torch = _torch()
+    out = torch.empty((c.M, c.K), dtype=torch.bfloat16, device=c.values.device)
+    _check(lib().prune24_decompress(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(out), c.K,
+                                    _stream(out.device)), "prune24_decompress")
+    return out
+
+
+def spmm24(c: Compressed24, X, out_dtype=None, out=None):
+    """Y = W X for compressed W (device layout) and X bf16 [K, N]."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _require_cuda(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    ldx = _rowmajor(X, "X")
+    if X.shape[0] != c.K:
+        raise ValueError(f"X has {X.shape[0]} rows, W has K = {c.K}")
+    N = X.shape[1]
+    if out is None:
+        out = torch.empty((c.M, N), dtype=out_dtype, device=X.device)
+    ldy = _rowmajor(out, "out")
+    _check(lib().spmm24(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(X), ldx, N, _ptr(out),
+                        _out_code(out.dtype), ldy, P24_ALGO_AUTO, _stream(X.device)), "spmm24")
+    return out
+
+
+def tvw_compress(W, tile_m: int = 128, keep_k: int | None = None, layout="device") -> CompressedTVW:
+    """TVW selection (per tile_m-row tile keep keep_k columns by L1 norm) + 2:4 compression."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("tvw_compress takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    keep_k = K // 2 if keep_k is None else int(keep_k)
+    lc = _layout_code(layout)
+    L = lib()
+    T = (M + tile_m - 1) // tile_m
+    vb, mb = L.prune24_values_bytes(M, keep_k, lc), L.prune24_meta_bytes(M, keep_k, lc)
+    wsb = L.tvw_workspace_bytes(M, K, tile_m, keep_k)
+    kept = torch.empty((T, keep_k), dtype=torch.int32, device=W.device)
+    values = torch.empty(max(vb // 2, 1), dtype=torch.bfloat16, device=W.device)
+    meta = torch.empty(max(mb // 4, 1), dtype=torch.int32, device=W.device)
+    ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device=W.device)
+    _check(L.tvw_compress(_ptr(W), P24_F32, M, K, ldw, tile_m, keep_k, _ptr(kept), _ptr(values), _ptr(meta),
+                          lc, _ptr(ws), ws.numel(), _stream(W.device)), "tvw_compress")
+    return CompressedTVW(kept, values, meta, M, K, tile_m, keep_k, lc)
+
+
+def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None):
+    """Y = W X for a TVW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _require_cuda(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    ldx = _rowmajor(X, "X")
+    if X.shape[0] != t.K:
+        raise ValueError(f"X has {X.shape[0]} rows, W has K = {t.K}")
+    N = X.shape[1]
+    if out is None:
+        out = torch.empty((t.M, N), dtype=out_dtype, device=X.device)
+    ldy = _rowmajor(out, "out")
+    _check(lib().spmm_tvw(_ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.layout, t.M, t.K, t.tile_m, t.keep_k,
+                          _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tvw")
+    return out
+
+
+def pack_dense(W):
+    """Dense bf16 W [M, K] -> MFMA operand order (input of gemm_bf16)."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.bfloat16:
+        raise ValueError("W must be bfloat16")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    nb = lib().gemm_bf16_packed_bytes(M, K)
+    if nb == 0 and M * K:
+        raise P24Error(P24_ERR_UNSUPPORTED, "gemm_bf16_pack")
+    Wp = torch.empty(max(nb // 2, 1), dtype=torch.bfloat16, device=W.device)
+    _check(lib().gemm_bf16_pack(_ptr(W), M, K, ldw, _ptr(Wp), _stream(W.device)), "gemm_bf16_pack")
+    return Wp
+
+
+def gemm_bf16(Wp, M: int, K: int, X, out_dtype=None, out=None):
+    """Dense baseline Y = W X from packed W (see pack_dense)."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _require_cuda(X, "X")
+    ldx = _rowmajor(X, "X")
+    N = X.shape[1]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
+    ldy = _rowmajor(out, "out")
+    _check(lib().gemm_bf16(_ptr(Wp), M, K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy,
+                           _stream(X.device)), "gemm_bf16")
+    return out

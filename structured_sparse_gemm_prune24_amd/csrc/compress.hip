@@ -1,0 +1,410 @@
+// 2:4 magnitude prune + compress, decompress, dense operand packing and TVW
+// column selection (gfx950).  All kernels here are HBM-bound scans.
+#include "p24_api_internal.hpp"
+#include "p24_device.hpp"
+
+namespace p24 {
+
+// --------------------------------------------------------------------------
+// Loading one group of four raw bit patterns
+// --------------------------------------------------------------------------
+template <typename T> __device__ __forceinline__ void load_group(const T* p, uint32_t b[4]);
+
+template <> __device__ __forceinline__ void load_group<float>(const float* p, uint32_t b[4]) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);   // 16 B aligned by contract
+  b[0] = v.x; b[1] = v.y; b[2] = v.z; b[3] = v.w;
+}
+template <> __device__ __forceinline__ void load_group<uint16_t>(const uint16_t* p, uint32_t b[4]) {
+  const u32x2 v = *reinterpret_cast<const u32x2*>(p);   // 8 B aligned by contract
+  b[0] = v.x & 0xFFFFu; b[1] = v.x >> 16; b[2] = v.y & 0xFFFFu; b[3] = v.y >> 16;
+}
+
+template <typename T> __device__ __forceinline__ uint32_t raw_bits(T v);
+template <> __device__ __forceinline__ uint32_t raw_bits<float>(float v) { return __float_as_uint(v); }
+template <> __device__ __forceinline__ uint32_t raw_bits<uint16_t>(uint16_t v) { return v; }
+
+// Row m, compacted group g.  Without a gather the group is W[m][4g .. 4g+4);
+// with one (TVW) its columns are kept[tile(m)][4g .. 4g+4).
+// Gathered columns are clamped into [0, kmax) so that no read leaves the row.
+template <typename T, bool GATHER>
+__device__ __forceinline__ void fetch_group(const T* __restrict__ W, int64_t ldw, int64_t m, int64_t g,
+                                            const int32_t* __restrict__ kept_row, int64_t kmax, uint32_t b[4]) {
+  const T* row = W + m * ldw;
+  if constexpr (GATHER) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      int64_t k = kept_row[4 * g + i];
+      k = k < 0 ? 0 : (k >= kmax ? kmax - 1 : k);
+      b[i] = raw_bits<T>(row[k]);
+    }
+  } else {
+    load_group<T>(row + 4 * g, b);
+  }
+}
+
+// --------------------------------------------------------------------------
+// Canonical layout: one thread per (row, metadata word) = 8 groups.
+// --------------------------------------------------------------------------
+template <typename T, bool GATHER>
+__global__ __launch_bounds__(256) void k_compress_canonical(const T* __restrict__ W, int64_t ldw, int64_t M,
+                                                            int64_t K, uint16_t* __restrict__ values,
+                                                            uint32_t* __restrict__ meta,
+                                                            const int32_t* __restrict__ kept, int64_t tile_m,
+                                                            int64_t kmax) {
+  const int64_t nw = (K + 31) / 32;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= M * nw) return;
+  const int64_t m = id / nw, w = id % nw;
+  const int64_t G = K / 4;
+  const int32_t* kept_row = GATHER ? kept + (m / tile_m) * K : nullptr;
+  uint32_t word = 0;
+  uint32_t* vrow = reinterpret_cast<uint32_t*>(values + m * (K / 2));   // 4 B per group
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int64_t g = 8 * w + q;
+    if (g < G) {
+      uint32_t b[4];
+      fetch_group<T, GATHER>(W, ldw, m, g, kept_row, kmax, b);
+      uint16_t v0, v1;
+      const uint32_t code = compress_group<T>(b, v0, v1);
+      vrow[g] = (uint32_t)v0 | ((uint32_t)v1 << 16);
+      word |= code << (4 * q);
+    }
+  }
+  meta[m * nw + w] = word;
+}
+
+// --------------------------------------------------------------------------
+// Device layout: one thread per (row block rb, K-pair t, row r) -- r fastest so
+// that the 16 B value stores of neighbouring threads are contiguous.
+// Rows M..Mp-1 are padding: zero values, positions (0, 1).
+// --------------------------------------------------------------------------
+template <typename T, bool GATHER>
+__global__ __launch_bounds__(256) void k_compress_device(const T* __restrict__ W, int64_t ldw, int64_t M,
+                                                         int64_t K, uint16_t* __restrict__ dvals,
+                                                         uint32_t* __restrict__ dmeta,
+                                                         const int32_t* __restrict__ kept, int64_t tile_m,
+                                                         int64_t kmax) {
+  const int64_t RB = (M + 31) / 32, T_ = K / 64, S = K / 32;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= RB * T_ * 32) return;
+  const int64_t r = id % 32, t = (id / 32) % T_, rb = id / (32 * T_);
+  const int64_t m = rb * 32 + r;
+  const bool live = m < M;
+  const int32_t* kept_row = (GATHER && live) ? kept + (m / tile_m) * K : nullptr;
+  uint32_t mword[2] = {0u, 0u};          // lane h = 0 and h = 1 words
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {   // the two K-steps of the pair (abid 0 / 1)
+    const int64_t s = 2 * t + half;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {          // lane half: compressed columns 8h .. 8h+8 of the step
+      uint32_t packed[4];
+      uint32_t code16 = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t g = 8 * s + 4 * h + q;
+        uint16_t v0 = 0, v1 = 0;
+        uint32_t code = 0x4u;              // positions (0, 1) for padding rows
+        if (live) {
+          uint32_t b[4];
+          fetch_group<T, GATHER>(W, ldw, m, g, kept_row, kmax, b);
+          code = compress_group<T>(b, v0, v1);
+        }
+        packed[q] = (uint32_t)v0 | ((uint32_t)v1 << 16);
+        code16 |= code << (4 * q);
+      }
+      const int64_t L = r + 32 * h;
+      u32x4 pv = {packed[0], packed[1], packed[2], packed[3]};
+      *reinterpret_cast<u32x4*>(dvals + ((rb * S + s) * 64 + L) * 8) = pv;
+      mword[h] |= code16 << (16 * half);
+    }
+  }
+  dmeta[(rb * T_ + t) * 64 + r] = mword[0];
+  dmeta[(rb * T_ + t) * 64 + r + 32] = mword[1];
+}
+
+// --------------------------------------------------------------------------
+// Decompress: one thread per (row, group) -> 4 dense bf16 entries.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_decompress(const uint16_t* __restrict__ values,
+                                                    const uint32_t* __restrict__ meta, int layout, int64_t M,
+                                                    int64_t K, uint16_t* __restrict__ out, int64_t ldo) {
+  const int64_t G = K / 4;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= M * G) return;
+  const int64_t m = id / G, g = id % G;
+  uint32_t code;
+  uint16_t v0, v1;
+  if (layout == P24_LAYOUT_CANONICAL) {
+    const int64_t nw = (K + 31) / 32;
+    code = (meta[m * nw + g / 8] >> (4 * (g % 8))) & 0xFu;
+    v0 = values[m * (K / 2) + 2 * g];
+    v1 = values[m * (K / 2) + 2 * g + 1];
+  } else {
+    const int64_t S = K / 32, T_ = K / 64;
+    const int64_t s = g / 8, h = (g % 8) / 4, q = g % 4;
+    const int64_t rb = m / 32, L = m % 32 + 32 * h;
+    code = (meta[(rb * T_ + s / 2) * 64 + L] >> (16 * (s % 2) + 4 * q)) & 0xFu;
+    const uint16_t* v = values + ((rb * S + s) * 64 + L) * 8 + 2 * q;
+    v0 = v[0];
+    v1 = v[1];
+  }
+  const uint32_t p0 = code & 3u, p1 = code >> 2;
+  uint16_t* o = out + m * ldo + 4 * g;
+#pragma unroll
+  for (uint32_t i = 0; i < 4; ++i) o[i] = (i == p0) ? v0 : ((i == p1) ? v1 : (uint16_t)0);
+}
+
+// --------------------------------------------------------------------------
+// Dense operand packing for the MFMA 32x32x16 bf16 tile loop.
+// One thread per (row block, K16 step, lane): one 16 B chunk.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_pack_dense(const uint16_t* __restrict__ W, int64_t ldw, int64_t M,
+                                                    int64_t K, uint16_t* __restrict__ Wp) {
+  const int64_t RB = (M + 31) / 32, S = K / 16;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= RB * S * 64) return;
+  const int64_t L = id % 64, s = (id / 64) % S, rb = id / (64 * S);
+  const int64_t m = rb * 32 + L % 32, k = 16 * s + 8 * (L / 32);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (m < M) v = *reinterpret_cast<const u32x4*>(W + m * ldw + k);
+  *reinterpret_cast<u32x4*>(Wp + id * 8) = v;
+}
+
+// --------------------------------------------------------------------------
+// TVW column scores: one thread per (tile, column); fp64 sum of |W| over the
+// tile's rows, one row at a time in ascending order (fixed order -> the same
+// correctly rounded sums as a sequential host loop).
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W, int64_t ldw, int64_t M,
+                                                    int64_t K, int64_t tile_m, double* __restrict__ scores) {
+  const int64_t T_ = (M + tile_m - 1) / tile_m;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= T_ * K) return;
+  const int64_t t = id / K, k = id % K;
+  const int64_t r1 = (t + 1) * tile_m < M ? (t + 1) * tile_m : M;
+  double acc = 0.0;
+  for (int64_t m = t * tile_m; m < r1; ++m) acc = acc + fabs((double)W[m * ldw + k]);
+  scores[id] = acc;
+}
+
+// --------------------------------------------------------------------------
+// TVW selection: one block per tile.  Column k is kept when fewer than keep_k
+// columns beat it (higher score bits, or equal bits and lower index).  Kept
+// columns are then written in ascending order by a block-wide prefix count.
+// --------------------------------------------------------------------------
+constexpr int SEL_THREADS = 256;
+constexpr int SEL_CHUNK = 2048;
+
+__global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __restrict__ scores, int64_t K,
+                                                            int64_t keep_k, int32_t* __restrict__ kept) {
+  __shared__ uint64_t chunk[SEL_CHUNK];
+  __shared__ uint32_t wave_counts[SEL_THREADS / 64];
+  extern __shared__ uint32_t keep_bits[];     // ceil(K/32) words
+  const int64_t t = blockIdx.x;
+  const uint64_t* key = reinterpret_cast<const uint64_t*>(scores + t * K);
+  const int tid = threadIdx.x;
+  const int64_t nwords = (K + 31) / 32;
+  for (int64_t i = tid; i < nwords; i += SEL_THREADS) keep_bits[i] = 0u;
+  __syncthreads();
+  // Each thread owns columns k = tid, tid + 256, ...; count how many columns beat each.
+  for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS * 8) {
+    uint64_t mykey[8];
+    int64_t beaten[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t k = k0 + tid + (int64_t)u * SEL_THREADS;
+      mykey[u] = k < K ? key[k] : 0;
+      beaten[u] = 0;
+    }
+    for (int64_t j0 = 0; j0 < K; j0 += SEL_CHUNK) {
+      const int64_t n = (K - j0) < SEL_CHUNK ? (K - j0) : SEL_CHUNK;
+      __syncthreads();
+      for (int64_t i = tid; i < n; i += SEL_THREADS) chunk[i] = key[j0 + i];
+      __syncthreads();
+      for (int64_t i = 0; i < n; ++i) {
+        const uint64_t kj = chunk[i];
+        const int64_t j = j0 + i;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int64_t k = k0 + tid + (int64_t)u * SEL_THREADS;
+          beaten[u] += (kj > mykey[u]) || (kj == mykey[u] && j < k);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t k = k0 + tid + (int64_t)u * SEL_THREADS;
+      if (k < K && beaten[u] < keep_k) atomicOr(&keep_bits[k / 32], 1u << (k % 32));
+    }
+  }
+  __syncthreads();
+  // Ordered compaction: blocks of 256 consecutive columns, one per thread.
+  int64_t base = 0;
+  const int lane = tid % 64, wave = tid / 64;
+  for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS) {
+    const int64_t k = k0 + tid;
+    const bool flag = k < K && ((keep_bits[k / 32] >> (k % 32)) & 1u);
+    const uint64_t ballot = __ballot(flag);
+    const uint32_t below = __popcll(ballot & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    if (lane == 0) wave_counts[wave] = __popcll(ballot);
+    __syncthreads();
+    int64_t off = base;
+    for (int w = 0; w < wave; ++w) off += wave_counts[w];
+    if (flag) kept[t * keep_k + off + below] = (int32_t)k;
+    int64_t total = 0;
+    for (int w = 0; w < SEL_THREADS / 64; ++w) total += wave_counts[w];
+    base += total;
+    __syncthreads();
+  }
+}
+
+}  // namespace p24
+
+// ============================================================================
+// C ABI
+// ============================================================================
+using namespace p24;
+
+static inline unsigned grid1d(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
+
+extern "C" P24_API size_t prune24_values_bytes(int64_t M, int64_t K, int32_t layout) {
+  if (M < 0 || K < 0 || K % 4) return 0;
+  if (layout == P24_LAYOUT_CANONICAL) return (size_t)M * (size_t)(K / 2) * 2;
+  if (layout == P24_LAYOUT_DEVICE) {
+    if (K % 64) return 0;
+    return (size_t)((M + 31) / 32) * 32 * (size_t)(K / 2) * 2;
+  }
+  return 0;
+}
+
+extern "C" P24_API size_t prune24_meta_bytes(int64_t M, int64_t K, int32_t layout) {
+  if (M < 0 || K < 0 || K % 4) return 0;
+  if (layout == P24_LAYOUT_CANONICAL) return (size_t)M * (size_t)((K + 31) / 32) * 4;
+  if (layout == P24_LAYOUT_DEVICE) {
+    if (K % 64) return 0;
+    return (size_t)((M + 31) / 32) * (size_t)(K / 64) * 64 * 4;
+  }
+  return 0;
+}
+
+static p24_status check_compress_args(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                      const void* values, const void* meta, int32_t layout) {
+  if (w_dtype != P24_F32 && w_dtype != P24_BF16) return P24_ERR_DTYPE;
+  if (layout != P24_LAYOUT_CANONICAL && layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
+  if (M < 0 || K < 0 || K % 4 || ldw < K) return P24_ERR_SHAPE;
+  if (M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (layout == P24_LAYOUT_DEVICE && K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return P24_OK;
+  if (!W || !values || !meta) return P24_ERR_NULL;
+  const size_t wal = w_dtype == P24_F32 ? 16 : 8;
+  if (!aligned(W, wal) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16)) return P24_ERR_ALIGN;
+  return P24_OK;
+}
+
+template <bool GATHER>
+static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                  void* values, void* meta, int32_t layout, const int32_t* kept,
+                                  int64_t tile_m, int64_t kmax, hipStream_t st) {
+  if (M == 0 || K == 0) return P24_OK;
+  if (layout == P24_LAYOUT_CANONICAL) {
+    const int64_t n = M * ((K + 31) / 32);
+    if (w_dtype == P24_F32)
+      hipLaunchKernelGGL((k_compress_canonical<float, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+                         (const float*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+    else
+      hipLaunchKernelGGL((k_compress_canonical<uint16_t, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+                         (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+  } else {
+    const int64_t n = ((M + 31) / 32) * (K / 64) * 32;
+    if (w_dtype == P24_F32)
+      hipLaunchKernelGGL((k_compress_device<float, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+                         (const float*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+    else
+      hipLaunchKernelGGL((k_compress_device<uint16_t, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+                         (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+  }
+  return launch_status();
+}
+
+extern "C" P24_API p24_status prune24_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K,
+                                               int64_t ldw, void* values, void* meta, int32_t layout,
+                                               void* stream) {
+  const p24_status s = check_compress_args(W, w_dtype, M, K, ldw, values, meta, layout);
+  if (s != P24_OK) return s;
+  return launch_compress<false>(W, w_dtype, M, K, ldw, values, meta, layout, nullptr, 1, K,
+                                (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status prune24_decompress(const void* values, const void* meta, int32_t layout,
+                                                 int64_t M, int64_t K, void* W_out, int64_t ldo,
+                                                 void* stream) {
+  if (layout != P24_LAYOUT_CANONICAL && layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
+  if (M < 0 || K < 0 || K % 4 || ldo < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (layout == P24_LAYOUT_DEVICE && K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return P24_OK;
+  if (!values || !meta || !W_out) return P24_ERR_NULL;
+  if (!aligned(values, 4) || !aligned(meta, 4) || !aligned(W_out, 2)) return P24_ERR_ALIGN;
+  const int64_t n = M * (K / 4);
+  hipLaunchKernelGGL(k_decompress, dim3(grid1d(n, 256)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)values, (const uint32_t*)meta, (int)layout, M, K, (uint16_t*)W_out, ldo);
+  return launch_status();
+}
+
+extern "C" P24_API size_t gemm_bf16_packed_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K < 0 || K % 64) return 0;
+  return (size_t)((M + 31) / 32) * 32 * (size_t)K * 2;
+}
+
+extern "C" P24_API p24_status gemm_bf16_pack(const void* W, int64_t M, int64_t K, int64_t ldw, void* Wp,
+                                             void* stream) {
+  if (M < 0 || K < 0 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return P24_OK;
+  if (!W || !Wp) return P24_ERR_NULL;
+  if (!aligned(W, 16) || ldw % 8 || !aligned(Wp, 16)) return P24_ERR_ALIGN;
+  const int64_t n = ((M + 31) / 32) * (K / 16) * 64;
+  hipLaunchKernelGGL(k_pack_dense, dim3(grid1d(n, 256)), dim3(256), 0, (hipStream_t)stream,
+                     (const uint16_t*)W, ldw, M, K, (uint16_t*)Wp);
+  return launch_status();
+}
+
+static constexpr int64_t TVW_MAX_K = 1 << 18;   // keep bitmap of the selection kernel: 32 KiB of LDS
+
+extern "C" P24_API size_t tvw_workspace_bytes(int64_t M, int64_t K, int64_t tile_m, int64_t keep_k) {
+  (void)keep_k;
+  if (M < 0 || K <= 0 || tile_m <= 0) return 0;
+  return (size_t)((M + tile_m - 1) / tile_m) * (size_t)K * sizeof(double);
+}
+
+extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                           int64_t tile_m, int64_t keep_k, int32_t* kept, void* values,
+                                           void* meta, int32_t layout, void* workspace, size_t ws_bytes,
+                                           void* stream) {
+  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
+  if (layout != P24_LAYOUT_CANONICAL && layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
+  if (M < 0 || K <= 0 || ldw < K || tile_m <= 0 || tile_m % 32 || keep_k <= 0 || keep_k > K || keep_k % 4)
+    return P24_ERR_SHAPE;
+  if (M > INT32_MAX || K > TVW_MAX_K) return P24_ERR_SHAPE;
+  if (layout == P24_LAYOUT_DEVICE && keep_k % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0) return P24_OK;
+  if (!W || !kept || !values || !meta) return P24_ERR_NULL;
+  if (!workspace || ws_bytes < tvw_workspace_bytes(M, K, tile_m, keep_k)) return P24_ERR_WORKSPACE;
+  if (!aligned(W, 16) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4) ||
+      !aligned(workspace, 8))
+    return P24_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t T_ = (M + tile_m - 1) / tile_m;
+  double* scores = (double*)workspace;
+  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
+                     tile_m, scores);
+  p24_status s = launch_status();
+  if (s != P24_OK) return s;
+  const size_t dyn = (size_t)((K + 31) / 32) * 4;
+  hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), dyn, st, (const double*)scores, K,
+                     keep_k, kept);
+  s = launch_status();
+  if (s != P24_OK) return s;
+  // 2:4 along the compacted axis, reading W through the kept column lists
+  return launch_compress<true>(W, w_dtype, M, keep_k, ldw, values, meta, layout, kept, tile_m, K, st);
+}

@@ -1,0 +1,110 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every entry point include/prune24.h declares, and
+its validation rejects bad arguments with the documented status before
+anything is enqueued (the pointers used here are never dereferenced).
+"""
+import ctypes
+
+import pytest
+
+p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
+
+
+@pytest.fixture(scope="module")
+def L():
+    try:
+        return p24.lib()
+    except RuntimeError as e:
+        pytest.fail(f"library not built: {e}")
+
+
+def test_exports_every_declared_symbol(L):
+    syms = p24.header_symbols()
+    assert len(syms) == len(set(syms)) == 13
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
+
+
+def test_version_and_strerror(L):
+    assert L.prune24_abi_version() == 1
+    for code in range(-8, 1):
+        assert p24.strerror(code)
+    assert p24.strerror(-99) == "unknown status"
+
+
+def test_size_helpers(L):
+    # canonical: K/2 bf16 values and ceil(K/32) words per row
+    assert L.prune24_values_bytes(3, 36, p24.P24_LAYOUT_CANONICAL) == 3 * 18 * 2
+    assert L.prune24_meta_bytes(3, 36, p24.P24_LAYOUT_CANONICAL) == 3 * 2 * 4
+    # device: rows rounded up to 32, K % 64 required
+    assert L.prune24_values_bytes(33, 128, p24.P24_LAYOUT_DEVICE) == 64 * 64 * 2
+    assert L.prune24_meta_bytes(33, 128, p24.P24_LAYOUT_DEVICE) == 2 * 2 * 64 * 4
+    assert L.prune24_values_bytes(32, 96, p24.P24_LAYOUT_DEVICE) == 0
+    assert L.prune24_values_bytes(4, 6, p24.P24_LAYOUT_CANONICAL) == 0
+    assert L.tvw_workspace_bytes(4096, 4096, 128, 2048) == 32 * 4096 * 8
+    assert L.gemm_bf16_packed_bytes(40, 128) == 64 * 128 * 2
+    assert L.gemm_bf16_packed_bytes(40, 96) == 0
+
+
+FAKE = ctypes.c_void_p(1 << 20)          # aligned, never dereferenced
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+NUL = ctypes.c_void_p(0)
+
+
+def test_compress_validation(L):
+    f = L.prune24_compress
+    assert f(FAKE, 7, 4, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_DTYPE
+    assert f(FAKE, 0, 4, 8, 8, FAKE, FAKE, 5, NUL) == p24.P24_ERR_LAYOUT
+    assert f(FAKE, 0, 4, 6, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_SHAPE          # K % 4
+    assert f(FAKE, 0, 4, 8, 4, FAKE, FAKE, 0, NUL) == p24.P24_ERR_SHAPE          # ldw < K
+    assert f(FAKE, 0, -1, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_SHAPE
+    assert f(FAKE, 0, 4, 96, 96, FAKE, FAKE, 1, NUL) == p24.P24_ERR_UNSUPPORTED  # device needs K % 64
+    assert f(NUL, 0, 4, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_NULL
+    assert f(MISALIGNED, 0, 4, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_ALIGN
+    assert f(FAKE, 0, 4, 8, 10, FAKE, FAKE, 0, NUL) == p24.P24_ERR_ALIGN          # ldw % 4
+    assert f(NUL, 0, 0, 8, 8, NUL, NUL, 0, NUL) == p24.P24_OK                     # M == 0: no-op
+
+
+def test_spmm_validation(L):
+    f = L.spmm24
+    args = lambda **k: [k.get("v", FAKE), k.get("m", FAKE), k.get("layout", 1), k.get("M", 64),
+                        k.get("K", 128), k.get("X", FAKE), k.get("ldx", 64), k.get("N", 64), k.get("Y", FAKE),
+                        k.get("yd", 0), k.get("ldy", 64), k.get("algo", 0), NUL]
+    assert f(*args(layout=0)) == p24.P24_ERR_LAYOUT
+    assert f(*args(K=96)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(yd=3)) == p24.P24_ERR_DTYPE
+    assert f(*args(algo=9)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(ldx=32)) == p24.P24_ERR_SHAPE
+    assert f(*args(ldx=68, N=60)) == p24.P24_ERR_ALIGN
+    assert f(*args(X=MISALIGNED)) == p24.P24_ERR_ALIGN
+    assert f(*args(v=NUL)) == p24.P24_ERR_NULL
+    assert f(*args(M=0, v=NUL, m=NUL, X=NUL, Y=NUL)) == p24.P24_OK
+    assert f(*args(N=0, ldx=0, ldy=0, v=NUL, m=NUL, X=NUL, Y=NUL)) == p24.P24_OK
+
+
+def test_tvw_validation(L):
+    f = L.tvw_compress
+    base = dict(W=FAKE, wd=0, M=256, K=256, ldw=256, tile=128, keep=128, kept=FAKE, v=FAKE, m=FAKE, layout=1,
+                ws=FAKE, wsb=1 << 30)
+    def call(**k):
+        a = {**base, **k}
+        return f(a["W"], a["wd"], a["M"], a["K"], a["ldw"], a["tile"], a["keep"], a["kept"], a["v"], a["m"],
+                 a["layout"], a["ws"], a["wsb"], NUL)
+    assert call(wd=1) == p24.P24_ERR_DTYPE
+    assert call(tile=100) == p24.P24_ERR_SHAPE
+    assert call(keep=300) == p24.P24_ERR_SHAPE
+    assert call(keep=130) == p24.P24_ERR_SHAPE
+    assert call(keep=132) == p24.P24_ERR_UNSUPPORTED         # device layout: keep % 64
+    assert call(wsb=16) == p24.P24_ERR_WORKSPACE
+    assert call(ws=NUL) == p24.P24_ERR_WORKSPACE
+    g = L.spmm_tvw
+    assert g(FAKE, FAKE, FAKE, 1, 256, 256, 64, 128, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert g(FAKE, FAKE, FAKE, 0, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_LAYOUT
+
+
+def test_dense_validation(L):
+    assert L.gemm_bf16_pack(FAKE, 64, 96, 96, FAKE, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert L.gemm_bf16_pack(FAKE, 64, 128, 132, FAKE, NUL) == p24.P24_ERR_ALIGN
+    assert L.gemm_bf16(NUL, 64, 128, FAKE, 64, 64, FAKE, 1, 64, NUL) == p24.P24_ERR_NULL

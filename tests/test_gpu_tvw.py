@@ -1,0 +1,89 @@
+"""GPU parity for tile-vector-wise sparsity: tvw_compress bit-exact, spmm_tvw in tolerance."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle import prune24 as O
+from gpu_util import bf16_dev, f32_dev, need_gpu, sample_rows, torch, u16_host, u32_host, y_host
+
+p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
+pytestmark = pytest.mark.gpu
+
+
+def _compare_compress(W, tile, keep, layout):
+    t = p24.tvw_compress(f32_dev(W), tile_m=tile, keep_k=keep, layout=layout)
+    torch.cuda.synchronize()
+    kept, values, meta = O.tvw_compress(W, tile, keep)
+    assert np.array_equal(t.kept.cpu().numpy(), kept)
+    if layout == "device":
+        values, meta = O.to_device_layout(values, meta, keep)
+    ov, om = values.reshape(-1), meta.reshape(-1)
+    assert np.array_equal(u16_host(t.values)[:ov.size], ov)
+    assert np.array_equal(u32_host(t.meta)[:om.size], om)
+    return t, kept, values, meta
+
+
+@pytest.mark.parametrize("M,K,tile,keep,layout", [
+    (256, 256, 128, 128, "device"),
+    (300, 256, 128, 128, "device"),       # partial last tile
+    (300, 200, 64, 100, "canonical"),
+    (256, 512, 128, 512, "device"),       # keep everything
+    (128, 2304, 128, 1152, "device"),
+])
+def test_compress_small(M, K, tile, keep, layout):
+    need_gpu()
+    W = workloads.random_matrix((M, K), seed=M + K + keep, sigma=0.02)
+    _compare_compress(W, tile, keep, layout)
+
+
+def test_compress_ties():
+    need_gpu()
+    W = workloads.small_int_matrix((256, 256), seed=5, lo=-1, hi=1)   # many tied scores and groups
+    _compare_compress(W, 128, 128, "device")
+
+
+def test_c5_full():
+    need_gpu()
+    wl = workloads.WORKLOADS["c5"]
+    print("[tvw] c5 compress", flush=True)
+    W = workloads.weights(wl)
+    t, kept, values, meta = _compare_compress(W, wl.tile_m, wl.keep_k, "device")
+    Xb = workloads.activations(wl)
+    for out, dt in (("bf16", torch.bfloat16), ("f32", torch.float32)):
+        print(f"[tvw] c5 spmm {out}", flush=True)
+        Y = p24.spmm_tvw(t, bf16_dev(Xb), out_dtype=dt)
+        torch.cuda.synchronize()
+        rows = sample_rows(wl.M, 40, seed=3)
+        v, m = O.from_device_layout(values, meta, wl.M, wl.keep_k)
+        Wd = O.tvw_decompress(kept, v, m, wl.M, wl.K, wl.tile_m)
+        y_ref, bnd = O.gemm_ref(Wd, Xb, rows=rows)
+        ok, worst = O.check(y_host(Y, rows), y_ref, bnd, out)
+        assert ok, worst
+
+
+@pytest.mark.parametrize("M,K,N,keep", [(256, 256, 200, 128), (384, 512, 1000, 256), (300, 256, 72, 128)])
+def test_spmm_tvw_small(M, K, N, keep):
+    need_gpu()
+    W = workloads.random_matrix((M, K), seed=N + keep, sigma=0.05)
+    Xb = workloads.random_bf16((K, N), seed=N)
+    t = p24.tvw_compress(f32_dev(W), tile_m=128, keep_k=keep)
+    Y = p24.spmm_tvw(t, bf16_dev(Xb), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kept, values, meta = O.tvw_compress(W, 128, keep)
+    y_ref, bnd = O.gemm_ref(O.tvw_decompress(kept, values, meta, M, K, 128), Xb)
+    ok, worst = O.check(y_host(Y), y_ref, bnd, "f32")
+    assert ok, worst
+
+
+def test_keep_all_equals_plain_24():
+    need_gpu()
+    M, K, N = 256, 256, 128
+    W = workloads.random_matrix((M, K), seed=77, sigma=0.05)
+    Xb = workloads.random_bf16((K, N), seed=78)
+    Wt = f32_dev(W)
+    t = p24.tvw_compress(Wt, tile_m=128, keep_k=K)
+    Yt = p24.spmm_tvw(t, bf16_dev(Xb), out_dtype=torch.float32)
+    Yp = p24.spmm24(p24.compress(Wt), bf16_dev(Xb), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert (t.kept.cpu().numpy() == np.arange(K)).all()
+    assert torch.equal(Yt, Yp)
