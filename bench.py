@@ -1,0 +1,239 @@
+"""Benchmark: dense-equivalent TFLOP/s of the 2:4 sparse GEMM on one MI355X.
+
+Headline workload: Y = W X with W 8192 x 8192 (N(0, 0.02^2), magnitude-pruned
+2:4 along K, compressed to bf16 values + 2-bit positions), X 8192 x 8192 bf16,
+fp32 accumulation, bf16 output.  One step = one spmm24 launch on inputs already
+resident in HBM.  Dense-equivalent flops = 2 M N K; the sparse kernel performs
+half of them (M N K).
+
+Beside the headline, the same run times (HIP events on the launch stream):
+  - prune24_compress of the same W (the offline prune + compress step),
+  - this project's dense bf16 GEMM of the unpruned W (the speedup denominator),
+  - torch.matmul (hipBLASLt) of the same shapes, as context only,
+  - the TVW workload (4096^3, tile 128, keep 2048): tvw_compress + spmm_tvw,
+and the CPU oracle on a bounded sample of the headline workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+       [--only spmm|dense|compress|tvw|copy]  (profiling aid: run one kernel only)
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_HBM_GBS = 8000.0               # MI355X HBM3E (published)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["spmm", "dense", "compress", "tvw", "copy"], default=None)
+    ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
+    return ap.parse_args()
+
+
+def event_times_ms(torch, fn, iters):
+    """Per-launch durations (ms) from HIP events recorded on the current stream."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(iters + 1)]
+    evs[0].record()
+    for i in range(iters):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(iters)]
+
+
+def median(xs):
+    s = sorted(xs)
+    n = len(s)
+    return s[n // 2] if n % 2 else 0.5 * (s[n // 2 - 1] + s[n // 2])
+
+
+def cpu_baseline(wl, W, Xb):
+    """Oracle (numpy, fp64) on a bounded row sample of the headline workload."""
+    import numpy as np
+    from oracle import prune24 as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    rows = 256
+    t0 = time.perf_counter()
+    values, meta = O.compress_24(W[:rows], "f32")
+    Wd = O.decompress_24(values, meta, wl.K)
+    y, bnd = O.gemm_ref(Wd, Xb)
+    dt = time.perf_counter() - t0
+    assert np.isfinite(y).all()
+    flops = 2.0 * rows * wl.N * wl.K
+    return {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s (dense-equivalent)",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": f"{rows} of {wl.M} output rows of {wl.key}: oracle prune+compress+decompress of those "
+                  f"rows and fp64 GEMM + |W||X| bound against the full X ({dt:.1f} s)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+              "see DESIGN.md for how the path would shard", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_prune24_amd as p24
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = workloads.WORKLOADS[args.workload]
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    W = workloads.weights(wl)
+    Xb = workloads.activations(wl)
+    Wt = torch.from_numpy(W).to(dev)
+    Xt = to_bf16(Xb)
+    Wd_bf16 = to_bf16(workloads.truncate_to_bf16_bits(W))
+    out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+    Y = torch.empty((wl.M, wl.N), dtype=out_dtype, device=dev)
+    c = p24.compress(Wt, layout="device")
+    torch.cuda.synchronize()
+
+    rows = {}
+    if args.only == "copy":
+        # plain copy of known size: calibration of the HBM byte counters
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": src.numel() * 4, "launches": 3}))
+        return
+    if args.only == "compress":
+        ts = event_times_ms(torch, lambda: p24.compress(Wt, layout="device"), max(args.steps, 3))
+        print(json.dumps({"prune24_compress_us": median(ts) * 1e3}))
+        return
+
+    # ---------------- headline: spmm24 ----------------
+    def step():
+        p24.spmm24(c, Xt, out=Y)
+
+    if args.only in (None, "spmm"):
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ev = event_times_ms(torch, step, args.steps)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms_per_step = wall * 1e3 / args.steps
+        launch_ms = sum(ev) / len(ev)
+        rows["spmm24_us_mean"] = launch_ms * 1e3
+        rows["spmm24_us_median"] = median(ev) * 1e3
+        if args.only == "spmm":
+            print(json.dumps(rows))
+            return
+    # ---------------- dense baseline ----------------
+    if args.only in (None, "dense"):
+        Wp = p24.pack_dense(Wd_bf16)
+        Yd = torch.empty_like(Y)
+        dstep = lambda: p24.gemm_bf16(Wp, wl.M, wl.K, Xt, out=Yd)
+        for _ in range(args.warmup):
+            dstep()
+        ev_d = event_times_ms(torch, dstep, max(args.steps // 2, 3))
+        rows["gemm_bf16_us_mean"] = sum(ev_d) / len(ev_d) * 1e3
+        if args.only == "dense":
+            print(json.dumps(rows))
+            return
+        del Wp, Yd
+        # context only: vendor library dense GEMM of the same shape
+        Xc = Xt
+        for _ in range(2):
+            torch.matmul(Wd_bf16, Xc)
+        ev_t = event_times_ms(torch, lambda: torch.matmul(Wd_bf16, Xc), 5)
+        rows["torch_matmul_us_mean"] = sum(ev_t) / len(ev_t) * 1e3
+        # compress of the headline W
+        for _ in range(2):
+            p24.compress(Wt, layout="device")
+        ev_c = event_times_ms(torch, lambda: p24.compress(Wt, layout="device"), 5)
+        rows["prune24_compress_us_mean"] = sum(ev_c) / len(ev_c) * 1e3
+
+    # ---------------- TVW workload ----------------
+    if args.only in (None, "tvw"):
+        wt = workloads.WORKLOADS["c5"]
+        W5 = torch.from_numpy(workloads.weights(wt)).to(dev)
+        X5 = to_bf16(workloads.activations(wt))
+        t5 = p24.tvw_compress(W5, tile_m=wt.tile_m, keep_k=wt.keep_k)
+        Y5 = torch.empty((wt.M, wt.N), dtype=torch.bfloat16, device=dev)
+        tstep = lambda: p24.spmm_tvw(t5, X5, out=Y5)
+        for _ in range(args.warmup):
+            tstep()
+        ev5 = event_times_ms(torch, tstep, max(args.steps, 5))
+        rows["spmm_tvw_c5_us_mean"] = sum(ev5) / len(ev5) * 1e3
+        rows["spmm_tvw_c5_dense_eq_tflops"] = wt.dense_flops / (rows["spmm_tvw_c5_us_mean"] * 1e-6) / 1e12
+        ev5c = event_times_ms(torch, lambda: p24.tvw_compress(W5, tile_m=wt.tile_m, keep_k=wt.keep_k), 3)
+        rows["tvw_compress_c5_us_mean"] = sum(ev5c) / len(ev5c) * 1e3
+        if args.only == "tvw":
+            print(json.dumps(rows))
+            return
+
+    value = wl.dense_flops / (ms_per_step * 1e-3) / 1e12
+    achieved = wl.kept_flops / (launch_ms * 1e-3) / 1e12
+    rows["speedup_vs_dense"] = rows["gemm_bf16_us_mean"] / rows["spmm24_us_mean"]
+    rows["speedup_vs_torch_matmul"] = rows["torch_matmul_us_mean"] / rows["spmm24_us_mean"]
+    rows["dense_eq_frac_of_sparse_peak"] = (wl.dense_flops / (launch_ms * 1e-3) / 1e12) / (2 * PEAK_BF16_MFMA_TFLOPS)
+    out = {
+        "metric": "dense-equiv TFLOP/s of 2:4 SpMM (bf16, 1 MI355X); speedup vs dense GEMM",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02^2) weights, N(0,1) bf16 activations)",
+        "config": {"workload": f"{wl.key}: {wl.name}, magnitude 2:4 along K, bf16 out",
+                   "M": wl.M, "K": wl.K, "N": wl.N, "out_dtype": wl.out_dtype},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_MFMA_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "k_gemm<256,256,2,2,sparse> (spmm24)",
+            "algorithmic_flops_per_launch": wl.kept_flops,
+        },
+        "speedup_vs_dense": round(rows["speedup_vs_dense"], 3),
+        "rows": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rows.items()},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, W, Xb)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
