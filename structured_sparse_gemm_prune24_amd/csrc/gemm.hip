@@ -5,50 +5,90 @@
 // Data flow per block (BM x BN outputs, K consumed 64 logical columns at a time):
 //   * W operand: the compressed values / metadata (or the packed dense W) are
 //     stored in MFMA operand order, so each wave loads its A fragments straight
-//     from global memory into registers: every load is one contiguous 1 KiB
-//     (values) or 256 B (metadata) block per wave.  No LDS is spent on W.
-//   * X operand: the 64 x BN tile (row-major, N contiguous) is staged in LDS
-//     with double buffering; rows are whole contiguous N-slices, so the TVW
-//     gather only changes which global row each slice comes from.  B fragments
-//     come out of LDS with ds_read_b64_tr_b16, which transposes 4 x 16 bf16
-//     sub-tiles so each lane receives 4 consecutive k of one column.
+//     from global memory into registers, one contiguous 1 KiB (values) or
+//     256 B (metadata) block per wave and load.  No LDS is spent on W.  The
+//     fragments of iteration it+1 are in flight while iteration it computes.
+//   * X operand: 64 x BN tiles (row-major, N contiguous) go global -> LDS with
+//     direct-to-LDS loads (global_load_lds_dwordx4: lane l writes its 16 B at
+//     the wave's LDS base + 16 l), into a ring of three LDS stages, two tiles
+//     ahead of the compute.  Rows are whole N-slices, so the TVW gather only
+//     changes the global row a slice comes from.  Inside a row the 16 B chunks
+//     are XOR-swizzled by the row's low bits so that the transposed reads below
+//     spread over all LDS banks.
+//   * B fragments come out of LDS with ds_read_b64_tr_b16: within a group of
+//     16 lanes, lane i receives element i%4 of the 8-byte pieces addressed by
+//     lanes 4e + i/4 (e = 0..3), i.e. 4 consecutive k of one column when the
+//     16 lanes address a 4-row x 16-column sub-tile.  These reads are issued as
+//     inline asm with explicit lgkmcnt waits tied to the fragments: the
+//     compiler would otherwise stall every LDS read on all outstanding
+//     direct-to-LDS loads.
+//   * Tails: addresses are clamped instead of branched on.  Columns of X at or
+//     beyond N only feed output columns that are never stored, and rows past M
+//     only feed rows that are never stored, so the clamped (valid) data there
+//     is harmless.
 //   * Accumulators stay in registers for the whole K loop; the epilogue rounds
 //     (fp32 -> bf16 RNE) or stores fp32 with row-contiguous lane groups.
 #include <cstdlib>
 #include <string>
+#include <type_traits>
 
 #include "p24_api_internal.hpp"
 #include "p24_device.hpp"
 
 namespace p24 {
 
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BK = 64;       // logical K per main-loop iteration
-constexpr int XPAD = 32;     // bf16 elements of padding per LDS row of the X tile
+constexpr int NSTAGE = 3;    // LDS ring depth for the X tiles
 
 template <int BM, int BN, int WGM, int WGN>
 struct TileCfg {
-  static constexpr int NT = WGM * WGN * 64;        // threads per block
+  static constexpr int NWAVES = WGM * WGN;
+  static constexpr int NT = NWAVES * 64;           // threads per block
   static constexpr int WTM = BM / WGM;             // wave tile rows
   static constexpr int WTN = BN / WGN;             // wave tile cols
   static constexpr int TM = WTM / 32;              // 32x32 MFMA tiles per wave (rows)
   static constexpr int TN = WTN / 32;              // ... (cols)
-  static constexpr int LDX = BN + XPAD;            // LDS row pitch of the X tile (elements)
-  static constexpr int XCH = BK * BN / 8;          // 16 B chunks per X tile
-  static constexpr int XCH_PER_T = XCH / NT;
+  static constexpr int ROWB = BN * 2;              // bytes per LDS row of an X tile
+  static constexpr int CPR = BN / 8;               // 16 B chunks per row
+  static constexpr int STAGE_BYTES = BK * ROWB;
+  static constexpr int XCH = BK * CPR;             // 16 B chunks per X tile
+  static constexpr int XCH_PER_T = XCH / NT;       // direct-to-LDS loads per thread per tile
   static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "wave tiles must be multiples of 32");
   static_assert(XCH % NT == 0, "X tile chunks must divide evenly among threads");
+  static_assert(CPR >= 16, "the chunk swizzle needs at least 16 chunks per row");
 };
 
-// 4 consecutive k (rows kb..kb+3 of the LDS tile) for column (c0 + lane%16)
-// of a 16-lane group; see the ds_read_b64_tr_b16 lane map above.
-__device__ __forceinline__ i16x4 tr_read(const uint16_t* xs, int ldx, int kb, int c0, int lane) {
-  const int li = lane & 15;
-  const uint16_t* p = xs + (kb + (li >> 2)) * ldx + c0 + 4 * (li & 3);
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// XOR applied to the 16 B chunk index of row r.  Rows r..r+3 of one transposed
+// read land on 32 B bank groups {0,3,5,6} (x2 chunks): distinct both modulo 4
+// and (pairs) modulo 8 groups.
+__device__ __forceinline__ int chunk_swizzle(int r) {
+  const int q = r & 3;
+  return ((q << 1) | (__builtin_popcount(q) & 1)) << 1;
+}
+
+template <int OFF>
+__device__ __forceinline__ i16x4 ds_read_tr(uint32_t addr) {
+  i16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
 template <typename OutT> __device__ __forceinline__ void store_out(OutT* p, float v);
@@ -72,9 +112,10 @@ struct GemmArgs {
 template <int BM, int BN, int WGM, int WGN, bool SPARSE, bool GATHER, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   using C = TileCfg<BM, BN, WGM, WGN>;
-  constexpr int TM = C::TM, TN = C::TN, LDX = C::LDX;
+  constexpr int TM = C::TM, TN = C::TN;
   constexpr int ASTEPS = SPARSE ? 2 : 4;           // A fragments per K64 per row block
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][BK * LDX];
+  constexpr int A_LOADS = SPARSE ? TM * (ASTEPS + 1) : TM * ASTEPS;   // vector loads per A prefetch
+  __shared__ __attribute__((aligned(1024))) uint8_t xs[NSTAGE * C::STAGE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
@@ -92,13 +133,65 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 
   const int M = args.M, N = args.N, Kc = args.Kc;
   const int nk = Kc / BK;
-  const int rb0 = (m0 + wm * C::WTM) / 32;
   const int nrb = (M + 31) / 32;
   const int64_t S = SPARSE ? Kc / 32 : Kc / 16;    // A blocks per row block
   const int64_t T_ = Kc / 64;
+  const int n_hi = ((N + 7) & ~7) - 8;             // last 8-aligned column start inside the readable row
 
   const int32_t* kept_tile = nullptr;
   if constexpr (GATHER) kept_tile = args.kept + (int64_t)(m0 / args.tile_m) * Kc;
+
+  // ---- A operand pointers (row blocks past the matrix are clamped) ----
+  const uint16_t* a_ptr[TM];
+  const uint32_t* m_ptr[TM];
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+    int rb = (m0 + wm * C::WTM) / 32 + i;
+    rb = rb < nrb ? rb : nrb - 1;
+    a_ptr[i] = args.A + ((int64_t)rb * S * 64 + lane) * 8;
+    m_ptr[i] = SPARSE ? args.Ameta + (int64_t)rb * T_ * 64 + lane : nullptr;
+  }
+
+  // ---- X direct-to-LDS loads: this lane's chunk of each load instruction ----
+  // load j of this wave covers tile chunks [(j*NWAVES + wave)*64, +64); lane -> one chunk.
+  int x_row[C::XCH_PER_T], x_col[C::XCH_PER_T];
+#pragma unroll
+  for (int j = 0; j < C::XCH_PER_T; ++j) {
+    const int p = (j * C::NWAVES + wave) * 64 + lane;
+    const int r = p / C::CPR, cs = p % C::CPR;
+    const int c = cs ^ chunk_swizzle(r);
+    int col = n0 + 8 * c;
+    col = col <= n_hi ? col : n_hi;
+    x_row[j] = r;
+    x_col[j] = col;
+  }
+  const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_void*)xs;
+
+  // TVW: the gathered X rows of tile it+1 are read one iteration ahead of their
+  // direct-to-LDS loads (issued just before them), so waiting for the indices
+  // never waits for the X tile still in flight.
+  int k_cur[GATHER ? C::XCH_PER_T : 1], k_nxt[GATHER ? C::XCH_PER_T : 1];
+  auto load_kept = [&](int it, int (&kk)[GATHER ? C::XCH_PER_T : 1]) {
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int j = 0; j < C::XCH_PER_T; ++j) kk[j] = kept_tile[(int64_t)it * BK + x_row[j]];
+    }
+  };
+
+  auto issue_x = [&](int it, int stage, const int (&kk)[GATHER ? C::XCH_PER_T : 1]) {
+#pragma unroll
+    for (int j = 0; j < C::XCH_PER_T; ++j) {
+      int64_t gk = (int64_t)it * BK + x_row[j];
+      if constexpr (GATHER) {
+        int k = kk[j];
+        k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
+        gk = k;
+      }
+      const uint16_t* src = args.X + gk * args.ldx + x_col[j];
+      uint8_t* dst = xs + stage * C::STAGE_BYTES + (j * C::NWAVES + wave) * 64 * 16;
+      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+    }
+  };
 
   // ---- register state ----
   f32x16 acc[TM][TN];
@@ -109,128 +202,139 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 
   bf16x8 a_cur[TM][ASTEPS], a_nxt[TM][ASTEPS];
   uint32_t m_cur[TM], m_nxt[TM];
-  u32x4 xr[C::XCH_PER_T];
 
   auto load_a = [&](int it, bf16x8 (&a)[TM][ASTEPS], uint32_t (&mt)[TM]) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int rb = rb0 + i;
-      if (rb < nrb) {
 #pragma unroll
-        for (int s = 0; s < ASTEPS; ++s)
-          a[i][s] = *reinterpret_cast<const bf16x8*>(args.A + (((int64_t)rb * S + (int64_t)it * ASTEPS + s) * 64 + lane) * 8);
-        if constexpr (SPARSE) mt[i] = args.Ameta[((int64_t)rb * T_ + it) * 64 + lane];
-      } else {
-#pragma unroll
-        for (int s = 0; s < ASTEPS; ++s) a[i][s] = (bf16x8){};
-        mt[i] = 0x44444444u;
-      }
+      for (int s = 0; s < ASTEPS; ++s)
+        a[i][s] = *reinterpret_cast<const bf16x8*>(a_ptr[i] + ((int64_t)it * ASTEPS + s) * 512);
+      if constexpr (SPARSE) mt[i] = m_ptr[i][(int64_t)it * 64];
     }
   };
 
-  auto load_x = [&](int it) {
+  // per-lane part of the transposed-read address of B fragment j (see the lane map above)
+  const int li = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
+  uint32_t b_off[TN];
 #pragma unroll
-    for (int j = 0; j < C::XCH_PER_T; ++j) {
-      const int c = tid + j * C::NT;
-      const int r = c / (BN / 8), c8 = c % (BN / 8);
-      int64_t gk = (int64_t)it * BK + r;
-      if constexpr (GATHER) {
-        int kk = kept_tile[gk];
-        kk = kk < 0 ? 0 : (kk >= args.Kx ? args.Kx - 1 : kk);
-        gk = kk;
-      }
-      const int col = n0 + c8 * 8;
-      const uint16_t* src = args.X + gk * args.ldx + col;
-      if (col + 8 <= N) {
-        xr[j] = *reinterpret_cast<const u32x4*>(src);
-      } else {
-        uint32_t e[8];
+  for (int j = 0; j < TN; ++j) {
+    const int c = (wn * C::WTN) / 8 + 4 * j + 2 * g16 + ((li & 3) >> 1);
+    const int cs = c ^ chunk_swizzle(li >> 2);
+    b_off[j] = xs_base + (8 * h + (li >> 2)) * C::ROWB + cs * 16 + (li & 1) * 8;
+  }
+
+  // B fragments of one K step: sparse 32 k (4 transposed reads per fragment),
+  // dense 16 k (2 reads).  KB is the step's first tile row.
+  auto read_b_sparse = [&](auto KB, uint32_t stage_off, i16x16 (&bf)[TN]) {
+    constexpr int R = decltype(KB)::value * C::ROWB;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) e[q] = (col + q < N) ? (uint32_t)src[q] : 0u;
-        xr[j] = (u32x4){e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-      }
+    for (int j = 0; j < TN; ++j) {
+      const uint32_t a = b_off[j] + stage_off;
+      const i16x4 q0 = ds_read_tr<R>(a);
+      const i16x4 q1 = ds_read_tr<R + 4 * C::ROWB>(a);
+      const i16x4 q2 = ds_read_tr<R + 16 * C::ROWB>(a);
+      const i16x4 q3 = ds_read_tr<R + 20 * C::ROWB>(a);
+      const i16x8 lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+      const i16x8 hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+      bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
     }
   };
-
-  auto store_x = [&](int buf) {
+  auto read_b_dense = [&](auto KB, uint32_t stage_off, i16x8 (&bf)[TN]) {
+    constexpr int R = decltype(KB)::value * C::ROWB;
 #pragma unroll
-    for (int j = 0; j < C::XCH_PER_T; ++j) {
-      const int c = tid + j * C::NT;
-      const int r = c / (BN / 8), c8 = c % (BN / 8);
-      *reinterpret_cast<u32x4*>(&xs[buf][r * LDX + c8 * 8]) = xr[j];
+    for (int j = 0; j < TN; ++j) {
+      const uint32_t a = b_off[j] + stage_off;
+      const i16x4 q0 = ds_read_tr<R>(a);
+      const i16x4 q1 = ds_read_tr<R + 4 * C::ROWB>(a);
+      bf[j] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
     }
   };
+  // Wait for all LDS reads and tie the wait to the fragments that carry them.
+  auto wait_b16 = [&](i16x16 (&bf)[TN]) {
+    static_assert(TN <= 4, "wait helper covers up to 4 fragments");
+    if constexpr (TN == 4)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
+    else if constexpr (TN == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]));
+  };
+  auto wait_b8 = [&](i16x8 (&bf)[TN]) {
+    if constexpr (TN == 4)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
+    else if constexpr (TN == 2)
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]));
+  };
 
-  const int h = lane >> 5;                       // lane half
-  const int cgrp = 16 * ((lane >> 4) & 1);       // column offset of this lane's 16-lane group
-  const int wcol = wn * C::WTN;
-
-  auto compute = [&](int buf) {
-    const uint16_t* xb = xs[buf];
+  auto compute = [&](int stage) {
+    const uint32_t so = (uint32_t)(stage * C::STAGE_BYTES);
     if constexpr (SPARSE) {
+      i16x16 b0[TN], b1[TN];
+      read_b_sparse(std::integral_constant<int, 0>{}, so, b0);
+      wait_b16(b0);
+      read_b_sparse(std::integral_constant<int, 32>{}, so, b1);
 #pragma unroll
-      for (int ss = 0; ss < 2; ++ss) {
-        bf16x16 bfr[TN];
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int c0 = wcol + 32 * j + cgrp;
-          const int kb = 32 * ss + 8 * h;
-          const i16x4 q0 = tr_read(xb, LDX, kb, c0, lane);
-          const i16x4 q1 = tr_read(xb, LDX, kb + 4, c0, lane);
-          const i16x4 q2 = tr_read(xb, LDX, kb + 16, c0, lane);
-          const i16x4 q3 = tr_read(xb, LDX, kb + 20, c0, lane);
-          const i16x8 lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const i16x8 hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
-          const i16x16 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-          bfr[j] = __builtin_bit_cast(bf16x16, v);
-        }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a_cur[i][0], __builtin_bit_cast(bf16x16, b0[j]),
+                                                                acc[i][j], (int)m_cur[i], 0, 0);
+      wait_b16(b1);
 #pragma unroll
-        for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            if (ss == 0)
-              acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a_cur[i][0], bfr[j], acc[i][j], (int)m_cur[i], 0, 0);
-            else
-              acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a_cur[i][1], bfr[j], acc[i][j], (int)m_cur[i], 0, 1);
-          }
-      }
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a_cur[i][1], __builtin_bit_cast(bf16x16, b1[j]),
+                                                                acc[i][j], (int)m_cur[i], 0, 1);
     } else {
-#pragma unroll
-      for (int ss = 0; ss < 4; ++ss) {
-        bf16x8 bfr[TN];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int c0 = wcol + 32 * j + cgrp;
-          const int kb = 16 * ss + 8 * h;
-          const i16x4 q0 = tr_read(xb, LDX, kb, c0, lane);
-          const i16x4 q1 = tr_read(xb, LDX, kb + 4, c0, lane);
-          bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7));
-        }
+      i16x8 bb[2][TN];
+      read_b_dense(std::integral_constant<int, 0>{}, so, bb[0]);
+      static_for<0, 4>([&](auto SS) {
+        constexpr int ss = decltype(SS)::value;
+        wait_b8(bb[ss & 1]);
+        if constexpr (ss + 1 < 4) read_b_dense(std::integral_constant<int, 16 * (ss + 1)>{}, so, bb[(ss + 1) & 1]);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i][ss], bfr[j], acc[i][j], 0, 0, 0);
-      }
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i][ss], __builtin_bit_cast(bf16x8, bb[ss & 1][j]),
+                                                                acc[i][j], 0, 0, 0);
+      });
     }
   };
 
-  // ---- main loop: one barrier per iteration, X double-buffered in LDS ----
-  load_x(0);
+  // ---- main loop ----
+  // Issue order per iteration it: [wait X(it); barrier; X(it+2) -> stage (it+2)%3;
+  // A(it+1) -> registers; compute(it)].  Vector-memory counters retire in issue
+  // order, so "X(it) has landed" is vmcnt <= (loads issued after it), which is at
+  // least |X(it+1)| + |A(it)| while a next tile exists and |A(it)| at the last.
+  load_kept(0, k_cur);
+  issue_x(0, 0, k_cur);
+  if (nk > 1) {
+    load_kept(1, k_cur);
+    issue_x(1, 1, k_cur);
+  }
+  if (nk > 2) load_kept(2, k_cur);
   load_a(0, a_cur, m_cur);
-  store_x(0);
-  __syncthreads();
   for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    const bool more = it + 1 < nk;
-    if (more) {
-      load_x(it + 1);
-      load_a(it + 1, a_nxt, m_nxt);
+    if (it + 1 < nk)
+      wait_vmcnt<C::XCH_PER_T + A_LOADS>();
+    else
+      wait_vmcnt<A_LOADS>();
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (it + 3 < nk) load_kept(it + 3, k_nxt);
+    if (it + 2 < nk) issue_x(it + 2, (it + 2) % NSTAGE, k_cur);
+    if (it + 1 < nk) load_a(it + 1, a_nxt, m_nxt);
+    asm volatile("" ::: "memory");
+    compute(it % NSTAGE);
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int j = 0; j < C::XCH_PER_T; ++j) k_cur[j] = k_nxt[j];
     }
-    compute(cur);
-    if (more) store_x(cur ^ 1);
-    __syncthreads();
-    if (more) {
+    if (it + 1 < nk) {
 #pragma unroll
       for (int i = 0; i < TM; ++i) {
         m_cur[i] = m_nxt[i];
@@ -243,7 +347,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // ---- epilogue ----
   OutT* Y = reinterpret_cast<OutT*>(args.Y);
   const int row_w = m0 + wm * C::WTM;
-  const int col_l = n0 + wcol + (lane & 31);
+  const int col_l = n0 + wn * C::WTN + (lane & 31);
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
