@@ -127,6 +127,9 @@ P24_API p24_status prune24_decompress(const void* values, const void* meta, int3
  *                 reads directly; other layouts return P24_ERR_LAYOUT).
  *   M, K          logical shape of W; K % 64 == 0 (else P24_ERR_UNSUPPORTED).
  *   X             K x N bf16, leading dim ldx >= N, ldx % 8 == 0, 16 B aligned.
+ *                 The kernel reads X in 16 B pieces: when N % 8 != 0 the last
+ *                 row must stay readable up to column roundup(N, 8) - 1 (any
+ *                 values there are ignored).
  *   Y             M x N, y_dtype P24_F32 or P24_BF16 (round to nearest even),
  *                 leading dim ldy >= N, naturally aligned.
  *   algo          P24_ALGO_AUTO or P24_ALGO_SMFMAC (same kernel family).

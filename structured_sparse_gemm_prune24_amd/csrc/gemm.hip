@@ -3,29 +3,32 @@
 // dense bf16 baseline on v_mfma_f32_32x32x16_bf16.
 //
 // Data flow per block (BM x BN outputs, K consumed 64 logical columns at a time):
+//   * Both operands stream global -> LDS with direct-to-LDS loads
+//     (global_load_lds_dwordx4 / _dword: lane l writes its 16 / 4 bytes at the
+//     wave's LDS base + l * size) into a ring of LDS stages, NSTAGE-1 K steps
+//     ahead of the compute.  No register holds data in flight, so the
+//     accumulators own the register file.
 //   * W operand: the compressed values / metadata (or the packed dense W) are
-//     stored in MFMA operand order, so each wave loads its A fragments straight
-//     from global memory into registers, one contiguous 1 KiB (values) or
-//     256 B (metadata) block per wave and load.  No LDS is spent on W.  The
-//     fragments of iteration it+1 are in flight while iteration it computes.
-//   * X operand: 64 x BN tiles (row-major, N contiguous) go global -> LDS with
-//     direct-to-LDS loads (global_load_lds_dwordx4: lane l writes its 16 B at
-//     the wave's LDS base + 16 l), into a ring of three LDS stages, two tiles
-//     ahead of the compute.  Rows are whole N-slices, so the TVW gather only
-//     changes the global row a slice comes from.  Inside a row the 16 B chunks
-//     are XOR-swizzled by the row's low bits so that the transposed reads below
-//     spread over all LDS banks.
+//     stored in MFMA operand order, so one K step of one 32-row block is a
+//     contiguous 1 KiB (values) or 256 B (metadata) run in memory, in LDS, and
+//     in the wave's registers (lane l reads 16 B at +16 l).
+//   * X operand: 64 x BN tiles, row-major (N contiguous).  Rows are whole
+//     N-slices, so the TVW gather only changes the global row a slice comes
+//     from.  Inside an LDS row the 16 B chunks are XOR-swizzled by the row's
+//     low bits so that the transposed reads spread over all LDS banks.
 //   * B fragments come out of LDS with ds_read_b64_tr_b16: within a group of
 //     16 lanes, lane i receives element i%4 of the 8-byte pieces addressed by
 //     lanes 4e + i/4 (e = 0..3), i.e. 4 consecutive k of one column when the
-//     16 lanes address a 4-row x 16-column sub-tile.  These reads are issued as
-//     inline asm with explicit lgkmcnt waits tied to the fragments: the
-//     compiler would otherwise stall every LDS read on all outstanding
-//     direct-to-LDS loads.
+//     16 lanes address a 4-row x 16-column sub-tile.
+//   * Every LDS read is inline asm followed by an explicit lgkmcnt wait tied
+//     to the registers it fills: the compiler would otherwise stall each LDS
+//     read on all outstanding direct-to-LDS loads.  The direct-to-LDS loads are
+//     waited for explicitly (vmcnt, which retires in issue order) before the
+//     block barrier that publishes a stage.
 //   * Tails: addresses are clamped instead of branched on.  Columns of X at or
-//     beyond N only feed output columns that are never stored, and rows past M
-//     only feed rows that are never stored, so the clamped (valid) data there
-//     is harmless.
+//     beyond N only feed output columns that are never stored, rows past M
+//     only feed rows that are never stored, and K steps past the end are
+//     loaded into stages that are never read, so every count is static.
 //   * Accumulators stay in registers for the whole K loop; the epilogue rounds
 //     (fp32 -> bf16 RNE) or stores fp32 with row-contiguous lane groups.
 #include <cstdlib>
@@ -41,10 +44,10 @@ typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int BK = 64;       // logical K per main-loop iteration
-constexpr int NSTAGE = 3;    // LDS ring depth for the X tiles
+constexpr int BK = 64;                 // logical K per main-loop iteration
+constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
 
-template <int BM, int BN, int WGM, int WGN>
+template <int BM, int BN, int WGM, int WGN, bool SPARSE>
 struct TileCfg {
   static constexpr int NWAVES = WGM * WGN;
   static constexpr int NT = NWAVES * 64;           // threads per block
@@ -52,14 +55,27 @@ struct TileCfg {
   static constexpr int WTN = BN / WGN;             // wave tile cols
   static constexpr int TM = WTM / 32;              // 32x32 MFMA tiles per wave (rows)
   static constexpr int TN = WTN / 32;              // ... (cols)
+  static constexpr int RB = BM / 32;               // 32-row blocks per block
+  static constexpr int ASTEPS = SPARSE ? 2 : 4;    // 1 KiB A blocks per row block per K step
+  // stage layout: [X tile | A blocks | metadata blocks]
   static constexpr int ROWB = BN * 2;              // bytes per LDS row of an X tile
-  static constexpr int CPR = BN / 8;               // 16 B chunks per row
-  static constexpr int STAGE_BYTES = BK * ROWB;
-  static constexpr int XCH = BK * CPR;             // 16 B chunks per X tile
-  static constexpr int XCH_PER_T = XCH / NT;       // direct-to-LDS loads per thread per tile
+  static constexpr int CPR = BN / 8;               // 16 B chunks per X row
+  static constexpr int X_BYTES = BK * ROWB;
+  static constexpr int A_BYTES = RB * ASTEPS * 1024;
+  static constexpr int M_BYTES = SPARSE ? RB * 256 : 0;
+  static constexpr int STAGE = X_BYTES + A_BYTES + M_BYTES;
+  static constexpr int NSTAGE = 3 * STAGE <= LDS_LIMIT ? 3 : 2;
+  // direct-to-LDS loads per wave per K step (each moves 1 KiB, or 256 B for metadata)
+  static constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
+  static constexpr int A_DMA = A_BYTES / 1024 / NWAVES;
+  static constexpr int M_DMA = SPARSE ? RB / NWAVES : 0;
+  static constexpr int DMA = X_DMA + A_DMA + M_DMA;
   static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "wave tiles must be multiples of 32");
-  static_assert(XCH % NT == 0, "X tile chunks must divide evenly among threads");
+  static_assert(X_BYTES % (1024 * NWAVES) == 0 && A_BYTES % (1024 * NWAVES) == 0, "even load split");
+  static_assert(!SPARSE || RB % NWAVES == 0, "metadata loads must split evenly among waves");
   static_assert(CPR >= 16, "the chunk swizzle needs at least 16 chunks per row");
+  static_assert(2 * STAGE <= LDS_LIMIT, "two stages must fit in LDS");
+  static_assert(DMA < 64, "vmcnt range");
 };
 
 template <int I, int N, typename F>
@@ -70,18 +86,30 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-// XOR applied to the 16 B chunk index of row r.  Rows r..r+3 of one transposed
-// read land on 32 B bank groups {0,3,5,6} (x2 chunks): distinct both modulo 4
-// and (pairs) modulo 8 groups.
+// XOR applied to the 16 B chunk index of X-tile row r.  The 4 rows of one
+// transposed read land on 32 B bank groups {0,3,5,6} (x2 chunks): distinct
+// both modulo 4 and, as pairs, modulo 8 groups.
 __device__ __forceinline__ int chunk_swizzle(int r) {
   const int q = r & 3;
   return ((q << 1) | (__builtin_popcount(q) & 1)) << 1;
 }
 
 template <int OFF>
-__device__ __forceinline__ i16x4 ds_read_tr(uint32_t addr) {
+__device__ __forceinline__ i16x4 lds_read_tr(uint32_t addr) {
   i16x4 v;
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ i16x8 lds_read_b128(uint32_t addr) {
+  i16x8 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+  return v;
+}
+template <int OFF>
+__device__ __forceinline__ uint32_t lds_read_b32(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
   return v;
 }
 
@@ -89,6 +117,17 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// lgkmcnt(0) tied to the registers that carry the LDS reads: every use of
+// those registers is ordered after the wait.
+template <typename T, int N>
+__device__ __forceinline__ void wait_lds(T (&r)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
 }
 
 template <typename OutT> __device__ __forceinline__ void store_out(OutT* p, float v);
@@ -109,15 +148,27 @@ struct GemmArgs {
   int nbm, nbn;            // block grid
 };
 
+// Buffer resource over [base, base + bytes): raw (untyped) loads, no swizzle.
+// Loads past `bytes` return zero instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void dma16_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_dst, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, voff, soff, 0, 0);
+}
+
 template <int BM, int BN, int WGM, int WGN, bool SPARSE, bool GATHER, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
-  using C = TileCfg<BM, BN, WGM, WGN>;
-  constexpr int TM = C::TM, TN = C::TN;
-  constexpr int ASTEPS = SPARSE ? 2 : 4;           // A fragments per K64 per row block
-  constexpr int A_LOADS = SPARSE ? TM * (ASTEPS + 1) : TM * ASTEPS;   // vector loads per A prefetch
-  __shared__ __attribute__((aligned(1024))) uint8_t xs[NSTAGE * C::STAGE_BYTES];
+  using C = TileCfg<BM, BN, WGM, WGN, SPARSE>;
+  constexpr int TM = C::TM, TN = C::TN, ASTEPS = C::ASTEPS, NSTAGE = C::NSTAGE;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * C::STAGE];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
   // ---- block -> output tile (XCD-aware, grouped raster) ----
@@ -134,214 +185,232 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   const int M = args.M, N = args.N, Kc = args.Kc;
   const int nk = Kc / BK;
   const int nrb = (M + 31) / 32;
+  const int rb0 = m0 / 32;
   const int64_t S = SPARSE ? Kc / 32 : Kc / 16;    // A blocks per row block
   const int64_t T_ = Kc / 64;
   const int n_hi = ((N + 7) & ~7) - 8;             // last 8-aligned column start inside the readable row
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+  const int64_t ldx = args.ldx;
+
+  // ---- direct-to-LDS load plan ----
+  // X: load j of this wave fills tile chunks [(j*NWAVES + wave)*64, +64), one
+  // per lane.  A 64-lane load covers 64/CPR whole rows, so the chunk position
+  // inside the row (hence the swizzled source column) is the same for every j
+  // and the row advances by a fixed multiple of 4: one per-lane offset plus a
+  // scalar stride covers every load.
+  static_assert(C::CPR % 32 == 0 || 64 % C::CPR == 0, "row/chunk split of a 64-lane load");
+  constexpr int X_ROWS_PER_LOAD = 64 / C::CPR > 0 ? 64 / C::CPR : 1;     // rows one 64-lane load covers
+  constexpr int X_LOADS_PER_ROW = C::CPR / 64 > 0 ? C::CPR / 64 : 1;     // loads per row when CPR > 64
+  static_assert(X_LOADS_PER_ROW == 1, "BN <= 512");
+  const int p0 = wave * 64 + lane;                   // chunk of load j = 0
+  const int x_r0 = p0 / C::CPR;                      // its tile row; load j adds j * NWAVES * X_ROWS_PER_LOAD rows
+  int x_col = n0 + 8 * ((p0 % C::CPR) ^ chunk_swizzle(x_r0));
+  x_col = x_col <= n_hi ? x_col : n_hi;
+  constexpr int X_ROW_STEP = C::NWAVES * X_ROWS_PER_LOAD;   // multiple of 4: the swizzle of row x_r0 holds for all j
+  static_assert(X_ROW_STEP % 4 == 0, "X row step must keep the swizzle phase");
+  const uint32_t x_voff = GATHER ? (uint32_t)x_col * 2 : (uint32_t)(x_r0 * ldx + x_col) * 2;
+  // A values / metadata: load j fills the (row block, step) block q = j*NWAVES + wave
+  // (metadata: row block q) of the stage.  Only the lane part of the address is
+  // per lane; the block part is wave-uniform and goes into the scalar offset.
+  // Row blocks past the matrix read past the resource end and come back as zeros.
+  const uint32_t a_voff = (uint32_t)lane * 16;
+  const uint32_t m_voff = (uint32_t)lane * 4;
+  auto a_block_off = [&](int j) -> uint32_t {
+    const int q = j * C::NWAVES + wave;
+    return (uint32_t)(((q / ASTEPS) * S + q % ASTEPS) * 1024);
+  };
+  auto m_block_off = [&](int j) -> uint32_t { return (uint32_t)((j * C::NWAVES + wave) * T_ * 256); };
+  const int rb_end = nrb < rb0 + C::RB ? nrb : rb0 + C::RB;
+  const __amdgpu_buffer_rsrc_t a_rsrc =
+      make_rsrc(args.A + (int64_t)rb0 * S * 512, (uint32_t)((rb_end - rb0) * S * 1024));
+  const __amdgpu_buffer_rsrc_t m_rsrc =
+      SPARSE ? make_rsrc(args.Ameta + (int64_t)rb0 * T_ * 64, (uint32_t)((rb_end - rb0) * T_ * 256)) : a_rsrc;
+  // TVW: whole-X resource (the host guarantees it spans < 4 GiB)
+  const __amdgpu_buffer_rsrc_t xg_rsrc = make_rsrc(args.X, (uint32_t)(GATHER ? (int64_t)args.Kx * ldx * 2 : 0));
 
   const int32_t* kept_tile = nullptr;
   if constexpr (GATHER) kept_tile = args.kept + (int64_t)(m0 / args.tile_m) * Kc;
-
-  // ---- A operand pointers (row blocks past the matrix are clamped) ----
-  const uint16_t* a_ptr[TM];
-  const uint32_t* m_ptr[TM];
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
-    int rb = (m0 + wm * C::WTM) / 32 + i;
-    rb = rb < nrb ? rb : nrb - 1;
-    a_ptr[i] = args.A + ((int64_t)rb * S * 64 + lane) * 8;
-    m_ptr[i] = SPARSE ? args.Ameta + (int64_t)rb * T_ * 64 + lane : nullptr;
-  }
-
-  // ---- X direct-to-LDS loads: this lane's chunk of each load instruction ----
-  // load j of this wave covers tile chunks [(j*NWAVES + wave)*64, +64); lane -> one chunk.
-  int x_row[C::XCH_PER_T], x_col[C::XCH_PER_T];
-#pragma unroll
-  for (int j = 0; j < C::XCH_PER_T; ++j) {
-    const int p = (j * C::NWAVES + wave) * 64 + lane;
-    const int r = p / C::CPR, cs = p % C::CPR;
-    const int c = cs ^ chunk_swizzle(r);
-    int col = n0 + 8 * c;
-    col = col <= n_hi ? col : n_hi;
-    x_row[j] = r;
-    x_col[j] = col;
-  }
-  const uint32_t xs_base = (uint32_t)(uintptr_t)(lds_void*)xs;
-
-  // TVW: the gathered X rows of tile it+1 are read one iteration ahead of their
-  // direct-to-LDS loads (issued just before them), so waiting for the indices
-  // never waits for the X tile still in flight.
-  int k_cur[GATHER ? C::XCH_PER_T : 1], k_nxt[GATHER ? C::XCH_PER_T : 1];
-  auto load_kept = [&](int it, int (&kk)[GATHER ? C::XCH_PER_T : 1]) {
+  // TVW: the gathered X rows of step g are read one step before their loads
+  // are issued (and are issued before them), so waiting for the indices never
+  // waits for a tile in flight.
+  int k_cur[GATHER ? C::X_DMA : 1], k_nxt[GATHER ? C::X_DMA : 1];
+  auto load_kept = [&](int g, int (&kk)[GATHER ? C::X_DMA : 1]) {
     if constexpr (GATHER) {
 #pragma unroll
-      for (int j = 0; j < C::XCH_PER_T; ++j) kk[j] = kept_tile[(int64_t)it * BK + x_row[j]];
+      for (int j = 0; j < C::X_DMA; ++j) kk[j] = kept_tile[(int64_t)g * BK + x_r0 + j * X_ROW_STEP];
     }
   };
 
-  auto issue_x = [&](int it, int stage, const int (&kk)[GATHER ? C::XCH_PER_T : 1]) {
+  // all direct-to-LDS loads of K step g into stage st
+  auto issue_step = [&](int g, int st) {
+    uint8_t* stage = lds + st * C::STAGE;
+    if constexpr (GATHER) {
 #pragma unroll
-    for (int j = 0; j < C::XCH_PER_T; ++j) {
-      int64_t gk = (int64_t)it * BK + x_row[j];
-      if constexpr (GATHER) {
-        int k = kk[j];
+      for (int j = 0; j < C::X_DMA; ++j) {
+        int k = k_cur[j];
         k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
-        gk = k;
+        dma16_to_lds(xg_rsrc, stage + (j * C::NWAVES + wave) * 1024, (uint32_t)(k * ldx * 2) + x_voff, 0);
       }
-      const uint16_t* src = args.X + gk * args.ldx + x_col[j];
-      uint8_t* dst = xs + stage * C::STAGE_BYTES + (j * C::NWAVES + wave) * 64 * 16;
-      __builtin_amdgcn_global_load_lds((const void*)src, (lds_void*)dst, 16, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t xr = make_rsrc(args.X + (int64_t)g * BK * ldx, (uint32_t)(BK * ldx * 2));
+#pragma unroll
+      for (int j = 0; j < C::X_DMA; ++j)
+        dma16_to_lds(xr, stage + (j * C::NWAVES + wave) * 1024, x_voff, (uint32_t)(j * X_ROW_STEP * ldx * 2));
+    }
+#pragma unroll
+    for (int j = 0; j < C::A_DMA; ++j)
+      dma16_to_lds(a_rsrc, stage + C::X_BYTES + (j * C::NWAVES + wave) * 1024, a_voff,
+                   (uint32_t)g * ASTEPS * 1024 + a_block_off(j));
+    if constexpr (SPARSE) {
+#pragma unroll
+      for (int j = 0; j < C::M_DMA; ++j)
+        dma4_to_lds(m_rsrc, stage + C::X_BYTES + C::A_BYTES + (j * C::NWAVES + wave) * 256, m_voff,
+                    (uint32_t)g * 256 + m_block_off(j));
     }
   };
 
-  // ---- register state ----
+  // ---- LDS read addresses, one set per stage ----
+  const int li = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
+  uint32_t b_off[NSTAGE][TN], a_off[NSTAGE], m_off[NSTAGE];
+#pragma unroll
+  for (int st = 0; st < NSTAGE; ++st) {
+    const uint32_t base = lds_base + st * C::STAGE;
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const int c = (wn * C::WTN) / 8 + 4 * j + 2 * g16 + ((li & 3) >> 1);
+      const int cs = c ^ chunk_swizzle(li >> 2);
+      b_off[st][j] = base + (8 * h + (li >> 2)) * C::ROWB + cs * 16 + (li & 1) * 8;
+    }
+    a_off[st] = base + C::X_BYTES + wm * TM * ASTEPS * 1024 + lane * 16;
+    m_off[st] = base + C::X_BYTES + C::A_BYTES + wm * TM * 256 + lane * 4;
+  }
+
   f32x16 acc[TM][TN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
-  bf16x8 a_cur[TM][ASTEPS], a_nxt[TM][ASTEPS];
-  uint32_t m_cur[TM], m_nxt[TM];
-
-  auto load_a = [&](int it, bf16x8 (&a)[TM][ASTEPS], uint32_t (&mt)[TM]) {
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
-#pragma unroll
-      for (int s = 0; s < ASTEPS; ++s)
-        a[i][s] = *reinterpret_cast<const bf16x8*>(a_ptr[i] + ((int64_t)it * ASTEPS + s) * 512);
-      if constexpr (SPARSE) mt[i] = m_ptr[i][(int64_t)it * 64];
-    }
-  };
-
-  // per-lane part of the transposed-read address of B fragment j (see the lane map above)
-  const int li = lane & 15, h = lane >> 5, g16 = (lane >> 4) & 1;
-  uint32_t b_off[TN];
-#pragma unroll
-  for (int j = 0; j < TN; ++j) {
-    const int c = (wn * C::WTN) / 8 + 4 * j + 2 * g16 + ((li & 3) >> 1);
-    const int cs = c ^ chunk_swizzle(li >> 2);
-    b_off[j] = xs_base + (8 * h + (li >> 2)) * C::ROWB + cs * 16 + (li & 1) * 8;
-  }
-
-  // B fragments of one K step: sparse 32 k (4 transposed reads per fragment),
-  // dense 16 k (2 reads).  KB is the step's first tile row.
-  auto read_b_sparse = [&](auto KB, uint32_t stage_off, i16x16 (&bf)[TN]) {
-    constexpr int R = decltype(KB)::value * C::ROWB;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const uint32_t a = b_off[j] + stage_off;
-      const i16x4 q0 = ds_read_tr<R>(a);
-      const i16x4 q1 = ds_read_tr<R + 4 * C::ROWB>(a);
-      const i16x4 q2 = ds_read_tr<R + 16 * C::ROWB>(a);
-      const i16x4 q3 = ds_read_tr<R + 20 * C::ROWB>(a);
-      const i16x8 lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-      const i16x8 hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
-      bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-    }
-  };
-  auto read_b_dense = [&](auto KB, uint32_t stage_off, i16x8 (&bf)[TN]) {
-    constexpr int R = decltype(KB)::value * C::ROWB;
-#pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const uint32_t a = b_off[j] + stage_off;
-      const i16x4 q0 = ds_read_tr<R>(a);
-      const i16x4 q1 = ds_read_tr<R + 4 * C::ROWB>(a);
-      bf[j] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-    }
-  };
-  // Wait for all LDS reads and tie the wait to the fragments that carry them.
-  auto wait_b16 = [&](i16x16 (&bf)[TN]) {
-    static_assert(TN <= 4, "wait helper covers up to 4 fragments");
-    if constexpr (TN == 4)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
-    else if constexpr (TN == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]));
-    else
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]));
-  };
-  auto wait_b8 = [&](i16x8 (&bf)[TN]) {
-    if constexpr (TN == 4)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]), "+v"(bf[2]), "+v"(bf[3]));
-    else if constexpr (TN == 2)
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]), "+v"(bf[1]));
-    else
-      asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(bf[0]));
-  };
-
-  auto compute = [&](int stage) {
-    const uint32_t so = (uint32_t)(stage * C::STAGE_BYTES);
+  // One K step on stage ST.
+  auto compute = [&](auto ST) {
+    constexpr int st = decltype(ST)::value;
     if constexpr (SPARSE) {
+      uint32_t meta[TM];
+      i16x8 a0[TM], a1[TM];
       i16x16 b0[TN], b1[TN];
-      read_b_sparse(std::integral_constant<int, 0>{}, so, b0);
-      wait_b16(b0);
-      read_b_sparse(std::integral_constant<int, 32>{}, so, b1);
+      // fragments of k 0..31 (abid 0) and 32..63 (abid 1)
+      auto read_a = [&](auto SS, i16x8 (&a)[TM]) {
+        static_for<0, TM>([&](auto I) {
+          a[decltype(I)::value] =
+              lds_read_b128<(decltype(I)::value * ASTEPS + decltype(SS)::value) * 1024>(a_off[st]);
+        });
+      };
+      auto read_b = [&](auto SS, i16x16 (&bf)[TN]) {
+        constexpr int R = 32 * decltype(SS)::value * C::ROWB;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const uint32_t ad = b_off[st][j];
+          const i16x4 q0 = lds_read_tr<R>(ad);
+          const i16x4 q1 = lds_read_tr<R + 4 * C::ROWB>(ad);
+          const i16x4 q2 = lds_read_tr<R + 16 * C::ROWB>(ad);
+          const i16x4 q3 = lds_read_tr<R + 20 * C::ROWB>(ad);
+          const i16x8 lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+          const i16x8 hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+          bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+        }
+      };
+      static_for<0, TM>([&](auto I) { meta[decltype(I)::value] = lds_read_b32<decltype(I)::value * 256>(m_off[st]); });
+      read_a(std::integral_constant<int, 0>{}, a0);
+      read_b(std::integral_constant<int, 0>{}, b0);
+      wait_lds(meta);
+      wait_lds(a0);
+      wait_lds(b0);
+      read_a(std::integral_constant<int, 1>{}, a1);
+      read_b(std::integral_constant<int, 1>{}, b1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a_cur[i][0], __builtin_bit_cast(bf16x16, b0[j]),
-                                                                acc[i][j], (int)m_cur[i], 0, 0);
-      wait_b16(b1);
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a0[i]),
+                                                                __builtin_bit_cast(bf16x16, b0[j]), acc[i][j],
+                                                                (int)meta[i], 0, 0);
+      wait_lds(a1);
+      wait_lds(b1);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a_cur[i][1], __builtin_bit_cast(bf16x16, b1[j]),
-                                                                acc[i][j], (int)m_cur[i], 0, 1);
+          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a1[i]),
+                                                                __builtin_bit_cast(bf16x16, b1[j]), acc[i][j],
+                                                                (int)meta[i], 0, 1);
     } else {
-      i16x8 bb[2][TN];
-      read_b_dense(std::integral_constant<int, 0>{}, so, bb[0]);
+      i16x8 a[2][TM], bb[2][TN];
+      auto read_step = [&](auto SS) {
+        constexpr int ss = decltype(SS)::value;
+        static_for<0, TM>([&](auto I) {
+          a[ss & 1][decltype(I)::value] = lds_read_b128<(decltype(I)::value * ASTEPS + ss) * 1024>(a_off[st]);
+        });
+        constexpr int R = 16 * ss * C::ROWB;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const uint32_t ad = b_off[st][j];
+          const i16x4 q0 = lds_read_tr<R>(ad);
+          const i16x4 q1 = lds_read_tr<R + 4 * C::ROWB>(ad);
+          bb[ss & 1][j] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      read_step(std::integral_constant<int, 0>{});
       static_for<0, 4>([&](auto SS) {
         constexpr int ss = decltype(SS)::value;
-        wait_b8(bb[ss & 1]);
-        if constexpr (ss + 1 < 4) read_b_dense(std::integral_constant<int, 16 * (ss + 1)>{}, so, bb[(ss + 1) & 1]);
+        wait_lds(a[ss & 1]);
+        wait_lds(bb[ss & 1]);
+        if constexpr (ss + 1 < 4) read_step(std::integral_constant<int, ss + 1>{});
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
           for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_cur[i][ss], __builtin_bit_cast(bf16x8, bb[ss & 1][j]),
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ss & 1][i]),
+                                                                __builtin_bit_cast(bf16x8, bb[ss & 1][j]),
                                                                 acc[i][j], 0, 0, 0);
       });
     }
   };
 
   // ---- main loop ----
-  // Issue order per iteration it: [wait X(it); barrier; X(it+2) -> stage (it+2)%3;
-  // A(it+1) -> registers; compute(it)].  Vector-memory counters retire in issue
-  // order, so "X(it) has landed" is vmcnt <= (loads issued after it), which is at
-  // least |X(it+1)| + |A(it)| while a next tile exists and |A(it)| at the last.
+  // Step g is loaded into stage g % NSTAGE by the loads issued NSTAGE-1 steps
+  // earlier.  At the top of step it the loads of steps it+1 .. it+NSTAGE-2 may
+  // still be in flight (vmcnt retires in issue order), then the barrier makes
+  // every wave's part of stage it visible and guarantees that no wave still
+  // reads the stage about to be refilled.  Steps past the end reload the last
+  // step into a stage that is never read, so the counts stay static.  The loop
+  // is unrolled by NSTAGE so every stage address is fixed at compile time.
   load_kept(0, k_cur);
-  issue_x(0, 0, k_cur);
-  if (nk > 1) {
-    load_kept(1, k_cur);
-    issue_x(1, 1, k_cur);
+  issue_step(0, 0);
+#pragma unroll
+  for (int g = 1; g < NSTAGE - 1; ++g) {
+    load_kept(min(g, nk - 1), k_cur);
+    issue_step(min(g, nk - 1), g);
   }
-  if (nk > 2) load_kept(2, k_cur);
-  load_a(0, a_cur, m_cur);
-  for (int it = 0; it < nk; ++it) {
-    if (it + 1 < nk)
-      wait_vmcnt<C::XCH_PER_T + A_LOADS>();
-    else
-      wait_vmcnt<A_LOADS>();
+  load_kept(min(NSTAGE - 1, nk - 1), k_cur);
+  auto body = [&](auto ST, int it) {
+    constexpr int st = decltype(ST)::value;
+    wait_vmcnt<(NSTAGE - 2) * C::DMA>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (it + 3 < nk) load_kept(it + 3, k_nxt);
-    if (it + 2 < nk) issue_x(it + 2, (it + 2) % NSTAGE, k_cur);
-    if (it + 1 < nk) load_a(it + 1, a_nxt, m_nxt);
+    const int gn = it + NSTAGE - 1;
+    load_kept(min(gn + 1, nk - 1), k_nxt);
+    issue_step(min(gn, nk - 1), (st + NSTAGE - 1) % NSTAGE);
     asm volatile("" ::: "memory");
-    compute(it % NSTAGE);
+    compute(ST);
     if constexpr (GATHER) {
 #pragma unroll
-      for (int j = 0; j < C::XCH_PER_T; ++j) k_cur[j] = k_nxt[j];
+      for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
     }
-    if (it + 1 < nk) {
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        m_cur[i] = m_nxt[i];
-#pragma unroll
-        for (int s = 0; s < ASTEPS; ++s) a_cur[i][s] = a_nxt[i][s];
-      }
-    }
+  };
+  for (int it = 0; it < nk; it += NSTAGE) {
+    static_for<0, NSTAGE>([&](auto ST) {
+      if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
+    });
   }
 
   // ---- epilogue ----
