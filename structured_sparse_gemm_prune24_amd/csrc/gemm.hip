@@ -413,6 +413,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     });
   }
 
+  // The last NSTAGE-1 steps issued loads into stages that are never read; they
+  // must land before the block ends and its LDS is handed to another block.
+  wait_vmcnt<0>();
+
   // ---- epilogue ----
   OutT* Y = reinterpret_cast<OutT*>(args.Y);
   const int row_w = m0 + wm * C::WTM;
@@ -478,8 +482,15 @@ static Tile choose_tile(int64_t M, int64_t N) {
 template <bool SPARSE>
 static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
   switch (choose_tile(a.M, a.N)) {
-    case Tile::T256x256: return launch_cfg<256, 256, 2, 2, SPARSE, false>(a, y_dtype, st);
-    case Tile::T128x256: return launch_cfg<128, 256, 2, 2, SPARSE, false>(a, y_dtype, st);
+    // Sparse tiles use one wave row (each wave: all BM rows x BN/4 columns): the
+    // B fragments, read with the slower transposing LDS reads, then feed BM/32
+    // MFMAs each.  The dense tile keeps 2 x 2 waves, whose register budget fits.
+    case Tile::T256x256:
+      if constexpr (SPARSE) return launch_cfg<256, 256, 1, 4, SPARSE, false>(a, y_dtype, st);
+      else return launch_cfg<256, 256, 2, 2, SPARSE, false>(a, y_dtype, st);
+    case Tile::T128x256:
+      if constexpr (SPARSE) return launch_cfg<128, 256, 1, 4, SPARSE, false>(a, y_dtype, st);
+      else return launch_cfg<128, 256, 2, 2, SPARSE, false>(a, y_dtype, st);
     case Tile::T128x128: return launch_cfg<128, 128, 2, 2, SPARSE, false>(a, y_dtype, st);
     case Tile::T64x128: return launch_cfg<64, 128, 1, 2, SPARSE, false>(a, y_dtype, st);
   }
@@ -565,7 +576,7 @@ extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, 
   a.Kx = (int)K;
   a.tile_m = (int)tile_m;
   // one block row = one 128-row slice of a TVW tile
-  return launch_cfg<128, 256, 2, 2, true, true>(a, y_dtype, (hipStream_t)stream);
+  return launch_cfg<128, 256, 1, 4, true, true>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
