@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["spmm", "dense", "compress", "tvw", "copy"], default=None)
+    ap.add_argument("--only", choices=["spmm", "xt", "dense", "compress", "tvw", "copy"], default=None)
     ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
     return ap.parse_args()
 
@@ -177,9 +177,26 @@ def main():
         launch_ms = sum(ev) / len(ev)
         rows["spmm24_us_mean"] = launch_ms * 1e3
         rows["spmm24_us_median"] = median(ev) * 1e3
-        if args.only == "spmm":
+    if args.only == "spmm":
+        print(json.dumps(rows))
+        return
+
+    # ---------------- X supplied transposed (N x K) ----------------
+    if args.only in (None, "xt"):
+        XT = p24.transpose(Xt)
+        xstep = lambda: p24.spmm24_xt(c, XT, out=Y)
+        tstep = lambda: p24.transpose(Xt, out=XT)
+        for _ in range(args.warmup):
+            xstep()
+            tstep()
+        ev_x = event_times_ms(torch, xstep, args.steps)
+        ev_t = event_times_ms(torch, tstep, args.steps)
+        rows["spmm24_xt_us_mean"] = sum(ev_x) / len(ev_x) * 1e3
+        rows["transpose_x_us_mean"] = sum(ev_t) / len(ev_t) * 1e3
+        if args.only == "xt":
             print(json.dumps(rows))
             return
+
     # ---------------- dense baseline ----------------
     if args.only in (None, "dense"):
         Wp = p24.pack_dense(Wd_bf16)
@@ -189,6 +206,13 @@ def main():
             dstep()
         ev_d = event_times_ms(torch, dstep, max(args.steps // 2, 3))
         rows["gemm_bf16_us_mean"] = sum(ev_d) / len(ev_d) * 1e3
+        XTd = p24.transpose(Xt)
+        dxstep = lambda: p24.gemm_bf16_xt(Wp, wl.M, wl.K, XTd, out=Yd)
+        for _ in range(args.warmup):
+            dxstep()
+        ev_dx = event_times_ms(torch, dxstep, max(args.steps // 2, 3))
+        rows["gemm_bf16_xt_us_mean"] = sum(ev_dx) / len(ev_dx) * 1e3
+        del XTd
         if args.only == "dense":
             print(json.dumps(rows))
             return
@@ -199,6 +223,14 @@ def main():
             torch.matmul(Wd_bf16, Xc)
         ev_t = event_times_ms(torch, lambda: torch.matmul(Wd_bf16, Xc), 5)
         rows["torch_matmul_us_mean"] = sum(ev_t) / len(ev_t) * 1e3
+        # context only: the same product with both operands K-contiguous (Y^T = X^T W^T, 2-D linear)
+        XTc = p24.transpose(Xt)
+        lin = lambda: torch.nn.functional.linear(XTc, Wd_bf16)
+        for _ in range(2):
+            lin()
+        ev_l = event_times_ms(torch, lin, 5)
+        rows["torch_linear_tn_us_mean"] = sum(ev_l) / len(ev_l) * 1e3
+        del XTc
         # compress of the headline W
         for _ in range(2):
             p24.compress(Wt, layout="device")

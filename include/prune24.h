@@ -141,6 +141,29 @@ P24_API p24_status spmm24(const void* values, const void* meta, int32_t layout, 
                           int32_t y_dtype, int64_t ldy, int32_t algo, void* stream);
 
 /*
+ * spmm24_xt -- spmm24 with X supplied transposed.
+ *   XT            N x K bf16 row-major (K contiguous: the layout of activations
+ *                 stored tokens x features), leading dim ldxt >= K, ldxt % 8 == 0,
+ *                 16 B aligned, 512 * ldxt < 2^32 (else P24_ERR_UNSUPPORTED).
+ *                 Rows of XT at or past N are never read.
+ * Everything else (layout, K % 64, Y, determinism) as for spmm24.  The MFMA
+ * operands want K-contiguous fragments, so this form reads X with plain 16 B
+ * LDS loads instead of transposing LDS loads; for the same inputs it returns
+ * bit-identical results to spmm24.
+ */
+P24_API p24_status spmm24_xt(const void* values, const void* meta, int32_t layout, int64_t M,
+                             int64_t K, const void* XT, int64_t ldxt, int64_t N, void* Y,
+                             int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * transpose_bf16 -- dst = src^T for 16-bit elements (a bit copy).
+ *   src   rows x cols, leading dim ld_src >= cols;  dst  cols x rows, ld_dst >= rows.
+ *   Both 4 B aligned; rows <= 65535 * 64.  Turns X (K x N) into XT for spmm24_xt.
+ */
+P24_API p24_status transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src,
+                                  void* dst, int64_t ld_dst, void* stream);
+
+/*
  * tvw_compress -- TVW selection and compression of fp32 W.
  *   Tile t covers output rows [t*tile_m, min(M, (t+1)*tile_m)).  Its column
  *   score is the fp64 sum over those rows, in ascending row order, of |W[m][k]|;
@@ -191,6 +214,9 @@ P24_API p24_status gemm_bf16_pack(const void* W, int64_t M, int64_t K, int64_t l
                                   void* stream);
 P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
                              int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream);
+/* gemm_bf16_xt -- the dense baseline with X supplied transposed (rules of spmm24_xt). */
+P24_API p24_status gemm_bf16_xt(const void* Wp, int64_t M, int64_t K, const void* XT, int64_t ldxt,
+                                int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream);
 
 #ifdef __cplusplus
 }

@@ -53,6 +53,10 @@ _SIGNATURES = {
                               _c_i32, _c_vp, _c_size, _c_vp]),
     "spmm_tvw": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
                           _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
+    "spmm24_xt": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
+                           _c_i64, _c_vp]),
+    "transpose_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
+    "gemm_bf16_xt": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
     "gemm_bf16_packed_bytes": (_c_size, [_c_i64, _c_i64]),
     "gemm_bf16_pack": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp]),
     "gemm_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
@@ -289,4 +293,53 @@ def gemm_bf16(Wp, M: int, K: int, X, out_dtype=None, out=None):
     ldy = _rowmajor(out, "out")
     _check(lib().gemm_bf16(_ptr(Wp), M, K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy,
                            _stream(X.device)), "gemm_bf16")
+    return out
+
+
+def transpose(src, out=None):
+    """bf16 src [R, C] -> out [C, R] (bit copy on the GPU)."""
+    torch = _torch()
+    _require_cuda(src, "src")
+    if src.dtype != torch.bfloat16:
+        raise ValueError("src must be bfloat16")
+    lds = _rowmajor(src, "src")
+    R, Cc = src.shape
+    if out is None:
+        out = torch.empty((Cc, R), dtype=src.dtype, device=src.device)
+    ldd = _rowmajor(out, "out")
+    _check(lib().transpose_bf16(_ptr(src), R, Cc, lds, _ptr(out), ldd, _stream(src.device)), "transpose_bf16")
+    return out
+
+
+def spmm24_xt(c: Compressed24, XT, out_dtype=None, out=None):
+    """Y = W X for compressed W with X supplied transposed: XT bf16 [N, K]."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _require_cuda(XT, "XT")
+    if XT.dtype != torch.bfloat16:
+        raise ValueError("XT must be bfloat16")
+    ldxt = _rowmajor(XT, "XT")
+    if XT.shape[1] != c.K:
+        raise ValueError(f"XT has {XT.shape[1]} columns, W has K = {c.K}")
+    N = XT.shape[0]
+    if out is None:
+        out = torch.empty((c.M, N), dtype=out_dtype, device=XT.device)
+    ldy = _rowmajor(out, "out")
+    _check(lib().spmm24_xt(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(XT), ldxt, N, _ptr(out),
+                           _out_code(out.dtype), ldy, _stream(XT.device)), "spmm24_xt")
+    return out
+
+
+def gemm_bf16_xt(Wp, M: int, K: int, XT, out_dtype=None, out=None):
+    """Dense baseline with X supplied transposed: XT bf16 [N, K]."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _require_cuda(XT, "XT")
+    ldxt = _rowmajor(XT, "XT")
+    N = XT.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=XT.device)
+    ldy = _rowmajor(out, "out")
+    _check(lib().gemm_bf16_xt(_ptr(Wp), M, K, _ptr(XT), ldxt, N, _ptr(out), _out_code(out.dtype), ldy,
+                              _stream(XT.device)), "gemm_bf16_xt")
     return out

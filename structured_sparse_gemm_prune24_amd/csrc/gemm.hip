@@ -47,6 +47,11 @@ typedef __attribute__((address_space(3))) void lds_void;
 constexpr int BK = 64;                 // logical K per main-loop iteration
 constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
 
+// How the X operand arrives: K x N row-major (N contiguous, transposed on the
+// LDS read), the same with a TVW row gather, or N x K row-major (X^T, K
+// contiguous: the operand order of the MFMA, read with plain 16-byte loads).
+enum XMode { X_KN = 0, X_KN_GATHER = 1, X_NK = 2 };
+
 template <int BM, int BN, int WGM, int WGN, bool SPARSE>
 struct TileCfg {
   static constexpr int NWAVES = WGM * WGN;
@@ -161,9 +166,11 @@ __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool SPARSE, bool GATHER, typename OutT>
+template <int BM, int BN, int WGM, int WGN, bool SPARSE, int XM, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   using C = TileCfg<BM, BN, WGM, WGN, SPARSE>;
+  constexpr bool GATHER = XM == X_KN_GATHER;
+  constexpr bool XT = XM == X_NK;
   constexpr int TM = C::TM, TN = C::TN, ASTEPS = C::ASTEPS, NSTAGE = C::NSTAGE;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * C::STAGE];
 
@@ -208,7 +215,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   x_col = x_col <= n_hi ? x_col : n_hi;
   constexpr int X_ROW_STEP = C::NWAVES * X_ROWS_PER_LOAD;   // multiple of 4: the swizzle of row x_r0 holds for all j
   static_assert(X_ROW_STEP % 4 == 0, "X row step must keep the swizzle phase");
-  const uint32_t x_voff = GATHER ? (uint32_t)x_col * 2 : (uint32_t)(x_r0 * ldx + x_col) * 2;
+  uint32_t x_voff = GATHER ? (uint32_t)x_col * 2 : (uint32_t)(x_r0 * ldx + x_col) * 2;
+  // X^T (N x K): the stage holds BN rows (n) of 64 k = 8 chunks of 16 B.  LDS
+  // slot of (n, chunk c) = (n ^ ((n >> 3) & 1)) * 8 + (c ^ (n & 7)): rows n and
+  // n+8 land in opposite 128 B halves of a bank line and the chunk XOR spreads 8
+  // rows over the 8 slots of a half, so 16 consecutive n at one chunk (one
+  // quarter of a 16-byte-per-lane read) hit 16 distinct bank groups.  Load j of
+  // this wave fills slots [(j*NWAVES + wave)*64, +64): rows 8q .. 8q+7, q = j*NWAVES + wave.
+  uint32_t xt_jstride = 0;
+  if constexpr (XT) {
+    const int q = wave;                                     // j = 0
+    const int n_loc = 8 * q + ((lane >> 3) ^ (q & 1));      // row' = 8q + lane/8, n = row' ^ (q & 1)
+    const int c = (lane & 7) ^ (n_loc & 7);
+    x_voff = (uint32_t)(n_loc * ldx + 8 * c) * 2;
+    xt_jstride = (uint32_t)(8 * C::NWAVES * ldx * 2);       // q advances by NWAVES (even: parity kept)
+    static_assert(C::NWAVES % 2 == 0, "X^T loads keep the row-pair parity per wave");
+  }
   // A values / metadata: load j fills the (row block, step) block q = j*NWAVES + wave
   // (metadata: row block q) of the stage.  Only the lane part of the address is
   // per lane; the block part is wave-uniform and goes into the scalar offset.
@@ -225,6 +247,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       make_rsrc(args.A + (int64_t)rb0 * S * 512, (uint32_t)((rb_end - rb0) * S * 1024));
   const __amdgpu_buffer_rsrc_t m_rsrc =
       SPARSE ? make_rsrc(args.Ameta + (int64_t)rb0 * T_ * 64, (uint32_t)((rb_end - rb0) * T_ * 256)) : a_rsrc;
+  const int n_rows = N - n0 < BN ? N - n0 : BN;
+  const __amdgpu_buffer_rsrc_t xt_rsrc =
+      make_rsrc(args.X + (XT ? (int64_t)n0 * ldx : 0), (uint32_t)(XT ? (int64_t)n_rows * ldx * 2 : 0));
   // TVW: whole-X resource (the host guarantees it spans < 4 GiB)
   const __amdgpu_buffer_rsrc_t xg_rsrc = make_rsrc(args.X, (uint32_t)(GATHER ? (int64_t)args.Kx * ldx * 2 : 0));
 
@@ -251,6 +276,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
         dma16_to_lds(xg_rsrc, stage + (j * C::NWAVES + wave) * 1024, (uint32_t)(k * ldx * 2) + x_voff, 0);
       }
+    } else if constexpr (XT) {
+#pragma unroll
+      for (int j = 0; j < C::X_DMA; ++j)
+        dma16_to_lds(xt_rsrc, stage + (j * C::NWAVES + wave) * 1024, x_voff, (uint32_t)g * BK * 2 + j * xt_jstride);
     } else {
       const __amdgpu_buffer_rsrc_t xr = make_rsrc(args.X + (int64_t)g * BK * ldx, (uint32_t)(BK * ldx * 2));
 #pragma unroll
@@ -284,6 +313,21 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     a_off[st] = base + C::X_BYTES + wm * TM * ASTEPS * 1024 + lane * 16;
     m_off[st] = base + C::X_BYTES + C::A_BYTES + wm * TM * 256 + lane * 4;
   }
+  // X^T fragments: lane (column n = wave cols + 32 j + lane % 32, half h) reads
+  // 16 B chunks of k; the fragment j offset (32 rows = 4 KiB) is an immediate.
+  uint32_t xt_off[XT ? NSTAGE : 1][4];
+  if constexpr (XT) {
+    const int nl = lane & 31;
+    const uint32_t row = (uint32_t)(wn * C::WTN + (nl ^ ((nl >> 3) & 1))) * 128;
+#pragma unroll
+    for (int st = 0; st < NSTAGE; ++st)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        // sparse: q = 2*ss + e reads chunk 4ss + 2e + h; dense: q = ss reads chunk 2ss + h
+        const int c = SPARSE ? (4 * (q >> 1) + 2 * (q & 1) + h) : (2 * q + h);
+        xt_off[st][q] = lds_base + st * C::STAGE + row + (uint32_t)((c ^ (nl & 7)) * 16);
+      }
+  }
 
   f32x16 acc[TM][TN];
 #pragma unroll
@@ -306,7 +350,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         });
       };
       auto read_b = [&](auto SS, i16x16 (&bf)[TN]) {
-        constexpr int R = 32 * decltype(SS)::value * C::ROWB;
+        constexpr int ss = decltype(SS)::value;
+        if constexpr (XT) {
+          static_for<0, TN>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            const i16x8 lo = lds_read_b128<j * 32 * 128>(xt_off[st][2 * ss]);
+            const i16x8 hi = lds_read_b128<j * 32 * 128>(xt_off[st][2 * ss + 1]);
+            bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+          });
+          return;
+        }
+        constexpr int R = 32 * ss * C::ROWB;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const uint32_t ad = b_off[st][j];
@@ -350,13 +404,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         static_for<0, TM>([&](auto I) {
           a[ss & 1][decltype(I)::value] = lds_read_b128<(decltype(I)::value * ASTEPS + ss) * 1024>(a_off[st]);
         });
-        constexpr int R = 16 * ss * C::ROWB;
+        if constexpr (XT) {
+          static_for<0, TN>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            bb[ss & 1][j] = lds_read_b128<j * 32 * 128>(xt_off[st][ss]);
+          });
+        } else {
+          constexpr int R = 16 * ss * C::ROWB;
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const uint32_t ad = b_off[st][j];
-          const i16x4 q0 = lds_read_tr<R>(ad);
-          const i16x4 q1 = lds_read_tr<R + 4 * C::ROWB>(ad);
-          bb[ss & 1][j] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+          for (int j = 0; j < TN; ++j) {
+            const uint32_t ad = b_off[st][j];
+            const i16x4 q0 = lds_read_tr<R>(ad);
+            const i16x4 q1 = lds_read_tr<R + 4 * C::ROWB>(ad);
+            bb[ss & 1][j] = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+          }
         }
       };
       read_step(std::integral_constant<int, 0>{});
@@ -439,15 +500,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 // ---------------------------------------------------------------------------
 enum class Tile { T256x256, T128x256, T128x128, T64x128 };
 
-template <int BM, int BN, int WGM, int WGN, bool SPARSE, bool GATHER>
+template <int BM, int BN, int WGM, int WGN, bool SPARSE, int XM>
 static p24_status launch_cfg(GemmArgs a, int32_t y_dtype, hipStream_t st) {
   a.nbm = (a.M + BM - 1) / BM;
   a.nbn = (a.N + BN - 1) / BN;
   const dim3 grid((unsigned)(a.nbm * a.nbn)), block(WGM * WGN * 64);
   if (y_dtype == P24_F32)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, SPARSE, GATHER, float>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, SPARSE, XM, float>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, SPARSE, GATHER, uint16_t>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, SPARSE, XM, uint16_t>), grid, block, 0, st, a);
   return launch_status();
 }
 
@@ -479,20 +540,21 @@ static Tile choose_tile(int64_t M, int64_t N) {
   return Tile::T64x128;
 }
 
-template <bool SPARSE>
+template <bool SPARSE, int XM>
 static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
   switch (choose_tile(a.M, a.N)) {
-    // Sparse tiles use one wave row (each wave: all BM rows x BN/4 columns): the
-    // B fragments, read with the slower transposing LDS reads, then feed BM/32
-    // MFMAs each.  The dense tile keeps 2 x 2 waves, whose register budget fits.
+    // Sparse tiles use one wave row (each wave: all BM rows x BN/4 columns): a
+    // B fragment then feeds BM/32 MFMAs, which matters most when B comes
+    // through the slower transposing LDS reads.  The dense tile keeps 2 x 2
+    // waves, whose register budget fits.
     case Tile::T256x256:
-      if constexpr (SPARSE) return launch_cfg<256, 256, 1, 4, SPARSE, false>(a, y_dtype, st);
-      else return launch_cfg<256, 256, 2, 2, SPARSE, false>(a, y_dtype, st);
+      if constexpr (SPARSE) return launch_cfg<256, 256, 1, 4, SPARSE, XM>(a, y_dtype, st);
+      else return launch_cfg<256, 256, 2, 2, SPARSE, XM>(a, y_dtype, st);
     case Tile::T128x256:
-      if constexpr (SPARSE) return launch_cfg<128, 256, 1, 4, SPARSE, false>(a, y_dtype, st);
-      else return launch_cfg<128, 256, 2, 2, SPARSE, false>(a, y_dtype, st);
-    case Tile::T128x128: return launch_cfg<128, 128, 2, 2, SPARSE, false>(a, y_dtype, st);
-    case Tile::T64x128: return launch_cfg<64, 128, 1, 2, SPARSE, false>(a, y_dtype, st);
+      if constexpr (SPARSE) return launch_cfg<128, 256, 1, 4, SPARSE, XM>(a, y_dtype, st);
+      else return launch_cfg<128, 256, 2, 2, SPARSE, XM>(a, y_dtype, st);
+    case Tile::T128x128: return launch_cfg<128, 128, 2, 2, SPARSE, XM>(a, y_dtype, st);
+    case Tile::T64x128: return launch_cfg<64, 128, 1, 2, SPARSE, XM>(a, y_dtype, st);
   }
   return P24_ERR_UNSUPPORTED;
 }
@@ -544,7 +606,7 @@ extern "C" P24_API p24_status spmm24(const void* values, const void* meta, int32
   a.Kc = (int)K;
   a.Kx = (int)K;
   a.tile_m = 1;
-  return dispatch<true>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<true, X_KN>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, const void* meta, int32_t layout,
@@ -576,7 +638,7 @@ extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, 
   a.Kx = (int)K;
   a.tile_m = (int)tile_m;
   // one block row = one 128-row slice of a TVW tile
-  return launch_cfg<128, 256, 1, 4, true, true>(a, y_dtype, (hipStream_t)stream);
+  return launch_cfg<128, 256, 1, 4, true, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
@@ -602,5 +664,130 @@ extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, co
   a.Kc = (int)K;
   a.Kx = (int)K;
   a.tile_m = 1;
-  return dispatch<false>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<false, X_KN>(a, y_dtype, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// X given as X^T (N x K row-major, K contiguous)
+// ---------------------------------------------------------------------------
+static p24_status check_xt(const void* XT, int64_t ldxt, int64_t N, int64_t K, const void* Y, int32_t y_dtype,
+                           int64_t ldy) {
+  if (y_dtype != P24_F32 && y_dtype != P24_BF16) return P24_ERR_DTYPE;
+  if (N < 0 || ldxt < K || ldy < N || N > INT32_MAX) return P24_ERR_SHAPE;
+  if (N > 0 && (uint64_t)ldxt * 2 * 256 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;   // one tile's rows in a 32-bit range
+  (void)XT;
+  (void)Y;
+  return P24_OK;
+}
+
+extern "C" P24_API p24_status spmm24_xt(const void* values, const void* meta, int32_t layout, int64_t M, int64_t K,
+                                        const void* XT, int64_t ldxt, int64_t N, void* Y, int32_t y_dtype,
+                                        int64_t ldy, void* stream) {
+  if (layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
+  if (M < 0 || K < 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  p24_status s = check_xt(XT, ldxt, N, K, Y, y_dtype, ldy);
+  if (s != P24_OK) return s;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return P24_OK;
+  if (K == 0) return P24_ERR_UNSUPPORTED;
+  if (!values || !meta) return P24_ERR_NULL;
+  if (!aligned(values, 16) || !aligned(meta, 16)) return P24_ERR_ALIGN;
+  s = check_xy_ptrs(XT, ldxt, Y, y_dtype);
+  if (s != P24_OK) return s;
+  GemmArgs a{};
+  a.A = (const uint16_t*)values;
+  a.Ameta = (const uint32_t*)meta;
+  a.X = (const uint16_t*)XT;
+  a.Y = Y;
+  a.ldx = ldxt;
+  a.ldy = ldy;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.Kc = (int)K;
+  a.Kx = (int)K;
+  a.tile_m = 1;
+  return dispatch<true, X_NK>(a, y_dtype, (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status gemm_bf16_xt(const void* Wp, int64_t M, int64_t K, const void* XT, int64_t ldxt,
+                                           int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream) {
+  if (M < 0 || K < 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  p24_status s = check_xt(XT, ldxt, N, K, Y, y_dtype, ldy);
+  if (s != P24_OK) return s;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return P24_OK;
+  if (K == 0) return P24_ERR_UNSUPPORTED;
+  if (!Wp) return P24_ERR_NULL;
+  if (!aligned(Wp, 16)) return P24_ERR_ALIGN;
+  s = check_xy_ptrs(XT, ldxt, Y, y_dtype);
+  if (s != P24_OK) return s;
+  GemmArgs a{};
+  a.A = (const uint16_t*)Wp;
+  a.X = (const uint16_t*)XT;
+  a.Y = Y;
+  a.ldx = ldxt;
+  a.ldy = ldy;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.Kc = (int)K;
+  a.Kx = (int)K;
+  a.tile_m = 1;
+  return dispatch<false, X_NK>(a, y_dtype, (hipStream_t)stream);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 transpose: dst (C x R) = src (R x C)^T, through a 64 x 64 LDS tile.
+// ---------------------------------------------------------------------------
+namespace p24 {
+__global__ __launch_bounds__(256) void k_transpose_bf16(const uint16_t* __restrict__ src, int64_t R, int64_t Cc,
+                                                       int64_t lds_src, uint16_t* __restrict__ dst, int64_t ldd) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;          // 32 x 8 threads, 2 columns each
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = ty + 8 * i;
+    const int64_t gr = r0 + r, gc = c0 + 2 * tx;
+    uint32_t v = 0;
+    if (gr < R) {
+      if (gc + 1 < Cc && ((gc & 1) == 0) && (lds_src % 2 == 0)) {
+        v = *reinterpret_cast<const uint32_t*>(src + gr * lds_src + gc);
+      } else {
+        const uint32_t lo = gc < Cc ? src[gr * lds_src + gc] : 0;
+        const uint32_t hi = gc + 1 < Cc ? src[gr * lds_src + gc + 1] : 0;
+        v = lo | (hi << 16);
+      }
+    }
+    tile[r][2 * tx] = (uint16_t)(v & 0xFFFFu);
+    tile[r][2 * tx + 1] = (uint16_t)(v >> 16);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = ty + 8 * i;                                      // output row (source column)
+    const int64_t gc = c0 + c, gr = r0 + 2 * tx;
+    if (gc < Cc) {
+      const uint32_t lo = tile[2 * tx][c], hi = tile[2 * tx + 1][c];
+      if (gr + 1 < R && (gr & 1) == 0 && (ldd % 2 == 0)) {
+        *reinterpret_cast<uint32_t*>(dst + gc * ldd + gr) = lo | (hi << 16);
+      } else {
+        if (gr < R) dst[gc * ldd + gr] = (uint16_t)lo;
+        if (gr + 1 < R) dst[gc * ldd + gr + 1] = (uint16_t)hi;
+      }
+    }
+  }
+}
+}  // namespace p24
+
+extern "C" P24_API p24_status transpose_bf16(const void* src, int64_t rows, int64_t cols, int64_t ld_src, void* dst,
+                                             int64_t ld_dst, void* stream) {
+  if (rows < 0 || cols < 0 || ld_src < cols || ld_dst < rows) return P24_ERR_SHAPE;
+  if (rows == 0 || cols == 0) return P24_OK;
+  if (!src || !dst) return P24_ERR_NULL;
+  if (!aligned(src, 4) || !aligned(dst, 4)) return P24_ERR_ALIGN;
+  if ((cols + 63) / 64 > INT32_MAX || (rows + 63) / 64 > 65535) return P24_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  hipLaunchKernelGGL(k_transpose_bf16, grid, dim3(256), 0, (hipStream_t)stream, (const uint16_t*)src, rows, cols,
+                     ld_src, (uint16_t*)dst, ld_dst);
+  return launch_status();
 }
