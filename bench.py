@@ -36,11 +36,14 @@ PEAK_HBM_GBS = 8000.0               # MI355X HBM3E (published)
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=30)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["spmm", "xt", "dense", "compress", "tvw", "copy"], default=None)
     ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
+    ap.add_argument("--table", action="store_true",
+                    help="instead of the headline line, time every workload (spmm24, spmm24_xt, dense) and "
+                         "print one JSON line per workload")
     return ap.parse_args()
 
 
@@ -53,6 +56,31 @@ def event_times_ms(torch, fn, iters):
         evs[i + 1].record()
     torch.cuda.synchronize()
     return [evs[i].elapsed_time(evs[i + 1]) for i in range(iters)]
+
+
+def graph_time_us(torch, fn, reps=20, replays=5):
+    """Per-call GPU time (us) from a HIP graph holding `reps` calls, replayed `replays` times:
+    no host launch overhead between the calls."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(reps):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * replays)
 
 
 def median(xs):
@@ -115,8 +143,58 @@ def measured_traffic():
     return int(b.group(1))
 
 
+def table(args):
+    """Per-workload timings (HIP events, mean of args.steps launches after args.warmup)."""
+    import numpy as np
+    import torch
+
+    import structured_sparse_gemm_prune24_amd as p24
+    import workloads
+    dev = torch.device("cuda:0")
+
+    def to_bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def timeit(fn):
+        return graph_time_us(torch, fn, reps=args.steps)
+
+    for key, wl in workloads.WORKLOADS.items():
+        W = torch.from_numpy(workloads.weights(wl)).to(dev)
+        Xb = workloads.activations(wl)
+        X = to_bf16(Xb)
+        XT = p24.transpose(X)
+        out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
+        Y = torch.empty((wl.M, wl.N), dtype=out_dtype, device=dev)
+        rec = {"workload": key, "M": wl.M, "K": wl.K, "N": wl.N, "out": wl.out_dtype}
+        if wl.tile_m:
+            t = p24.tvw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
+            rec["spmm_tvw_us"] = timeit(lambda: p24.spmm_tvw(t, X, out=Y))
+            sparse_us = rec["spmm_tvw_us"]
+        else:
+            c = p24.compress(W)
+            rec["spmm24_us"] = timeit(lambda: p24.spmm24(c, X, out=Y))
+            rec["spmm24_xt_us"] = timeit(lambda: p24.spmm24_xt(c, XT, out=Y))
+            rec["transpose_x_us"] = timeit(lambda: p24.transpose(X, out=XT))
+            sparse_us = rec["spmm24_us"]
+        Wp = p24.pack_dense(to_bf16(workloads.truncate_to_bf16_bits(workloads.weights(wl))))
+        rec["gemm_bf16_us"] = timeit(lambda: p24.gemm_bf16(Wp, wl.M, wl.K, X, out=Y))
+        rec["gemm_bf16_xt_us"] = timeit(lambda: p24.gemm_bf16_xt(Wp, wl.M, wl.K, XT, out=Y))
+        rec["dense_eq_tflops"] = wl.dense_flops / (sparse_us * 1e-6) / 1e12
+        rec["speedup_vs_dense"] = rec["gemm_bf16_us"] / sparse_us
+        bytes_alg = (wl.M * (wl.keep_k or wl.K) // 2 * 2 + wl.M * (wl.keep_k or wl.K) // 8 + wl.K * wl.N * 2
+                     + wl.M * wl.N * (2 if wl.out_dtype == "bf16" else 4))
+        rec["algorithmic_bytes"] = bytes_alg
+        rec["hbm_frac"] = bytes_alg / (sparse_us * 1e-6) / (PEAK_HBM_GBS * 1e9)
+        rec["mfma_frac"] = wl.kept_flops / (sparse_us * 1e-6) / (PEAK_BF16_MFMA_TFLOPS * 1e12)
+        print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in rec.items()}), flush=True)
+        del W, X, XT, Y, Wp
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
+    if args.table:
+        return table(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
               "see DESIGN.md for how the path would shard", file=sys.stderr)
@@ -283,7 +361,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
             "traffic": measured_traffic() if wl.key == "c4" else None,
-            "kernel": "k_gemm<256,256,1,4,sparse> (spmm24)",
+            "kernel": "k_gemm<256,256,2,4,sparse,X_KN> (spmm24)",
             "algorithmic_flops_per_launch": wl.kept_flops,
         },
         "speedup_vs_dense": round(rows["speedup_vs_dense"], 3),

@@ -543,13 +543,12 @@ static Tile choose_tile(int64_t M, int64_t N) {
 template <bool SPARSE, int XM>
 static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
   switch (choose_tile(a.M, a.N)) {
-    // Sparse tiles use one wave row (each wave: all BM rows x BN/4 columns): a
-    // B fragment then feeds BM/32 MFMAs, which matters most when B comes
-    // through the slower transposing LDS reads.  The dense tile keeps 2 x 2
-    // waves, whose register budget fits.
-    case Tile::T256x256:
-      if constexpr (SPARSE) return launch_cfg<256, 256, 1, 4, SPARSE, XM>(a, y_dtype, st);
-      else return launch_cfg<256, 256, 2, 2, SPARSE, XM>(a, y_dtype, st);
+    // The 256 x 256 tile runs 8 waves (2 x 4, each 128 x 64), two per SIMD:
+    // while one wave waits on LDS reads or the stage barrier the other issues
+    // MFMAs.  The 128 x 256 sparse tile keeps one wave row (each wave: all 128
+    // rows x 64 columns, a B fragment feeding 4 MFMAs), since its 4 metadata
+    // blocks cannot split over 8 waves.
+    case Tile::T256x256: return launch_cfg<256, 256, 2, 4, SPARSE, XM>(a, y_dtype, st);
     case Tile::T128x256:
       if constexpr (SPARSE) return launch_cfg<128, 256, 1, 4, SPARSE, XM>(a, y_dtype, st);
       else return launch_cfg<128, 256, 2, 2, SPARSE, XM>(a, y_dtype, st);
