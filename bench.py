@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--only", choices=["spmm", "xt", "dense", "compress", "tvw", "copy"], default=None)
+    ap.add_argument("--only", choices=["spmm", "xt", "decomp", "dense", "compress", "tvw", "copy"], default=None)
     ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
     ap.add_argument("--table", action="store_true",
                     help="instead of the headline line, time every workload (spmm24, spmm24_xt, dense) and "
@@ -174,6 +174,7 @@ def table(args):
             c = p24.compress(W)
             rec["spmm24_us"] = timeit(lambda: p24.spmm24(c, X, out=Y))
             rec["spmm24_xt_us"] = timeit(lambda: p24.spmm24_xt(c, XT, out=Y))
+            rec["spmm24_decomp_mfma_us"] = timeit(lambda: p24.spmm24(c, X, out=Y, algo="decomp_mfma"))
             rec["transpose_x_us"] = timeit(lambda: p24.transpose(X, out=XT))
             sparse_us = rec["spmm24_us"]
         Wp = p24.pack_dense(to_bf16(workloads.truncate_to_bf16_bits(workloads.weights(wl))))
@@ -272,6 +273,17 @@ def main():
         rows["spmm24_xt_us_mean"] = sum(ev_x) / len(ev_x) * 1e3
         rows["transpose_x_us_mean"] = sum(ev_t) / len(ev_t) * 1e3
         if args.only == "xt":
+            print(json.dumps(rows))
+            return
+
+    # ---------------- same operand expanded in LDS, dense MFMA ----------------
+    if args.only in (None, "decomp"):
+        dcstep = lambda: p24.spmm24(c, Xt, out=Y, algo="decomp_mfma")
+        for _ in range(args.warmup):
+            dcstep()
+        ev_dc = event_times_ms(torch, dcstep, max(args.steps // 2, 3))
+        rows["spmm24_decomp_mfma_us_mean"] = sum(ev_dc) / len(ev_dc) * 1e3
+        if args.only == "decomp":
             print(json.dumps(rows))
             return
 

@@ -85,7 +85,7 @@ enum {
 
 enum { P24_F32 = 0, P24_BF16 = 1 };                         /* element dtypes */
 enum { P24_LAYOUT_CANONICAL = 0, P24_LAYOUT_DEVICE = 1 };    /* compressed layouts */
-enum { P24_ALGO_AUTO = 0, P24_ALGO_SMFMAC = 1 };             /* spmm24 algorithms */
+enum { P24_ALGO_AUTO = 0, P24_ALGO_SMFMAC = 1, P24_ALGO_DECOMP_MFMA = 2 };   /* spmm24 algorithms */
 
 /* ABI version of the loaded library (PRUNE24_ABI_VERSION). */
 P24_API int32_t prune24_abi_version(void);
@@ -132,9 +132,22 @@ P24_API p24_status prune24_decompress(const void* values, const void* meta, int3
  *                 values there are ignored).
  *   Y             M x N, y_dtype P24_F32 or P24_BF16 (round to nearest even),
  *                 leading dim ldy >= N, naturally aligned.
- *   algo          P24_ALGO_AUTO or P24_ALGO_SMFMAC (same kernel family).
+ *   algo          P24_ALGO_SMFMAC: the sparse MFMA consumes the compressed
+ *                 operand and its metadata directly (the 2:4 pattern the
+ *                 matrix units exploit, "Accelerating Sparse Deep Neural
+ *                 Networks", Abstract).
+ *                 P24_ALGO_DECOMP_MFMA: each block expands the compressed
+ *                 operand into a dense tile in LDS (zeros in the pruned slots)
+ *                 and runs the dense MFMA on it: the same result up to fp32
+ *                 summation order, twice the MFMA work.  Kept as the measured
+ *                 alternative.
+ *                 P24_ALGO_AUTO: P24_ALGO_SMFMAC.  Other codes return
+ *                 P24_ERR_UNSUPPORTED.
  * Products are exact in fp32 and accumulate in fp32.  The result is
- * deterministic run to run (no atomics, fixed reduction order).
+ * deterministic run to run (no atomics, fixed reduction order).  With finite X
+ * both algorithms agree with the exact product of the pruned W within the same
+ * bound; a non-finite X element meets the explicit zeros of
+ * P24_ALGO_DECOMP_MFMA (0 * inf = NaN) but is skipped by P24_ALGO_SMFMAC.
  */
 P24_API p24_status spmm24(const void* values, const void* meta, int32_t layout, int64_t M,
                           int64_t K, const void* X, int64_t ldx, int64_t N, void* Y,

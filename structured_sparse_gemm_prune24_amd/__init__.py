@@ -34,7 +34,8 @@ P24_ERR_WORKSPACE = -7
 P24_ERR_LAYOUT = -8
 P24_F32, P24_BF16 = 0, 1
 P24_LAYOUT_CANONICAL, P24_LAYOUT_DEVICE = 0, 1
-P24_ALGO_AUTO, P24_ALGO_SMFMAC = 0, 1
+P24_ALGO_AUTO, P24_ALGO_SMFMAC, P24_ALGO_DECOMP_MFMA = 0, 1, 2
+_ALGOS = {"auto": P24_ALGO_AUTO, "smfmac": P24_ALGO_SMFMAC, "decomp_mfma": P24_ALGO_DECOMP_MFMA}
 
 _c_i32, _c_i64, _c_size, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -204,9 +205,14 @@ def decompress(c: Compressed24):
     return out
 
 
-def spmm24(c: Compressed24, X, out_dtype=None, out=None):
-    """Y = W X for compressed W (device layout) and X bf16 [K, N]."""
+def spmm24(c: Compressed24, X, out_dtype=None, out=None, algo="auto"):
+    """Y = W X for compressed W (device layout) and X bf16 [K, N].
+
+    algo: "smfmac" (sparse MFMA on the compressed operand; what "auto" picks) or
+    "decomp_mfma" (operand expanded to a dense LDS tile, dense MFMA)."""
     torch = _torch()
+    if algo not in _ALGOS:
+        raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
     out_dtype = out_dtype or torch.bfloat16
     _require_cuda(X, "X")
     if X.dtype != torch.bfloat16:
@@ -219,7 +225,7 @@ def spmm24(c: Compressed24, X, out_dtype=None, out=None):
         out = torch.empty((c.M, N), dtype=out_dtype, device=X.device)
     ldy = _rowmajor(out, "out")
     _check(lib().spmm24(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(X), ldx, N, _ptr(out),
-                        _out_code(out.dtype), ldy, P24_ALGO_AUTO, _stream(X.device)), "spmm24")
+                        _out_code(out.dtype), ldy, _ALGOS[algo], _stream(X.device)), "spmm24")
     return out
 
 

@@ -52,8 +52,15 @@ constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
 // contiguous: the operand order of the MFMA, read with plain 16-byte loads).
 enum XMode { X_KN = 0, X_KN_GATHER = 1, X_NK = 2 };
 
-template <int BM, int BN, int WGM, int WGN, bool SPARSE>
+// How the W operand arrives and is multiplied: packed dense bf16 on dense MFMA;
+// compressed 2:4 values + metadata on the sparse MFMA (smfmac); or the same
+// compressed operand expanded block-wide into a dense LDS tile (zeros in the
+// pruned slots) that the dense MFMA loop then reads.
+enum AMode { A_DENSE = 0, A_SPARSE = 1, A_DECOMP = 2 };
+
+template <int BM, int BN, int WGM, int WGN, int AM>
 struct TileCfg {
+  static constexpr bool SPARSE = AM != A_DENSE;    // compressed operand staged in LDS
   static constexpr int NWAVES = WGM * WGN;
   static constexpr int NT = NWAVES * 64;           // threads per block
   static constexpr int WTM = BM / WGM;             // wave tile rows
@@ -69,7 +76,9 @@ struct TileCfg {
   static constexpr int A_BYTES = RB * ASTEPS * 1024;
   static constexpr int M_BYTES = SPARSE ? RB * 256 : 0;
   static constexpr int STAGE = X_BYTES + A_BYTES + M_BYTES;
-  static constexpr int NSTAGE = 3 * STAGE <= LDS_LIMIT ? 3 : 2;
+  // A_DECOMP: one dense A tile (BM x BK bf16 in dense fragment order) after the stages
+  static constexpr int D_BYTES = AM == A_DECOMP ? RB * 4 * 1024 : 0;
+  static constexpr int NSTAGE = 3 * STAGE + D_BYTES <= LDS_LIMIT ? 3 : 2;
   // direct-to-LDS loads per wave per K step (each moves 1 KiB, or 256 B for metadata)
   static constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
   static constexpr int A_DMA = A_BYTES / 1024 / NWAVES;
@@ -79,7 +88,7 @@ struct TileCfg {
   static_assert(X_BYTES % (1024 * NWAVES) == 0 && A_BYTES % (1024 * NWAVES) == 0, "even load split");
   static_assert(!SPARSE || RB % NWAVES == 0, "metadata loads must split evenly among waves");
   static_assert(CPR >= 16, "the chunk swizzle needs at least 16 chunks per row");
-  static_assert(2 * STAGE <= LDS_LIMIT, "two stages must fit in LDS");
+  static_assert(2 * STAGE + D_BYTES <= LDS_LIMIT, "two stages must fit in LDS");
   static_assert(DMA < 64, "vmcnt range");
 };
 
@@ -166,13 +175,15 @@ __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, bool SPARSE, int XM, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int AM, int XM, typename OutT>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
-  using C = TileCfg<BM, BN, WGM, WGN, SPARSE>;
+  using C = TileCfg<BM, BN, WGM, WGN, AM>;
+  constexpr bool SPARSE = C::SPARSE, SMFMAC = AM == A_SPARSE, DECOMP = AM == A_DECOMP;
   constexpr bool GATHER = XM == X_KN_GATHER;
   constexpr bool XT = XM == X_NK;
   constexpr int TM = C::TM, TN = C::TN, ASTEPS = C::ASTEPS, NSTAGE = C::NSTAGE;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * C::STAGE];
+  static_assert(!DECOMP || XM == X_KN, "the expanded-tile path reads X as K x N");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NSTAGE * C::STAGE + C::D_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -310,7 +321,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       const int cs = c ^ chunk_swizzle(li >> 2);
       b_off[st][j] = base + (8 * h + (li >> 2)) * C::ROWB + cs * 16 + (li & 1) * 8;
     }
-    a_off[st] = base + C::X_BYTES + wm * TM * ASTEPS * 1024 + lane * 16;
+    a_off[st] = DECOMP ? lds_base + NSTAGE * C::STAGE + wm * TM * 4 * 1024 + lane * 16
+                       : base + C::X_BYTES + wm * TM * ASTEPS * 1024 + lane * 16;
     m_off[st] = base + C::X_BYTES + C::A_BYTES + wm * TM * 256 + lane * 4;
   }
   // X^T fragments: lane (column n = wave cols + 32 j + lane % 32, half h) reads
@@ -324,7 +336,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         // sparse: q = 2*ss + e reads chunk 4ss + 2e + h; dense: q = ss reads chunk 2ss + h
-        const int c = SPARSE ? (4 * (q >> 1) + 2 * (q & 1) + h) : (2 * q + h);
+        const int c = SMFMAC ? (4 * (q >> 1) + 2 * (q & 1) + h) : (2 * q + h);
         xt_off[st][q] = lds_base + st * C::STAGE + row + (uint32_t)((c ^ (nl & 7)) * 16);
       }
   }
@@ -335,10 +347,49 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = (f32x16){};
 
+  // A_DECOMP: expand the compressed W of stage ST into the dense tile.  Thread
+  // (row block q, lane L) takes lane L of the two 32-k value blocks of q and its
+  // metadata word: value block s' holds row L % 32, k 32 s' + 16 (L / 32) + [0, 16)
+  // as 4 groups of (2 values, one nibble: position of the first value in bits
+  // 0-1, of the second in bits 2-3).  Those 16 dense k are the first 8 k of
+  // dense lane L % 32 and the last 8 of dense lane L % 32 + 32 in the dense
+  // 16-k block 2 s' + L / 32.
+  auto expand = [&](auto ST) {
+    constexpr int st = decltype(ST)::value;
+    const uint32_t cbase = lds_base + st * C::STAGE + C::X_BYTES;
+    const uint32_t dbase = lds_base + NSTAGE * C::STAGE;
+    static_for<0, C::RB / C::NWAVES>([&](auto J) {
+      const int q = decltype(J)::value * C::NWAVES + wave;
+      const uint32_t va = cbase + q * ASTEPS * 1024 + lane * 16;
+      uint32_t mw[1] = {lds_read_b32<0>(cbase + C::A_BYTES + q * 256 + lane * 4)};
+      i16x8 v[2] = {lds_read_b128<0>(va), lds_read_b128<1024>(va)};
+      wait_lds(mw);
+      wait_lds(v);
+#pragma unroll
+      for (int sp = 0; sp < 2; ++sp) {
+        const u32x4 w = __builtin_bit_cast(u32x4, v[sp]);
+        uint32_t d[8];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint32_t nib = mw[0] >> (16 * sp + 4 * g);
+          const uint64_t e = ((uint64_t)(w[g] & 0xFFFFu) << (16 * (nib & 3))) |
+                             ((uint64_t)(w[g] >> 16) << (16 * ((nib >> 2) & 3)));
+          d[2 * g] = (uint32_t)e;
+          d[2 * g + 1] = (uint32_t)(e >> 32);
+        }
+        const uint32_t dst = dbase + (q * 4 + 2 * sp + (lane >> 5)) * 1024 + (lane & 31) * 16;
+        const u32x4 lo = {d[0], d[1], d[2], d[3]}, hi = {d[4], d[5], d[6], d[7]};
+        asm volatile("ds_write_b128 %0, %1" ::"v"(dst), "v"(lo) : "memory");
+        asm volatile("ds_write_b128 %0, %1 offset:512" ::"v"(dst), "v"(hi) : "memory");
+      }
+    });
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  };
+
   // One K step on stage ST.
   auto compute = [&](auto ST) {
     constexpr int st = decltype(ST)::value;
-    if constexpr (SPARSE) {
+    if constexpr (SMFMAC) {
       uint32_t meta[TM];
       i16x8 a0[TM], a1[TM];
       i16x16 b0[TN], b1[TN];
@@ -399,10 +450,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
                                                                 (int)meta[i], 0, 1);
     } else {
       i16x8 a[2][TM], bb[2][TN];
+      constexpr int DSTEPS = 4;    // dense 16-k blocks per row block per K step (packed W or expanded tile)
       auto read_step = [&](auto SS) {
         constexpr int ss = decltype(SS)::value;
         static_for<0, TM>([&](auto I) {
-          a[ss & 1][decltype(I)::value] = lds_read_b128<(decltype(I)::value * ASTEPS + ss) * 1024>(a_off[st]);
+          a[ss & 1][decltype(I)::value] = lds_read_b128<(decltype(I)::value * DSTEPS + ss) * 1024>(a_off[st]);
         });
         if constexpr (XT) {
           static_for<0, TN>([&](auto J) {
@@ -462,6 +514,13 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     load_kept(min(gn + 1, nk - 1), k_nxt);
     issue_step(min(gn, nk - 1), (st + NSTAGE - 1) % NSTAGE);
     asm volatile("" ::: "memory");
+    if constexpr (DECOMP) {
+      // the dense tile is rewritten after the barrier above (every wave is past
+      // its reads of the previous step) and read after this one
+      expand(ST);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
     compute(ST);
     if constexpr (GATHER) {
 #pragma unroll
@@ -500,15 +559,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 // ---------------------------------------------------------------------------
 enum class Tile { T256x256, T128x256, T128x128, T64x128 };
 
-template <int BM, int BN, int WGM, int WGN, bool SPARSE, int XM>
+template <int BM, int BN, int WGM, int WGN, int AM, int XM>
 static p24_status launch_cfg(GemmArgs a, int32_t y_dtype, hipStream_t st) {
   a.nbm = (a.M + BM - 1) / BM;
   a.nbn = (a.N + BN - 1) / BN;
   const dim3 grid((unsigned)(a.nbm * a.nbn)), block(WGM * WGN * 64);
   if (y_dtype == P24_F32)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, SPARSE, XM, float>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, AM, XM, float>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, SPARSE, XM, uint16_t>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, AM, XM, uint16_t>), grid, block, 0, st, a);
   return launch_status();
 }
 
@@ -540,20 +599,20 @@ static Tile choose_tile(int64_t M, int64_t N) {
   return Tile::T64x128;
 }
 
-template <bool SPARSE, int XM>
+template <int AM, int XM>
 static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
   switch (choose_tile(a.M, a.N)) {
     // The 256 x 256 tile runs 8 waves (2 x 4, each 128 x 64), two per SIMD:
     // while one wave waits on LDS reads or the stage barrier the other issues
-    // MFMAs.  The 128 x 256 sparse tile keeps one wave row (each wave: all 128
+    // MFMAs.  The 128 x 256 smfmac tile keeps one wave row (each wave: all 128
     // rows x 64 columns, a B fragment feeding 4 MFMAs), since its 4 metadata
     // blocks cannot split over 8 waves.
-    case Tile::T256x256: return launch_cfg<256, 256, 2, 4, SPARSE, XM>(a, y_dtype, st);
+    case Tile::T256x256: return launch_cfg<256, 256, 2, 4, AM, XM>(a, y_dtype, st);
     case Tile::T128x256:
-      if constexpr (SPARSE) return launch_cfg<128, 256, 1, 4, SPARSE, XM>(a, y_dtype, st);
-      else return launch_cfg<128, 256, 2, 2, SPARSE, XM>(a, y_dtype, st);
-    case Tile::T128x128: return launch_cfg<128, 128, 2, 2, SPARSE, XM>(a, y_dtype, st);
-    case Tile::T64x128: return launch_cfg<64, 128, 1, 2, SPARSE, XM>(a, y_dtype, st);
+      if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 1, 4, AM, XM>(a, y_dtype, st);
+      else return launch_cfg<128, 256, 2, 2, AM, XM>(a, y_dtype, st);
+    case Tile::T128x128: return launch_cfg<128, 128, 2, 2, AM, XM>(a, y_dtype, st);
+    case Tile::T64x128: return launch_cfg<64, 128, 1, 2, AM, XM>(a, y_dtype, st);
   }
   return P24_ERR_UNSUPPORTED;
 }
@@ -582,7 +641,7 @@ extern "C" P24_API p24_status spmm24(const void* values, const void* meta, int32
                                      const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
                                      int64_t ldy, int32_t algo, void* stream) {
   if (layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
-  if (algo != P24_ALGO_AUTO && algo != P24_ALGO_SMFMAC) return P24_ERR_UNSUPPORTED;
+  if (algo != P24_ALGO_AUTO && algo != P24_ALGO_SMFMAC && algo != P24_ALGO_DECOMP_MFMA) return P24_ERR_UNSUPPORTED;
   p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
   if (s != P24_OK) return s;
   if (M < 0 || K < 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
@@ -605,7 +664,10 @@ extern "C" P24_API p24_status spmm24(const void* values, const void* meta, int32
   a.Kc = (int)K;
   a.Kx = (int)K;
   a.tile_m = 1;
-  return dispatch<true, X_KN>(a, y_dtype, (hipStream_t)stream);
+  // AUTO takes the sparse MFMA: on every measured shape it beats expanding the
+  // operand for the dense MFMA, which issues twice the MFMA work.
+  if (algo == P24_ALGO_DECOMP_MFMA) return dispatch<A_DECOMP, X_KN>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<A_SPARSE, X_KN>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, const void* meta, int32_t layout,
@@ -637,7 +699,7 @@ extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, 
   a.Kx = (int)K;
   a.tile_m = (int)tile_m;
   // one block row = one 128-row slice of a TVW tile
-  return launch_cfg<128, 256, 1, 4, true, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
+  return launch_cfg<128, 256, 1, 4, A_SPARSE, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
@@ -663,7 +725,7 @@ extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, co
   a.Kc = (int)K;
   a.Kx = (int)K;
   a.tile_m = 1;
-  return dispatch<false, X_KN>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<A_DENSE, X_KN>(a, y_dtype, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -705,7 +767,7 @@ extern "C" P24_API p24_status spmm24_xt(const void* values, const void* meta, in
   a.Kc = (int)K;
   a.Kx = (int)K;
   a.tile_m = 1;
-  return dispatch<true, X_NK>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<A_SPARSE, X_NK>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16_xt(const void* Wp, int64_t M, int64_t K, const void* XT, int64_t ldxt,
@@ -731,7 +793,7 @@ extern "C" P24_API p24_status gemm_bf16_xt(const void* Wp, int64_t M, int64_t K,
   a.Kc = (int)K;
   a.Kx = (int)K;
   a.tile_m = 1;
-  return dispatch<false, X_NK>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<A_DENSE, X_NK>(a, y_dtype, (hipStream_t)stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -76,6 +76,12 @@ def test_spmm_validation(L):
     assert f(*args(K=96)) == p24.P24_ERR_UNSUPPORTED
     assert f(*args(yd=3)) == p24.P24_ERR_DTYPE
     assert f(*args(algo=9)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(algo=3)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(algo=-1)) == p24.P24_ERR_UNSUPPORTED
+    for algo in (0, 1, 2):     # every accepted algorithm runs the same validation
+        assert f(*args(algo=algo, layout=0)) == p24.P24_ERR_LAYOUT
+        assert f(*args(algo=algo, K=96)) == p24.P24_ERR_UNSUPPORTED
+        assert f(*args(algo=algo, M=0, v=NUL, m=NUL, X=NUL, Y=NUL)) == p24.P24_OK
     assert f(*args(ldx=32)) == p24.P24_ERR_SHAPE
     assert f(*args(ldx=68, N=60)) == p24.P24_ERR_ALIGN
     assert f(*args(X=MISALIGNED)) == p24.P24_ERR_ALIGN
