@@ -386,69 +386,57 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   };
 
-  // One K step on stage ST.
+  // Sparse-MFMA fragments of stage ST, 32-k half SS (k 0..31 or 32..63 of the step).
+  auto rd_meta = [&](auto ST, uint32_t (&meta)[TM]) {
+    constexpr int st = decltype(ST)::value;
+    static_for<0, TM>([&](auto I) { meta[decltype(I)::value] = lds_read_b32<decltype(I)::value * 256>(m_off[st]); });
+  };
+  auto rd_a = [&](auto ST, auto SS, i16x8 (&a)[TM]) {
+    constexpr int st = decltype(ST)::value;
+    static_for<0, TM>([&](auto I) {
+      a[decltype(I)::value] =
+          lds_read_b128<(decltype(I)::value * ASTEPS + decltype(SS)::value) * 1024>(a_off[st]);
+    });
+  };
+  auto rd_b = [&](auto ST, auto SS, i16x16 (&bf)[TN]) {
+    constexpr int st = decltype(ST)::value;
+    constexpr int ss = decltype(SS)::value;
+    if constexpr (XT) {
+      static_for<0, TN>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const i16x8 lo = lds_read_b128<j * 32 * 128>(xt_off[st][2 * ss]);
+        const i16x8 hi = lds_read_b128<j * 32 * 128>(xt_off[st][2 * ss + 1]);
+        bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      });
+    } else {
+      constexpr int R = 32 * ss * C::ROWB;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const uint32_t ad = b_off[st][j];
+        const i16x4 q0 = lds_read_tr<R>(ad);
+        const i16x4 q1 = lds_read_tr<R + 4 * C::ROWB>(ad);
+        const i16x4 q2 = lds_read_tr<R + 16 * C::ROWB>(ad);
+        const i16x4 q3 = lds_read_tr<R + 20 * C::ROWB>(ad);
+        const i16x8 lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const i16x8 hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
+        bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+      }
+    }
+  };
+  auto mma_sparse = [&](auto SS, const i16x8 (&a)[TM], const i16x16 (&bf)[TN], const uint32_t (&meta)[TM]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                              __builtin_bit_cast(bf16x16, bf[j]), acc[i][j],
+                                                              (int)meta[i], 0, decltype(SS)::value);
+  };
+
+  // One K step on stage ST (dense MFMA on packed W or on the expanded tile).
   auto compute = [&](auto ST) {
     constexpr int st = decltype(ST)::value;
-    if constexpr (SMFMAC) {
-      uint32_t meta[TM];
-      i16x8 a0[TM], a1[TM];
-      i16x16 b0[TN], b1[TN];
-      // fragments of k 0..31 (abid 0) and 32..63 (abid 1)
-      auto read_a = [&](auto SS, i16x8 (&a)[TM]) {
-        static_for<0, TM>([&](auto I) {
-          a[decltype(I)::value] =
-              lds_read_b128<(decltype(I)::value * ASTEPS + decltype(SS)::value) * 1024>(a_off[st]);
-        });
-      };
-      auto read_b = [&](auto SS, i16x16 (&bf)[TN]) {
-        constexpr int ss = decltype(SS)::value;
-        if constexpr (XT) {
-          static_for<0, TN>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            const i16x8 lo = lds_read_b128<j * 32 * 128>(xt_off[st][2 * ss]);
-            const i16x8 hi = lds_read_b128<j * 32 * 128>(xt_off[st][2 * ss + 1]);
-            bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-          });
-          return;
-        }
-        constexpr int R = 32 * ss * C::ROWB;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const uint32_t ad = b_off[st][j];
-          const i16x4 q0 = lds_read_tr<R>(ad);
-          const i16x4 q1 = lds_read_tr<R + 4 * C::ROWB>(ad);
-          const i16x4 q2 = lds_read_tr<R + 16 * C::ROWB>(ad);
-          const i16x4 q3 = lds_read_tr<R + 20 * C::ROWB>(ad);
-          const i16x8 lo = __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const i16x8 hi = __builtin_shufflevector(q2, q3, 0, 1, 2, 3, 4, 5, 6, 7);
-          bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
-        }
-      };
-      static_for<0, TM>([&](auto I) { meta[decltype(I)::value] = lds_read_b32<decltype(I)::value * 256>(m_off[st]); });
-      read_a(std::integral_constant<int, 0>{}, a0);
-      read_b(std::integral_constant<int, 0>{}, b0);
-      wait_lds(meta);
-      wait_lds(a0);
-      wait_lds(b0);
-      read_a(std::integral_constant<int, 1>{}, a1);
-      read_b(std::integral_constant<int, 1>{}, b1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a0[i]),
-                                                                __builtin_bit_cast(bf16x16, b0[j]), acc[i][j],
-                                                                (int)meta[i], 0, 0);
-      wait_lds(a1);
-      wait_lds(b1);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a1[i]),
-                                                                __builtin_bit_cast(bf16x16, b1[j]), acc[i][j],
-                                                                (int)meta[i], 0, 1);
-    } else {
+    if constexpr (!SMFMAC) {
       i16x8 a[2][TM], bb[2][TN];
       constexpr int DSTEPS = 4;    // dense 16-k blocks per row block per K step (packed W or expanded tile)
       auto read_step = [&](auto SS) {
@@ -490,47 +478,114 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   };
 
   // ---- main loop ----
-  // Step g is loaded into stage g % NSTAGE by the loads issued NSTAGE-1 steps
-  // earlier.  At the top of step it the loads of steps it+1 .. it+NSTAGE-2 may
-  // still be in flight (vmcnt retires in issue order), then the barrier makes
-  // every wave's part of stage it visible and guarantees that no wave still
-  // reads the stage about to be refilled.  Steps past the end reload the last
-  // step into a stage that is never read, so the counts stay static.  The loop
-  // is unrolled by NSTAGE so every stage address is fixed at compile time.
-  load_kept(0, k_cur);
-  issue_step(0, 0);
+  if constexpr (SMFMAC) {
+    // Step g is loaded into stage g % NSTAGE.  The stage barrier sits between
+    // the two 32-k halves of a step: after it every wave is done with stage
+    // it (its reads were waited for) and sees stage it+1, so a wave refills
+    // stage it with step it+NSTAGE and reads the first half of step it+1 while
+    // its MFMAs on the second half of step it run.  Waves on one SIMD never
+    // meet an LDS wait with an empty MFMA queue except at the block's start.
+    // At the barrier of step it the loads of steps it+2 .. it+NSTAGE-1 may
+    // still be in flight (vmcnt retires in issue order).  Steps past the end
+    // reload the last step into a stage that is never read and the reads of
+    // "step nk" go to a stage that is never used, so every count is static.
+    // The loop is unrolled by NSTAGE so every stage address is a constant.
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
 #pragma unroll
-  for (int g = 1; g < NSTAGE - 1; ++g) {
-    load_kept(min(g, nk - 1), k_cur);
-    issue_step(min(g, nk - 1), g);
-  }
-  load_kept(min(NSTAGE - 1, nk - 1), k_cur);
-  auto body = [&](auto ST, int it) {
-    constexpr int st = decltype(ST)::value;
-    wait_vmcnt<(NSTAGE - 2) * C::DMA>();
+    for (int g = 0; g < NSTAGE; ++g) {
+      load_kept(min(g, nk - 1), k_cur);
+      issue_step(min(g, nk - 1), g);
+    }
+    load_kept(min(NSTAGE, nk - 1), k_cur);
+    wait_vmcnt<(NSTAGE - 1) * C::DMA>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    const int gn = it + NSTAGE - 1;
-    load_kept(min(gn + 1, nk - 1), k_nxt);
-    issue_step(min(gn, nk - 1), (st + NSTAGE - 1) % NSTAGE);
-    asm volatile("" ::: "memory");
-    if constexpr (DECOMP) {
-      // the dense tile is rewritten after the barrier above (every wave is past
-      // its reads of the previous step) and read after this one
-      expand(ST);
+    uint32_t meta[TM], meta_n[TM];
+    i16x8 a0[TM], a1[TM];
+    i16x16 b0[TN], b1[TN];
+    rd_meta(I0{}, meta);
+    rd_a(I0{}, I0{}, a0);
+    rd_b(I0{}, I0{}, b0);
+    auto body = [&](auto ST, int it) {
+      constexpr int st = decltype(ST)::value;
+      constexpr int nx = (st + 1) % NSTAGE;
+      wait_lds(meta);
+      wait_lds(a0);
+      wait_lds(b0);
+      rd_a(ST, I1{}, a1);
+      rd_b(ST, I1{}, b1);
+      mma_sparse(I0{}, a0, b0, meta);
+      wait_lds(a1);
+      wait_lds(b1);
+      wait_vmcnt<(NSTAGE - 2) * C::DMA>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-    }
-    compute(ST);
-    if constexpr (GATHER) {
+      load_kept(min(it + NSTAGE + 1, nk - 1), k_nxt);
+      issue_step(min(it + NSTAGE, nk - 1), st);
+      asm volatile("" ::: "memory");
+      rd_meta(std::integral_constant<int, nx>{}, meta_n);
+      rd_a(std::integral_constant<int, nx>{}, I0{}, a0);
+      rd_b(std::integral_constant<int, nx>{}, I0{}, b0);
+      mma_sparse(I1{}, a1, b1, meta);
 #pragma unroll
-      for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
+      for (int i = 0; i < TM; ++i) meta[i] = meta_n[i];
+      if constexpr (GATHER) {
+#pragma unroll
+        for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
+      }
+    };
+    for (int it = 0; it < nk; it += NSTAGE) {
+      static_for<0, NSTAGE>([&](auto ST) {
+        if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
+      });
     }
-  };
-  for (int it = 0; it < nk; it += NSTAGE) {
-    static_for<0, NSTAGE>([&](auto ST) {
-      if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
-    });
+    wait_lds(a0);
+    wait_lds(b0);
+    wait_lds(meta);
+  } else {
+    // Step g is loaded into stage g % NSTAGE by the loads issued NSTAGE-1 steps
+    // earlier.  At the top of step it the loads of steps it+1 .. it+NSTAGE-2 may
+    // still be in flight (vmcnt retires in issue order), then the barrier makes
+    // every wave's part of stage it visible and guarantees that no wave still
+    // reads the stage about to be refilled.  Steps past the end reload the last
+    // step into a stage that is never read, so the counts stay static.  The loop
+    // is unrolled by NSTAGE so every stage address is fixed at compile time.
+    load_kept(0, k_cur);
+    issue_step(0, 0);
+#pragma unroll
+    for (int g = 1; g < NSTAGE - 1; ++g) {
+      load_kept(min(g, nk - 1), k_cur);
+      issue_step(min(g, nk - 1), g);
+    }
+    load_kept(min(NSTAGE - 1, nk - 1), k_cur);
+    auto body = [&](auto ST, int it) {
+      constexpr int st = decltype(ST)::value;
+      wait_vmcnt<(NSTAGE - 2) * C::DMA>();
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      const int gn = it + NSTAGE - 1;
+      load_kept(min(gn + 1, nk - 1), k_nxt);
+      issue_step(min(gn, nk - 1), (st + NSTAGE - 1) % NSTAGE);
+      asm volatile("" ::: "memory");
+      if constexpr (DECOMP) {
+        // the dense tile is rewritten after the barrier above (every wave is past
+        // its reads of the previous step) and read after this one
+        expand(ST);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+      }
+      compute(ST);
+      if constexpr (GATHER) {
+#pragma unroll
+        for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
+      }
+    };
+    for (int it = 0; it < nk; it += NSTAGE) {
+      static_for<0, NSTAGE>([&](auto ST) {
+        if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
+      });
+    }
   }
 
   // The last NSTAGE-1 steps issued loads into stages that are never read; they
