@@ -75,52 +75,68 @@ __global__ __launch_bounds__(256) void k_compress_canonical(const T* __restrict_
 }
 
 // --------------------------------------------------------------------------
-// Device layout: one thread per (row block rb, K-pair t, row r) -- r fastest so
-// that the 16 B value stores of neighbouring threads are contiguous.
+// Device layout: one wave per (row block rb, chunk of 256 columns).  Lane l
+// owns group 64 c + l of every row, so each row is one contiguous read (1 KiB
+// of fp32).  The device layout puts that group at step s = 8 c + l / 8, lane
+// half h = (l / 4) % 2, pair q = l % 4 of lane L = r + 32 h of block (rb, s):
+// the wave collects its up-to-8 value blocks and 4 metadata blocks in LDS and
+// writes them out as contiguous 16 B (values) and 4 B (metadata) pieces.
+// Staging pads (4 words after every 32 lanes of a block, 8 per block, one
+// per metadata row) spread one row's writes over distinct banks.
 // Rows M..Mp-1 are padding: zero values, positions (0, 1).
 // --------------------------------------------------------------------------
+constexpr int CMP_WAVES = 4;
+constexpr int CMP_BLK_WORDS = 264;    // 64 lanes x 4 words + 2 pads of 4
+constexpr int CMP_META_PITCH = 65;
+
 template <typename T, bool GATHER>
-__global__ __launch_bounds__(256) void k_compress_device(const T* __restrict__ W, int64_t ldw, int64_t M,
-                                                         int64_t K, uint16_t* __restrict__ dvals,
-                                                         uint32_t* __restrict__ dmeta,
-                                                         const int32_t* __restrict__ kept, int64_t tile_m,
-                                                         int64_t kmax) {
-  const int64_t RB = (M + 31) / 32, T_ = K / 64, S = K / 32;
-  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (id >= RB * T_ * 32) return;
-  const int64_t r = id % 32, t = (id / 32) % T_, rb = id / (32 * T_);
-  const int64_t m = rb * 32 + r;
-  const bool live = m < M;
-  const int32_t* kept_row = (GATHER && live) ? kept + (m / tile_m) * K : nullptr;
-  uint32_t mword[2] = {0u, 0u};          // lane h = 0 and h = 1 words
-#pragma unroll
-  for (int half = 0; half < 2; ++half) {   // the two K-steps of the pair (abid 0 / 1)
-    const int64_t s = 2 * t + half;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {          // lane half: compressed columns 8h .. 8h+8 of the step
-      uint32_t packed[4];
-      uint32_t code16 = 0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t g = 8 * s + 4 * h + q;
-        uint16_t v0 = 0, v1 = 0;
-        uint32_t code = 0x4u;              // positions (0, 1) for padding rows
-        if (live) {
-          uint32_t b[4];
-          fetch_group<T, GATHER>(W, ldw, m, g, kept_row, kmax, b);
-          code = compress_group<T>(b, v0, v1);
-        }
-        packed[q] = (uint32_t)v0 | ((uint32_t)v1 << 16);
-        code16 |= code << (4 * q);
-      }
-      const int64_t L = r + 32 * h;
-      u32x4 pv = {packed[0], packed[1], packed[2], packed[3]};
-      *reinterpret_cast<u32x4*>(dvals + ((rb * S + s) * 64 + L) * 8) = pv;
-      mword[h] |= code16 << (16 * half);
+__global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __restrict__ W, int64_t ldw, int64_t M,
+                                                                    int64_t K, uint16_t* __restrict__ dvals,
+                                                                    uint32_t* __restrict__ dmeta,
+                                                                    const int32_t* __restrict__ kept,
+                                                                    int64_t tile_m, int64_t kmax) {
+  __shared__ uint32_t sv[CMP_WAVES][8 * CMP_BLK_WORDS];
+  __shared__ uint32_t sm[CMP_WAVES][4 * CMP_META_PITCH];
+  const int64_t RB = (M + 31) / 32, S = K / 32, T_ = K / 64, G = K / 4;
+  const int64_t NC = (K + 255) / 256;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t wid = (int64_t)blockIdx.x * CMP_WAVES + wv;
+  if (wid >= RB * NC) return;            // wave-uniform
+  const int64_t rb = wid / NC, c = wid % NC;
+  const int64_t g = 64 * c + lane;
+  const bool gv = g < G;
+  const int ns = (int)(S - 8 * c < 8 ? S - 8 * c : 8);     // steps in this chunk (even: K % 64 == 0)
+  const int sl = lane >> 3, hl = (lane >> 2) & 1, ql = lane & 3;
+  uint32_t* vst = sv[wv];
+  uint32_t* mst = sm[wv];
+#pragma unroll 8
+  for (int r = 0; r < 32; ++r) {
+    const int64_t m = rb * 32 + r;
+    uint16_t v0 = 0, v1 = 0;
+    uint32_t code = 0x4u;                // positions (0, 1) for padding rows
+    if (m < M && gv) {
+      const int32_t* kept_row = GATHER ? kept + (m / tile_m) * K : nullptr;
+      uint32_t b[4];
+      fetch_group<T, GATHER>(W, ldw, m, g, kept_row, kmax, b);
+      code = compress_group<T>(b, v0, v1);
     }
+    const int L = r + 32 * hl;
+    vst[sl * CMP_BLK_WORDS + L * 4 + hl * 4 + ql] = (uint32_t)v0 | ((uint32_t)v1 << 16);
+    // 16-bit code of (step, half): the 4 pairs' nibbles; the metadata word of
+    // K-pair t holds step 2t in bits 0-15 and step 2t+1 in bits 16-31
+    uint32_t c16 = code << (4 * ql);
+    c16 |= __shfl_xor(c16, 1);
+    c16 |= __shfl_xor(c16, 2);
+    const uint32_t hi = __shfl_xor(c16, 8);
+    if (ql == 0 && (sl & 1) == 0) mst[(sl >> 1) * CMP_META_PITCH + L] = c16 | (hi << 16);
   }
-  dmeta[(rb * T_ + t) * 64 + r] = mword[0];
-  dmeta[(rb * T_ + t) * 64 + r + 32] = mword[1];
+  u32x4* vout = reinterpret_cast<u32x4*>(dvals + (rb * S + 8 * c) * 64 * 8);
+  for (int j = 0; j < ns; ++j) {
+    const uint32_t* e = vst + j * CMP_BLK_WORDS + lane * 4 + (lane >> 5) * 4;
+    vout[j * 64 + lane] = u32x4{e[0], e[1], e[2], e[3]};
+  }
+  uint32_t* mout = dmeta + (rb * T_ + 4 * c) * 64;
+  for (int j = 0; j < ns / 2; ++j) mout[j * 64 + lane] = mst[j * CMP_META_PITCH + lane];
 }
 
 // --------------------------------------------------------------------------
@@ -316,12 +332,13 @@ static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int
       hipLaunchKernelGGL((k_compress_canonical<uint16_t, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
                          (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
   } else {
-    const int64_t n = ((M + 31) / 32) * (K / 64) * 32;
+    const int64_t waves = ((M + 31) / 32) * ((K + 255) / 256);
+    const dim3 grid(grid1d(waves, CMP_WAVES)), block(64 * CMP_WAVES);
     if (w_dtype == P24_F32)
-      hipLaunchKernelGGL((k_compress_device<float, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+      hipLaunchKernelGGL((k_compress_device<float, GATHER>), grid, block, 0, st,
                          (const float*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
     else
-      hipLaunchKernelGGL((k_compress_device<uint16_t, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+      hipLaunchKernelGGL((k_compress_device<uint16_t, GATHER>), grid, block, 0, st,
                          (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
   }
   return launch_status();

@@ -593,20 +593,61 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   wait_vmcnt<0>();
 
   // ---- epilogue ----
+  // Each wave passes its tile through LDS one 32-row slice at a time: the
+  // MFMA result holds one column per lane, the store wants rows.  Slice i is
+  // written as [32 rows][WTN cols] with a 16 B pad per row (the two row
+  // halves a write instruction touches land on disjoint banks), read back as
+  // 16 B row pieces and stored with one 16 B store per piece when Y allows
+  // it, element by element at ragged edges or for an unaligned Y.
+  __builtin_amdgcn_s_barrier();   // every wave's loads have landed and its reads are done
+  asm volatile("" ::: "memory");
+  constexpr int ES = (int)sizeof(OutT);
+  constexpr int PITCH = C::WTN * ES + 16;           // bytes per staged row
+  constexpr int VEC = 16 / ES;                      // elements per 16 B piece
+  constexpr int PPR = C::WTN / VEC;                 // pieces per row
+  constexpr int PPL = 32 * PPR / 64;                // pieces per lane per slice
+  static_assert(C::NWAVES * 32 * PITCH <= NSTAGE * C::STAGE + C::D_BYTES, "epilogue staging fits in LDS");
+  static_assert((32 * PPR) % 64 == 0, "whole pieces per lane");
   OutT* Y = reinterpret_cast<OutT*>(args.Y);
+  uint8_t* region = lds + wave * 32 * PITCH;
   const int row_w = m0 + wm * C::WTM;
-  const int col_l = n0 + wn * C::WTN + (lane & 31);
+  const int col_w = n0 + wn * C::WTN;
+  const bool vec_ok = ((uintptr_t)Y % 16 == 0) && ((args.ldy * ES) % 16 == 0);
+  // The staged slice is written as OutT and read back as 16 B words: the
+  // compiler barriers keep those differently typed accesses in program order
+  // (the wave's LDS operations then execute in that order).
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int i = 0; i < TM; ++i) {
+    asm volatile("" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      const int col = col_l + 32 * j;
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int row = row_w + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
-        if (row < M && col < N) store_out<OutT>(Y + (int64_t)row * args.ldy + col, acc[i][j][e]);
+        const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+        OutT v;
+        if constexpr (ES == 2) v = f32_to_bf16_rne(__float_as_uint(acc[i][j][e]));
+        else v = acc[i][j][e];
+        *reinterpret_cast<OutT*>(region + r * PITCH + (32 * j + (lane & 31)) * ES) = v;
+      }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int t = 0; t < PPL; ++t) {
+      const int q = t * 64 + lane;
+      const int r = q / PPR, cc = (q % PPR) * VEC;
+      const u32x4 piece = *reinterpret_cast<const u32x4*>(region + r * PITCH + cc * ES);
+      const int row = row_w + 32 * i + r, col = col_w + cc;
+      if (row >= M) continue;
+      OutT* dst = Y + (int64_t)row * args.ldy + col;
+      if (vec_ok && col + VEC <= N) {
+        *reinterpret_cast<u32x4*>(dst) = piece;
+      } else {
+        const OutT* pv = reinterpret_cast<const OutT*>(&piece);
+#pragma unroll
+        for (int u = 0; u < VEC; ++u)
+          if (col + u < N) dst[u] = pv[u];
       }
     }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -637,9 +678,13 @@ static int64_t nblocks_for(Tile t, int64_t M, int64_t N) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-// Largest tile that still gives at least one block per CU; otherwise the one
-// with the most blocks.  P24_TILE=<256x256|128x256|128x128|64x128> overrides
-// (measurement aid).
+// The largest of 256x256, 128x128 and 64x128 that still gives at least 160
+// blocks (five eighths of the CUs), else the one with the most blocks.  The
+// big tile moves the fewest bytes per MFMA, so it wins even with a quarter of
+// the CUs idle; below that the smaller tiles, which also fit two blocks per CU,
+// win on parallelism.  128x256 (one wave per SIMD) never beat 128x128 on the
+// measured shapes and is only taken by request.  P24_TILE=<256x256|128x256|
+// 128x128|64x128> overrides (measurement aid).
 static Tile choose_tile(int64_t M, int64_t N) {
   if (const char* e = getenv("P24_TILE")) {
     const std::string s(e);
@@ -648,9 +693,9 @@ static Tile choose_tile(int64_t M, int64_t N) {
     if (s == "128x128") return Tile::T128x128;
     if (s == "64x128") return Tile::T64x128;
   }
-  const Tile order[] = {Tile::T256x256, Tile::T128x256, Tile::T128x128, Tile::T64x128};
+  const Tile order[] = {Tile::T256x256, Tile::T128x128, Tile::T64x128};
   for (Tile t : order)
-    if (nblocks_for(t, M, N) >= 256) return t;
+    if (nblocks_for(t, M, N) >= 160) return t;
   return Tile::T64x128;
 }
 
