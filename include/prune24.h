@@ -184,7 +184,8 @@ P24_API p24_status transpose_bf16(const void* src, int64_t rows, int64_t cols, i
  *   by their fp64 bit pattern, so NaN ranks highest) are kept, listed ascending
  *   in kept[t][0..keep_k).  The tile's rows restricted to those columns are then
  *   compressed 2:4 exactly as prune24_compress does, along the compacted axis.
- *   W         M x K fp32 (w_dtype must be P24_F32), ldw % 4 == 0, 16 B aligned.
+ *   W         M x K fp32 (w_dtype must be P24_F32), ldw % 4 == 0, 16 B aligned;
+ *             M, K <= 2^31 - 1.
  *   tile_m    > 0 and a multiple of 32.  keep_k: 0 < keep_k <= K, keep_k % 4 == 0
  *             (% 64 for the device layout).
  *   kept      output int32 [ceil(M/tile_m)][keep_k].

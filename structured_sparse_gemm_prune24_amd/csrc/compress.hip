@@ -200,78 +200,100 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
   const int64_t t = id / K, k = id % K;
   const int64_t r1 = (t + 1) * tile_m < M ? (t + 1) * tile_m : M;
   double acc = 0.0;
-  for (int64_t m = t * tile_m; m < r1; ++m) acc = acc + fabs((double)W[m * ldw + k]);
+  int64_t m = t * tile_m;
+  for (; m + 8 <= r1; m += 8) {          // 8 loads in flight, then the adds in row order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = W[(m + u) * ldw + k];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc = acc + fabs((double)v[u]);
+  }
+  for (; m < r1; ++m) acc = acc + fabs((double)W[m * ldw + k]);
   scores[id] = acc;
 }
 
 // --------------------------------------------------------------------------
-// TVW selection: one block per tile.  Column k is kept when fewer than keep_k
-// columns beat it (higher score bits, or equal bits and lower index).  Kept
-// columns are then written in ascending order by a block-wide prefix count.
+// TVW selection: one block per tile.  The kept set is the keep_k largest
+// scores, ties to the lower column.  Scores are non-negative fp64 sums, so
+// their bit patterns order like the values.  An MSB-first radix select (8
+// passes of 8 bits, a 256-bin histogram over the keys that still match the
+// prefix found so far) finds the keep_k-th largest key v and how many of the
+// keys equal to v are kept; a block-wide scan in column order then writes
+// every column with key > v and the first `need` columns with key == v.
 // --------------------------------------------------------------------------
-constexpr int SEL_THREADS = 256;
-constexpr int SEL_CHUNK = 2048;
+constexpr int SEL_THREADS = 1024;
+constexpr int SEL_WAVES = SEL_THREADS / 64;
+
+// Exclusive block-wide prefix of per-thread counts in thread order; returns
+// this thread's prefix and writes the block total.
+__device__ __forceinline__ int64_t block_exclusive_scan(uint32_t v, int64_t* total, uint32_t* wave_sums) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_up(incl, d);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_sums[wave] = incl;
+  __syncthreads();
+  int64_t before = 0, all = 0;
+  for (int w = 0; w < SEL_WAVES; ++w) {
+    if (w < wave) before += wave_sums[w];
+    all += wave_sums[w];
+  }
+  __syncthreads();
+  *total = all;
+  return before + incl - v;
+}
 
 __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __restrict__ scores, int64_t K,
                                                             int64_t keep_k, int32_t* __restrict__ kept) {
-  __shared__ uint64_t chunk[SEL_CHUNK];
-  __shared__ uint32_t wave_counts[SEL_THREADS / 64];
-  extern __shared__ uint32_t keep_bits[];     // ceil(K/32) words
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t wave_sums[SEL_WAVES];
+  __shared__ uint64_t sh_prefix;
+  __shared__ int64_t sh_need;
   const int64_t t = blockIdx.x;
   const uint64_t* key = reinterpret_cast<const uint64_t*>(scores + t * K);
   const int tid = threadIdx.x;
-  const int64_t nwords = (K + 31) / 32;
-  for (int64_t i = tid; i < nwords; i += SEL_THREADS) keep_bits[i] = 0u;
-  __syncthreads();
-  // Each thread owns columns k = tid, tid + 256, ...; count how many columns beat each.
-  for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS * 8) {
-    uint64_t mykey[8];
-    int64_t beaten[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t k = k0 + tid + (int64_t)u * SEL_THREADS;
-      mykey[u] = k < K ? key[k] : 0;
-      beaten[u] = 0;
+  uint64_t prefix = 0;        // digits of the threshold found so far (high bits)
+  int64_t need = keep_k;      // rank of the threshold among keys matching the prefix
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0u;
+    __syncthreads();
+    const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+    for (int64_t k = tid; k < K; k += SEL_THREADS) {
+      const uint64_t x = key[k];
+      if ((x & hi_mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
-    for (int64_t j0 = 0; j0 < K; j0 += SEL_CHUNK) {
-      const int64_t n = (K - j0) < SEL_CHUNK ? (K - j0) : SEL_CHUNK;
-      __syncthreads();
-      for (int64_t i = tid; i < n; i += SEL_THREADS) chunk[i] = key[j0 + i];
-      __syncthreads();
-      for (int64_t i = 0; i < n; ++i) {
-        const uint64_t kj = chunk[i];
-        const int64_t j = j0 + i;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const int64_t k = k0 + tid + (int64_t)u * SEL_THREADS;
-          beaten[u] += (kj > mykey[u]) || (kj == mykey[u] && j < k);
-        }
+    __syncthreads();
+    if (tid == 0) {
+      int64_t above = 0;
+      int d = 255;
+      for (; d > 0; --d) {
+        if (above + hist[d] >= need) break;
+        above += hist[d];
       }
+      sh_prefix = prefix | ((uint64_t)d << shift);
+      sh_need = need - above;
     }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int64_t k = k0 + tid + (int64_t)u * SEL_THREADS;
-      if (k < K && beaten[u] < keep_k) atomicOr(&keep_bits[k / 32], 1u << (k % 32));
-    }
+    __syncthreads();
+    prefix = sh_prefix;
+    need = sh_need;
   }
-  __syncthreads();
-  // Ordered compaction: blocks of 256 consecutive columns, one per thread.
-  int64_t base = 0;
-  const int lane = tid % 64, wave = tid / 64;
+  // prefix is the threshold key; `need` columns equal to it are kept, lowest first
+  int64_t eq_base = 0, out_base = 0;
   for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS) {
     const int64_t k = k0 + tid;
-    const bool flag = k < K && ((keep_bits[k / 32] >> (k % 32)) & 1u);
-    const uint64_t ballot = __ballot(flag);
-    const uint32_t below = __popcll(ballot & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    if (lane == 0) wave_counts[wave] = __popcll(ballot);
-    __syncthreads();
-    int64_t off = base;
-    for (int w = 0; w < wave; ++w) off += wave_counts[w];
-    if (flag) kept[t * keep_k + off + below] = (int32_t)k;
-    int64_t total = 0;
-    for (int w = 0; w < SEL_THREADS / 64; ++w) total += wave_counts[w];
-    base += total;
-    __syncthreads();
+    const uint64_t x = k < K ? key[k] : 0ull;
+    const bool gt = k < K && x > prefix;
+    const bool eq = k < K && x == prefix;
+    int64_t eq_total, keep_total;
+    const int64_t eq_rank = eq_base + block_exclusive_scan(eq ? 1u : 0u, &eq_total, wave_sums);
+    const bool keep = gt || (eq && eq_rank < need);
+    const int64_t pos = out_base + block_exclusive_scan(keep ? 1u : 0u, &keep_total, wave_sums);
+    if (keep) kept[t * keep_k + pos] = (int32_t)k;
+    eq_base += eq_total;
+    out_base += keep_total;
   }
 }
 
@@ -386,8 +408,6 @@ extern "C" P24_API p24_status gemm_bf16_pack(const void* W, int64_t M, int64_t K
   return launch_status();
 }
 
-static constexpr int64_t TVW_MAX_K = 1 << 18;   // keep bitmap of the selection kernel: 32 KiB of LDS
-
 extern "C" P24_API size_t tvw_workspace_bytes(int64_t M, int64_t K, int64_t tile_m, int64_t keep_k) {
   (void)keep_k;
   if (M < 0 || K <= 0 || tile_m <= 0) return 0;
@@ -402,7 +422,7 @@ extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64
   if (layout != P24_LAYOUT_CANONICAL && layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
   if (M < 0 || K <= 0 || ldw < K || tile_m <= 0 || tile_m % 32 || keep_k <= 0 || keep_k > K || keep_k % 4)
     return P24_ERR_SHAPE;
-  if (M > INT32_MAX || K > TVW_MAX_K) return P24_ERR_SHAPE;
+  if (M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;    // kept lists are int32
   if (layout == P24_LAYOUT_DEVICE && keep_k % 64) return P24_ERR_UNSUPPORTED;
   if (M == 0) return P24_OK;
   if (!W || !kept || !values || !meta) return P24_ERR_NULL;
@@ -417,8 +437,7 @@ extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64
                      tile_m, scores);
   p24_status s = launch_status();
   if (s != P24_OK) return s;
-  const size_t dyn = (size_t)((K + 31) / 32) * 4;
-  hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), dyn, st, (const double*)scores, K,
+  hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
                      keep_k, kept);
   s = launch_status();
   if (s != P24_OK) return s;

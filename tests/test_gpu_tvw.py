@@ -42,6 +42,31 @@ def test_compress_ties():
     _compare_compress(W, 128, 128, "device")
 
 
+@pytest.mark.parametrize("fill", [0.5, 0.0])
+def test_select_all_tied(fill):
+    """Every column scores the same: the lowest keep_k columns are kept."""
+    need_gpu()
+    W = np.full((256, 3000), fill, dtype=np.float32)
+    t, kept, _, _ = _compare_compress(W, 128, 1500, "canonical")
+    assert np.array_equal(kept, np.tile(np.arange(1500, dtype=np.int32), (2, 1)))
+
+
+def test_select_many_chunks():
+    """K spans several 1024-column scan chunks with a ragged tail."""
+    need_gpu()
+    W = workloads.random_matrix((160, 5000), seed=77, sigma=0.02)
+    _compare_compress(W, 128, 2500, "canonical")
+
+
+def test_select_threshold_tie():
+    """A tie straddling the cut: only the lowest-index tied columns make it."""
+    need_gpu()
+    W = workloads.random_matrix((128, 1024), seed=78, sigma=0.02)
+    W[:, 100:400] = 0.25                 # 300 equal columns around the keep_k-th score
+    W[:, 600:700] = 1.0                  # 100 columns above every other score
+    _compare_compress(W, 128, 256, "device")
+
+
 def test_c5_full():
     need_gpu()
     wl = workloads.WORKLOADS["c5"]
