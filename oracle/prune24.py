@@ -208,7 +208,8 @@ def decompress_24(values: np.ndarray, meta: np.ndarray, K: int) -> np.ndarray:
 # of the i-th compressed value sits at bits [2i, 2i+2) -- the same bit-stream
 # order as the canonical layout.  Padded rows get position pattern 0x4444.
 def device_rows(M: int) -> int:
-    return ((M + 31) // 32) * 32
+    """Rows of the device layout: M rounded up to whole groups of four 32-row blocks."""
+    return ((M + 127) // 128) * 128
 
 
 def to_device_layout(values: np.ndarray, meta: np.ndarray, K: int):
@@ -217,6 +218,9 @@ def to_device_layout(values: np.ndarray, meta: np.ndarray, K: int):
     Requires K % 64 == 0.  Index names: rb row block, r row in block, s K-step
     of 32 logical columns, t K-pair (64 logical columns), h lane half (L // 32),
     half = which K-step of the pair (abid), i compressed value within a lane.
+    Rows are padded to a multiple of 128.  Values are stored [rb, s, L, i];
+    metadata words [rb // 4, t, rb % 4, L] (the four row blocks of a group sit
+    side by side for each K-pair, 1 KiB together).
     """
     if K % 64:
         raise ValueError("device layout needs K % 64 == 0")
@@ -234,7 +238,8 @@ def to_device_layout(values: np.ndarray, meta: np.ndarray, K: int):
     p6 = pos.reshape(RB, 32, T, 2, 2, 8).transpose(0, 2, 4, 1, 3, 5)   # rb, t, h, r, half, i
     shifts = (16 * np.arange(2)[:, None] + 2 * np.arange(8)[None, :]).astype(np.uint64)
     words = (p6 << shifts).sum(axis=(-2, -1), dtype=np.uint64)           # disjoint bits: sum == or
-    return dv.reshape(-1).copy(), words.reshape(RB, T, 64).astype(np.uint32).reshape(-1)
+    grouped = words.reshape(RB // 4, 4, T, 64).transpose(0, 2, 1, 3)     # rbg, t, rq, L
+    return dv.reshape(-1).copy(), grouped.astype(np.uint32).reshape(-1)
 
 
 def from_device_layout(dvals: np.ndarray, dmeta: np.ndarray, M: int, K: int):
@@ -243,7 +248,8 @@ def from_device_layout(dvals: np.ndarray, dmeta: np.ndarray, M: int, K: int):
     RB, S, T = Mp // 32, K // 32, K // 64
     dv = np.asarray(dvals, dtype=np.uint16).reshape(RB, S, 2, 32, 8)          # rb, s, h, r, i
     values = dv.transpose(0, 3, 1, 2, 4).reshape(Mp, K // 2)
-    w = np.asarray(dmeta, dtype=np.uint32).reshape(RB, T, 2, 32).astype(np.uint64)  # rb, t, h, r
+    w = (np.asarray(dmeta, dtype=np.uint32).reshape(RB // 4, T, 4, 64).transpose(0, 2, 1, 3)
+         .reshape(RB, T, 2, 32).astype(np.uint64))                               # rb, t, h, r
     shifts = (16 * np.arange(2)[:, None] + 2 * np.arange(8)[None, :]).astype(np.uint64)
     p6 = (w[..., None, None] >> shifts) & np.uint64(3)                             # rb, t, h, r, half, i
     pos = p6.transpose(0, 3, 1, 4, 2, 5).reshape(Mp, K // 2)                       # rb, r, t, half, h, i

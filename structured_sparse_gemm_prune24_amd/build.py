@@ -2,6 +2,7 @@
 
 Each .hip source is compiled to an object under <repo>/_build, then linked into
 the shared library.  Always recompiles (a build is the "does it build" check).
+The device assembly kept by -save-temps is checked by isa_check.
 """
 from __future__ import annotations
 
@@ -10,6 +11,11 @@ import os
 import shutil
 import subprocess
 import sys
+
+try:
+    from . import isa_check
+except ImportError:          # run as a script
+    import isa_check
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -39,9 +45,15 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
+def device_asm(src: str) -> str:
+    """The gfx950 assembly that -save-temps leaves next to the object of `src`."""
+    stem = os.path.splitext(os.path.basename(src))[0]
+    return os.path.join(BUILD_DIR, f"{stem}-hip-amdgcn-amd-amdhsa-{ARCH}.s")
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc(), *COMMON_FLAGS, "-save-temps=obj", "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -64,6 +76,9 @@ def build(verbose: bool = False) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"link failed\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, out)
+    # every kernel's final assembly: no LDS read result used before its wait
+    for src in srcs:
+        isa_check.check_file(device_asm(src))
     return out
 
 

@@ -83,7 +83,9 @@ __global__ __launch_bounds__(256) void k_compress_canonical(const T* __restrict_
 // writes them out as contiguous 16 B (values) and 4 B (metadata) pieces.
 // Staging pads (4 words after every 32 lanes of a block, 8 per block, one
 // per metadata row) spread one row's writes over distinct banks.
-// Rows M..Mp-1 are padding: zero values, positions (0, 1).
+// Rows M..Mp-1 (Mp = M rounded up to 128) are padding: zero values, positions
+// (0, 1).  Metadata words are stored [rb / 4][t][rb % 4][L]: the four row
+// blocks of a group side by side per K-pair, one 1 KiB load for the GEMM.
 // --------------------------------------------------------------------------
 constexpr int CMP_WAVES = 4;
 constexpr int CMP_BLK_WORDS = 264;    // 64 lanes x 4 words + 2 pads of 4
@@ -97,7 +99,7 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
                                                                     int64_t tile_m, int64_t kmax) {
   __shared__ uint32_t sv[CMP_WAVES][8 * CMP_BLK_WORDS];
   __shared__ uint32_t sm[CMP_WAVES][4 * CMP_META_PITCH];
-  const int64_t RB = (M + 31) / 32, S = K / 32, T_ = K / 64, G = K / 4;
+  const int64_t RB = device_row_blocks(M), S = K / 32, T_ = K / 64, G = K / 4;
   const int64_t NC = (K + 255) / 256;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t wid = (int64_t)blockIdx.x * CMP_WAVES + wv;
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
     const uint32_t* e = vst + j * CMP_BLK_WORDS + lane * 4 + (lane >> 5) * 4;
     vout[j * 64 + lane] = u32x4{e[0], e[1], e[2], e[3]};
   }
-  uint32_t* mout = dmeta + (rb * T_ + 4 * c) * 64;
-  for (int j = 0; j < ns / 2; ++j) mout[j * 64 + lane] = mst[j * CMP_META_PITCH + lane];
+  uint32_t* mout = dmeta + (((rb >> 2) * T_ + 4 * c) * 4 + (rb & 3)) * 64;
+  for (int j = 0; j < ns / 2; ++j) mout[j * 256 + lane] = mst[j * CMP_META_PITCH + lane];
 }
 
 // --------------------------------------------------------------------------
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256) void k_decompress(const uint16_t* __restrict__
     const int64_t S = K / 32, T_ = K / 64;
     const int64_t s = g / 8, h = (g % 8) / 4, q = g % 4;
     const int64_t rb = m / 32, L = m % 32 + 32 * h;
-    code = (meta[(rb * T_ + s / 2) * 64 + L] >> (16 * (s % 2) + 4 * q)) & 0xFu;
+    code = (meta[(((rb >> 2) * T_ + s / 2) * 4 + (rb & 3)) * 64 + L] >> (16 * (s % 2) + 4 * q)) & 0xFu;
     const uint16_t* v = values + ((rb * S + s) * 64 + L) * 8 + 2 * q;
     v0 = v[0];
     v1 = v[1];
@@ -311,7 +313,7 @@ extern "C" P24_API size_t prune24_values_bytes(int64_t M, int64_t K, int32_t lay
   if (layout == P24_LAYOUT_CANONICAL) return (size_t)M * (size_t)(K / 2) * 2;
   if (layout == P24_LAYOUT_DEVICE) {
     if (K % 64) return 0;
-    return (size_t)((M + 31) / 32) * 32 * (size_t)(K / 2) * 2;
+    return (size_t)device_row_blocks(M) * 32 * (size_t)(K / 2) * 2;
   }
   return 0;
 }
@@ -321,7 +323,7 @@ extern "C" P24_API size_t prune24_meta_bytes(int64_t M, int64_t K, int32_t layou
   if (layout == P24_LAYOUT_CANONICAL) return (size_t)M * (size_t)((K + 31) / 32) * 4;
   if (layout == P24_LAYOUT_DEVICE) {
     if (K % 64) return 0;
-    return (size_t)((M + 31) / 32) * (size_t)(K / 64) * 64 * 4;
+    return (size_t)device_row_blocks(M) * (size_t)(K / 64) * 64 * 4;
   }
   return 0;
 }
@@ -354,7 +356,7 @@ static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int
       hipLaunchKernelGGL((k_compress_canonical<uint16_t, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
                          (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
   } else {
-    const int64_t waves = ((M + 31) / 32) * ((K + 255) / 256);
+    const int64_t waves = device_row_blocks(M) * ((K + 255) / 256);
     const dim3 grid(grid1d(waves, CMP_WAVES)), block(64 * CMP_WAVES);
     if (w_dtype == P24_F32)
       hipLaunchKernelGGL((k_compress_device<float, GATHER>), grid, block, 0, st,

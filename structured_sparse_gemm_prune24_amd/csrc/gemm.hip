@@ -74,7 +74,10 @@ struct TileCfg {
   static constexpr int CPR = BN / 8;               // 16 B chunks per X row
   static constexpr int X_BYTES = BK * ROWB;
   static constexpr int A_BYTES = RB * ASTEPS * 1024;
-  static constexpr int M_BYTES = SPARSE ? RB * 256 : 0;
+  // metadata: one 1 KiB load per group of four row blocks (a 64-row block
+  // loads its whole group and reads its half)
+  static constexpr int MG = SPARSE ? (RB >= 4 ? RB / 4 : 1) : 0;
+  static constexpr int M_BYTES = MG * 1024;
   static constexpr int STAGE = X_BYTES + A_BYTES + M_BYTES;
   // A_DECOMP: one dense A tile (BM x BK bf16 in dense fragment order) after the stages
   static constexpr int D_BYTES = AM == A_DECOMP ? RB * 4 * 1024 : 0;
@@ -82,14 +85,18 @@ struct TileCfg {
   // direct-to-LDS loads per wave per K step (each moves 1 KiB, or 256 B for metadata)
   static constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
   static constexpr int A_DMA = A_BYTES / 1024 / NWAVES;
-  static constexpr int M_DMA = SPARSE ? RB / NWAVES : 0;
-  static constexpr int DMA = X_DMA + A_DMA + M_DMA;
+  // waves 0 .. MG-1 issue one metadata load per step on top of their share
+  // of X and A, so the per-wave load counts differ by one
+  static constexpr int DMA_O = X_DMA + A_DMA;
+  static constexpr int DMA_M = DMA_O + 1;
   static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "wave tiles must be multiples of 32");
   static_assert(X_BYTES % (1024 * NWAVES) == 0 && A_BYTES % (1024 * NWAVES) == 0, "even load split");
-  static_assert(!SPARSE || RB % NWAVES == 0, "metadata loads must split evenly among waves");
+  static_assert(AM != A_DECOMP || RB % NWAVES == 0, "the expansion splits row blocks evenly among waves");
+  static_assert(RB >= 4 ? RB % 4 == 0 : RB == 2, "row blocks come in whole metadata groups or one half");
+  static_assert(MG <= NWAVES, "one metadata load per wave at most");
   static_assert(CPR >= 16, "the chunk swizzle needs at least 16 chunks per row");
   static_assert(2 * STAGE + D_BYTES <= LDS_LIMIT, "two stages must fit in LDS");
-  static_assert(DMA < 64, "vmcnt range");
+  static_assert(3 * DMA_M < 64, "vmcnt range");
 };
 
 template <int I, int N, typename F>
@@ -131,6 +138,14 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// vmcnt wait for a count that depends on whether this wave issues a metadata
+// load per step (the wave index is uniform, so this is a scalar branch).
+template <int N_META, int N_OTHER>
+__device__ __forceinline__ void wait_vmcnt_by_wave(bool meta_wave) {
+  if (meta_wave) wait_vmcnt<N_META>();
+  else wait_vmcnt<N_OTHER>();
 }
 
 // lgkmcnt(0) tied to the registers that carry the LDS reads: every use of
@@ -242,22 +257,26 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     xt_jstride = (uint32_t)(8 * C::NWAVES * ldx * 2);       // q advances by NWAVES (even: parity kept)
     static_assert(C::NWAVES % 2 == 0, "X^T loads keep the row-pair parity per wave");
   }
-  // A values / metadata: load j fills the (row block, step) block q = j*NWAVES + wave
-  // (metadata: row block q) of the stage.  Only the lane part of the address is
-  // per lane; the block part is wave-uniform and goes into the scalar offset.
-  // Row blocks past the matrix read past the resource end and come back as zeros.
+  // A values: load j fills the (row block, step) block q = j*NWAVES + wave of
+  // the stage.  Metadata: wave w < MG loads group w (four row blocks, 1 KiB per
+  // K-pair).  Only the lane part of an address is per lane; the block part is
+  // wave-uniform and goes into the scalar offset.  Blocks past the matrix read
+  // past the resource end and come back as zeros.
   const uint32_t a_voff = (uint32_t)lane * 16;
-  const uint32_t m_voff = (uint32_t)lane * 4;
   auto a_block_off = [&](int j) -> uint32_t {
     const int q = j * C::NWAVES + wave;
     return (uint32_t)(((q / ASTEPS) * S + q % ASTEPS) * 1024);
   };
-  auto m_block_off = [&](int j) -> uint32_t { return (uint32_t)((j * C::NWAVES + wave) * T_ * 256); };
+  const bool meta_wave = wave < C::MG;
   const int rb_end = nrb < rb0 + C::RB ? nrb : rb0 + C::RB;
   const __amdgpu_buffer_rsrc_t a_rsrc =
       make_rsrc(args.A + (int64_t)rb0 * S * 512, (uint32_t)((rb_end - rb0) * S * 1024));
+  const int ngroups = (int)(device_row_blocks(M) / 4);       // metadata groups in the array
+  const int g0 = rb0 / 4;
+  const int g_end = ngroups < g0 + C::MG ? ngroups : g0 + C::MG;
   const __amdgpu_buffer_rsrc_t m_rsrc =
-      SPARSE ? make_rsrc(args.Ameta + (int64_t)rb0 * T_ * 64, (uint32_t)((rb_end - rb0) * T_ * 256)) : a_rsrc;
+      SPARSE ? make_rsrc(args.Ameta + (int64_t)g0 * T_ * 256, (uint32_t)((g_end - g0) * T_ * 1024)) : a_rsrc;
+  const int m_in_group = C::RB < 4 ? (rb0 & 3) : 0;         // a 64-row block's row blocks inside its group
   const int n_rows = N - n0 < BN ? N - n0 : BN;
   const __amdgpu_buffer_rsrc_t xt_rsrc =
       make_rsrc(args.X + (XT ? (int64_t)n0 * ldx : 0), (uint32_t)(XT ? (int64_t)n_rows * ldx * 2 : 0));
@@ -302,10 +321,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       dma16_to_lds(a_rsrc, stage + C::X_BYTES + (j * C::NWAVES + wave) * 1024, a_voff,
                    (uint32_t)g * ASTEPS * 1024 + a_block_off(j));
     if constexpr (SPARSE) {
-#pragma unroll
-      for (int j = 0; j < C::M_DMA; ++j)
-        dma4_to_lds(m_rsrc, stage + C::X_BYTES + C::A_BYTES + (j * C::NWAVES + wave) * 256, m_voff,
-                    (uint32_t)g * 256 + m_block_off(j));
+      if (meta_wave)
+        dma16_to_lds(m_rsrc, stage + C::X_BYTES + C::A_BYTES + wave * 1024, a_voff,
+                     (uint32_t)g * 1024 + (uint32_t)wave * T_ * 1024);
     }
   };
 
@@ -323,7 +341,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     }
     a_off[st] = DECOMP ? lds_base + NSTAGE * C::STAGE + wm * TM * 4 * 1024 + lane * 16
                        : base + C::X_BYTES + wm * TM * ASTEPS * 1024 + lane * 16;
-    m_off[st] = base + C::X_BYTES + C::A_BYTES + wm * TM * 256 + lane * 4;
+    m_off[st] = base + C::X_BYTES + C::A_BYTES + (m_in_group + wm * TM) * 256 + lane * 4;
   }
   // X^T fragments: lane (column n = wave cols + 32 j + lane % 32, half h) reads
   // 16 B chunks of k; the fragment j offset (32 rows = 4 KiB) is an immediate.
@@ -361,7 +379,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     static_for<0, C::RB / C::NWAVES>([&](auto J) {
       const int q = decltype(J)::value * C::NWAVES + wave;
       const uint32_t va = cbase + q * ASTEPS * 1024 + lane * 16;
-      uint32_t mw[1] = {lds_read_b32<0>(cbase + C::A_BYTES + q * 256 + lane * 4)};
+      uint32_t mw[1] = {lds_read_b32<0>(cbase + C::A_BYTES + (m_in_group + q) * 256 + lane * 4)};
       i16x8 v[2] = {lds_read_b128<0>(va), lds_read_b128<1024>(va)};
       wait_lds(mw);
       wait_lds(v);
@@ -498,38 +516,45 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       issue_step(min(g, nk - 1), g);
     }
     load_kept(min(NSTAGE, nk - 1), k_cur);
-    wait_vmcnt<(NSTAGE - 1) * C::DMA>();
+    wait_vmcnt_by_wave<(NSTAGE - 1) * C::DMA_M, (NSTAGE - 1) * C::DMA_O>(meta_wave);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    uint32_t meta[TM], meta_n[TM];
+    // The fragment reads are asynchronous (results land at the lgkmcnt wait)
+    // but the compiler treats them as complete at issue, so no read result may
+    // be copied before its wait: the metadata words get one register set per
+    // stage (no copy between steps), and each step ends with the wait for the
+    // next step's first-half reads, ahead of any copy at the loop edge.
+    uint32_t meta[NSTAGE][TM];
     i16x8 a0[TM], a1[TM];
     i16x16 b0[TN], b1[TN];
-    rd_meta(I0{}, meta);
+    rd_meta(I0{}, meta[0]);
     rd_a(I0{}, I0{}, a0);
     rd_b(I0{}, I0{}, b0);
+    wait_lds(meta[0]);
+    wait_lds(a0);
+    wait_lds(b0);
     auto body = [&](auto ST, int it) {
       constexpr int st = decltype(ST)::value;
       constexpr int nx = (st + 1) % NSTAGE;
-      wait_lds(meta);
-      wait_lds(a0);
-      wait_lds(b0);
       rd_a(ST, I1{}, a1);
       rd_b(ST, I1{}, b1);
-      mma_sparse(I0{}, a0, b0, meta);
+      mma_sparse(I0{}, a0, b0, meta[st]);
       wait_lds(a1);
       wait_lds(b1);
-      wait_vmcnt<(NSTAGE - 2) * C::DMA>();
+      wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(meta_wave);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       load_kept(min(it + NSTAGE + 1, nk - 1), k_nxt);
       issue_step(min(it + NSTAGE, nk - 1), st);
       asm volatile("" ::: "memory");
-      rd_meta(std::integral_constant<int, nx>{}, meta_n);
+      rd_meta(std::integral_constant<int, nx>{}, meta[nx]);
       rd_a(std::integral_constant<int, nx>{}, I0{}, a0);
       rd_b(std::integral_constant<int, nx>{}, I0{}, b0);
-      mma_sparse(I1{}, a1, b1, meta);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) meta[i] = meta_n[i];
+      mma_sparse(I1{}, a1, b1, meta[st]);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lds(meta[nx]);
+      wait_lds(a0);
+      wait_lds(b0);
       if constexpr (GATHER) {
 #pragma unroll
         for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
@@ -540,9 +565,6 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
       });
     }
-    wait_lds(a0);
-    wait_lds(b0);
-    wait_lds(meta);
   } else {
     // Step g is loaded into stage g % NSTAGE by the loads issued NSTAGE-1 steps
     // earlier.  At the top of step it the loads of steps it+1 .. it+NSTAGE-2 may
@@ -561,7 +583,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     load_kept(min(NSTAGE - 1, nk - 1), k_cur);
     auto body = [&](auto ST, int it) {
       constexpr int st = decltype(ST)::value;
-      wait_vmcnt<(NSTAGE - 2) * C::DMA>();
+      wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(meta_wave);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       const int gn = it + NSTAGE - 1;

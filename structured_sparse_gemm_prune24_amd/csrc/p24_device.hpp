@@ -14,6 +14,11 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// 32-row blocks of the device layout: M rounded up to whole groups of four
+// blocks, so the metadata of one 128-row group for one K-pair is a single
+// contiguous 1 KiB piece ([rb / 4][t][rb % 4][lane]).
+__host__ __device__ inline int64_t device_row_blocks(int64_t M) { return ((M + 127) / 128) * 4; }
+
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN -> 0x7FC0 | sign.
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(uint32_t u) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);

@@ -39,8 +39,10 @@ def test_size_helpers(L):
     assert L.prune24_values_bytes(3, 36, p24.P24_LAYOUT_CANONICAL) == 3 * 18 * 2
     assert L.prune24_meta_bytes(3, 36, p24.P24_LAYOUT_CANONICAL) == 3 * 2 * 4
     # device: rows rounded up to 32, K % 64 required
-    assert L.prune24_values_bytes(33, 128, p24.P24_LAYOUT_DEVICE) == 64 * 64 * 2
-    assert L.prune24_meta_bytes(33, 128, p24.P24_LAYOUT_DEVICE) == 2 * 2 * 64 * 4
+    assert L.prune24_values_bytes(33, 128, p24.P24_LAYOUT_DEVICE) == 128 * 64 * 2      # rows padded to 128
+    assert L.prune24_meta_bytes(33, 128, p24.P24_LAYOUT_DEVICE) == 4 * 2 * 64 * 4
+    assert L.prune24_values_bytes(128, 64, p24.P24_LAYOUT_DEVICE) == 128 * 32 * 2
+    assert L.prune24_meta_bytes(129, 64, p24.P24_LAYOUT_DEVICE) == 8 * 1 * 64 * 4
     assert L.prune24_values_bytes(32, 96, p24.P24_LAYOUT_DEVICE) == 0
     assert L.prune24_values_bytes(4, 6, p24.P24_LAYOUT_CANONICAL) == 0
     assert L.tvw_workspace_bytes(4096, 4096, 128, 2048) == 32 * 4096 * 8

@@ -108,11 +108,11 @@ def test_device_layout_through_instruction_model():
     Xb = (X.view(np.uint32) >> 16).astype(np.uint16)
     values, meta = O.compress_24(W, "f32")
     dv, dm = O.to_device_layout(values, meta, K)
-    RB, S, T = M // 32, K // 32, K // 64
+    RB, S, T = O.device_rows(M) // 32, K // 32, K // 64
     dv = O.bf16_to_f64(dv.reshape(RB, S, 64, 8))
-    dm = dm.reshape(RB, T, 64)
+    dm = dm.reshape(RB // 4, T, 4, 64).transpose(0, 2, 1, 3).reshape(RB, T, 64)   # [rb // 4, t, rb % 4, L]
     Xf = O.bf16_to_f64(Xb)
-    Y = np.zeros((M, N))
+    Y = np.zeros((RB * 32, N))
     for rb in range(RB):
         acc = np.zeros((64, 16))
         for s in range(S):
@@ -127,4 +127,5 @@ def test_device_layout_through_instruction_model():
             for i in range(16):
                 Y[32 * rb + 8 * (i // 4) + 4 * (lo // 32) + i % 4, lo % 32] = acc[lo, i]
     y_ref, _ = O.gemm_ref(O.decompress_24(values, meta, K), Xb)
-    assert np.array_equal(Y, y_ref)
+    assert np.array_equal(Y[:M], y_ref)
+    assert not Y[M:].any()          # padded rows: zero values
