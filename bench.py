@@ -143,8 +143,18 @@ def measured_traffic():
     return int(b.group(1))
 
 
+COLD_BYTES = 512 << 20
+
+
+def prune24_bytes(wl):
+    """Compressed W bytes (values + metadata) of a workload."""
+    k = wl.keep_k or wl.K
+    return wl.M * k // 2 * 2 + wl.M * k // 8
+
+
 def table(args):
-    """Per-workload timings (HIP events, mean of args.steps launches after args.warmup)."""
+    """Per-workload timings: HIP-graph replay of args.steps calls on one buffer set (warm MALL),
+    and the same calls rotating through enough sets that inputs come from HBM (cold)."""
     import numpy as np
     import torch
 
@@ -158,6 +168,10 @@ def table(args):
     def timeit(fn):
         return graph_time_us(torch, fn, reps=args.steps)
 
+    def timeit_rot(fns):
+        calls = [fns[i % len(fns)] for i in range(max(args.steps, 2 * len(fns)))]
+        return graph_time_us(torch, lambda: [f() for f in calls], reps=1) / len(calls)
+
     for key, wl in workloads.WORKLOADS.items():
         W = torch.from_numpy(workloads.weights(wl)).to(dev)
         Xb = workloads.activations(wl)
@@ -166,13 +180,25 @@ def table(args):
         out_dtype = torch.bfloat16 if wl.out_dtype == "bf16" else torch.float32
         Y = torch.empty((wl.M, wl.N), dtype=out_dtype, device=dev)
         rec = {"workload": key, "M": wl.M, "K": wl.K, "N": wl.N, "out": wl.out_dtype}
+        # cold-cache variant: rotate through enough input/output sets (>= 512 MB in
+        # all, at most 32 sets) that nothing stays in the 256 MB MALL between calls
+        set_bytes = (prune24_bytes(wl) + wl.K * wl.N * 2 + wl.M * wl.N * Y.element_size())
+        nsets = int(min(32, max(2, -(-COLD_BYTES // set_bytes))))
+        rec["cold_sets"] = nsets
         if wl.tile_m:
             t = p24.tvw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
             rec["spmm_tvw_us"] = timeit(lambda: p24.spmm_tvw(t, X, out=Y))
+            sets = [(p24.tvw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k), X.clone(), torch.empty_like(Y))
+                    for _ in range(nsets)]
+            rec["spmm_tvw_cold_us"] = timeit_rot([lambda s=s_: p24.spmm_tvw(s[0], s[1], out=s[2]) for s_ in sets])
             sparse_us = rec["spmm_tvw_us"]
+            del sets
         else:
             c = p24.compress(W)
             rec["spmm24_us"] = timeit(lambda: p24.spmm24(c, X, out=Y))
+            sets = [(p24.compress(W), X.clone(), torch.empty_like(Y)) for _ in range(nsets)]
+            rec["spmm24_cold_us"] = timeit_rot([lambda s=s_: p24.spmm24(s[0], s[1], out=s[2]) for s_ in sets])
+            del sets
             rec["spmm24_xt_us"] = timeit(lambda: p24.spmm24_xt(c, XT, out=Y))
             rec["spmm24_decomp_mfma_us"] = timeit(lambda: p24.spmm24(c, X, out=Y, algo="decomp_mfma"))
             rec["transpose_x_us"] = timeit(lambda: p24.transpose(X, out=XT))
@@ -182,10 +208,11 @@ def table(args):
         rec["gemm_bf16_xt_us"] = timeit(lambda: p24.gemm_bf16_xt(Wp, wl.M, wl.K, XT, out=Y))
         rec["dense_eq_tflops"] = wl.dense_flops / (sparse_us * 1e-6) / 1e12
         rec["speedup_vs_dense"] = rec["gemm_bf16_us"] / sparse_us
-        bytes_alg = (wl.M * (wl.keep_k or wl.K) // 2 * 2 + wl.M * (wl.keep_k or wl.K) // 8 + wl.K * wl.N * 2
-                     + wl.M * wl.N * (2 if wl.out_dtype == "bf16" else 4))
+        bytes_alg = prune24_bytes(wl) + wl.K * wl.N * 2 + wl.M * wl.N * (2 if wl.out_dtype == "bf16" else 4)
         rec["algorithmic_bytes"] = bytes_alg
         rec["hbm_frac"] = bytes_alg / (sparse_us * 1e-6) / (PEAK_HBM_GBS * 1e9)
+        cold_us = rec.get("spmm24_cold_us", rec.get("spmm_tvw_cold_us"))
+        rec["hbm_frac_cold"] = bytes_alg / (cold_us * 1e-6) / (PEAK_HBM_GBS * 1e9)
         rec["mfma_frac"] = wl.kept_flops / (sparse_us * 1e-6) / (PEAK_BF16_MFMA_TFLOPS * 1e12)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in rec.items()}), flush=True)
         del W, X, XT, Y, Wp
