@@ -79,8 +79,10 @@ __global__ __launch_bounds__(256) void k_compress_canonical(const T* __restrict_
 // owns group 64 c + l of every row, so each row is one contiguous read (1 KiB
 // of fp32).  The device layout puts that group at step s = 8 c + l / 8, lane
 // half h = (l / 4) % 2, pair q = l % 4 of lane L = r + 32 h of block (rb, s):
-// the wave collects its up-to-8 value blocks and 4 metadata blocks in LDS and
-// writes them out as contiguous 16 B (values) and 4 B (metadata) pieces.
+// the wave collects its up-to-8 value blocks and 4 metadata blocks in LDS.
+// Every 8 rows complete two whole 128 B lines of each value block (lanes r and
+// r + 32), which are written right away so that stores interleave with the
+// loads; the metadata goes out at the end as contiguous 4 B pieces.
 // Staging pads (4 words after every 32 lanes of a block, 8 per block, one
 // per metadata row) spread one row's writes over distinct banks.
 // Rows M..Mp-1 (Mp = M rounded up to 128) are padding: zero values, positions
@@ -111,31 +113,46 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
   const int sl = lane >> 3, hl = (lane >> 2) & 1, ql = lane & 3;
   uint32_t* vst = sv[wv];
   uint32_t* mst = sm[wv];
-#pragma unroll 8
-  for (int r = 0; r < 32; ++r) {
-    const int64_t m = rb * 32 + r;
-    uint16_t v0 = 0, v1 = 0;
-    uint32_t code = 0x4u;                // positions (0, 1) for padding rows
-    if (m < M && gv) {
-      const int32_t* kept_row = GATHER ? kept + (m / tile_m) * K : nullptr;
-      uint32_t b[4];
-      fetch_group<T, GATHER>(W, ldw, m, g, kept_row, kmax, b);
-      code = compress_group<T>(b, v0, v1);
-    }
-    const int L = r + 32 * hl;
-    vst[sl * CMP_BLK_WORDS + L * 4 + hl * 4 + ql] = (uint32_t)v0 | ((uint32_t)v1 << 16);
-    // 16-bit code of (step, half): the 4 pairs' nibbles; the metadata word of
-    // K-pair t holds step 2t in bits 0-15 and step 2t+1 in bits 16-31
-    uint32_t c16 = code << (4 * ql);
-    c16 |= __shfl_xor(c16, 1);
-    c16 |= __shfl_xor(c16, 2);
-    const uint32_t hi = __shfl_xor(c16, 8);
-    if (ql == 0 && (sl & 1) == 0) mst[(sl >> 1) * CMP_META_PITCH + L] = c16 | (hi << 16);
-  }
+  // Branch-free rows: padding rows and lanes past K read a clamped in-range
+  // group and then take the padding result (zero values, positions (0, 1)).
+  const int64_t g_rd = gv ? g : G - 1;
   u32x4* vout = reinterpret_cast<u32x4*>(dvals + (rb * S + 8 * c) * 64 * 8);
-  for (int j = 0; j < ns; ++j) {
-    const uint32_t* e = vst + j * CMP_BLK_WORDS + lane * 4 + (lane >> 5) * 4;
-    vout[j * 64 + lane] = u32x4{e[0], e[1], e[2], e[3]};
+  for (int r0 = 0; r0 < 32; r0 += 8) {
+#pragma unroll
+    for (int rr = 0; rr < 8; ++rr) {
+      const int r = r0 + rr;
+      const int64_t m = rb * 32 + r;
+      const bool live = m < M && gv;
+      const int64_t m_rd = m < M ? m : M - 1;
+      const int32_t* kept_row = GATHER ? kept + (m_rd / tile_m) * K : nullptr;
+      uint32_t b[4];
+      fetch_group<T, GATHER>(W, ldw, m_rd, g_rd, kept_row, kmax, b);
+      uint16_t v0, v1;
+      uint32_t code = compress_group<T>(b, v0, v1);
+      const uint32_t packed = live ? ((uint32_t)v0 | ((uint32_t)v1 << 16)) : 0u;
+      code = live ? code : 0x4u;
+      const int L = r + 32 * hl;
+      vst[sl * CMP_BLK_WORDS + L * 4 + hl * 4 + ql] = packed;
+      // 16-bit code of (step, half): the 4 pairs' nibbles, gathered with DPP
+      // lane permutes inside each quad; the metadata word of K-pair t holds step
+      // 2t in bits 0-15 and step 2t+1 (the lanes 8 higher) in bits 16-31
+      uint32_t c16 = code << (4 * ql);
+      c16 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)c16, 0xB1, 0xF, 0xF, false);   // quad_perm [1,0,3,2]: lane ^ 1
+      c16 |= (uint32_t)__builtin_amdgcn_mov_dpp((int)c16, 0x4E, 0xF, 0xF, false);   // quad_perm [2,3,0,1]: lane ^ 2
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)c16, 0x128, 0xF, 0xF, false);  // row_ror:8: lane ^ 8
+      if (ql == 0 && (sl & 1) == 0) mst[(sl >> 1) * CMP_META_PITCH + L] = c16 | (hi << 16);
+    }
+    // rows r0..r0+7 complete lanes r0..r0+7 and r0+32..r0+39 of every block:
+    // two whole 128 B lines per block, written now
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int q = t * 64 + lane, j = q >> 4, idx = q & 15;
+      const int L = r0 + (idx & 7) + 32 * (idx >> 3);
+      if (j < ns) {
+        const uint32_t* e = vst + j * CMP_BLK_WORDS + L * 4 + (L >> 5) * 4;
+        vout[j * 64 + L] = u32x4{e[0], e[1], e[2], e[3]};
+      }
+    }
   }
   uint32_t* mout = dmeta + (((rb >> 2) * T_ + 4 * c) * 4 + (rb & 3)) * 64;
   for (int j = 0; j < ns / 2; ++j) mout[j * 256 + lane] = mst[j * CMP_META_PITCH + lane];

@@ -20,9 +20,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __host__ __device__ inline int64_t device_row_blocks(int64_t M) { return ((M + 127) / 128) * 4; }
 
 // fp32 -> bf16 bits, round to nearest, ties to even; NaN -> 0x7FC0 | sign.
+// Both results are computed and one is selected (no branch).
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(uint32_t u) {
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7FC0u);
-  return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+  const uint32_t rne = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t qnan = ((u >> 16) & 0x8000u) | 0x7FC0u;
+  return (uint16_t)((u & 0x7FFFFFFFu) > 0x7F800000u ? qnan : rne);
 }
 
 // 2-of-4 selection under (magnitude key descending, index ascending).
@@ -63,9 +65,11 @@ __device__ __forceinline__ uint32_t compress_group(const uint32_t b[4], uint16_t
   const uint32_t code = select_2of4(GroupIO<T>::key(b[0]), GroupIO<T>::key(b[1]),
                                     GroupIO<T>::key(b[2]), GroupIO<T>::key(b[3]));
   const uint32_t p0 = code & 3u, p1 = code >> 2;
-  // select by position without dynamic register indexing
-  const uint32_t w0 = p0 == 0 ? b[0] : (p0 == 1 ? b[1] : b[2]);
-  const uint32_t w1 = p1 == 1 ? b[1] : (p1 == 2 ? b[2] : b[3]);
+  // select by position with masks (no dynamic register indexing, no branches)
+  const uint32_t w0 = (b[0] & (0u - (uint32_t)(p0 == 0))) | (b[1] & (0u - (uint32_t)(p0 == 1))) |
+                      (b[2] & (0u - (uint32_t)(p0 == 2)));
+  const uint32_t w1 = (b[1] & (0u - (uint32_t)(p1 == 1))) | (b[2] & (0u - (uint32_t)(p1 == 2))) |
+                      (b[3] & (0u - (uint32_t)(p1 == 3)));
   v0 = GroupIO<T>::to_bf16(w0);
   v1 = GroupIO<T>::to_bf16(w1);
   return code;
