@@ -285,15 +285,31 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
       if ((x & hi_mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
     }
     __syncthreads();
-    if (tid == 0) {
-      int64_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= need) break;
-        above += hist[d];
+    if (tid < 64) {
+      // one wave finds the digit: lane l owns bins 4l .. 4l+3; `above` counts
+      // the keys in all higher bins (a suffix scan over lanes, high to low)
+      const int l = tid;
+      const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
+      const uint32_t own = h0 + h1 + h2 + h3;
+      uint32_t incl = own;                 // inclusive suffix sum over lanes l .. 63
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t o = __shfl_down(incl, d);
+        if (l + d < 64) incl += o;
       }
-      sh_prefix = prefix | ((uint64_t)d << shift);
-      sh_need = need - above;
+      const int64_t above = incl - own;
+      if (above < need && above + own >= need) {
+        // the cut lies in this lane's bins: walk them from the highest
+        int64_t a = above;
+        int d = 4 * l + 3;
+        const uint32_t hb[4] = {h0, h1, h2, h3};
+        for (int i = 3; i > 0 && a + hb[i] < need; --i) {
+          a += hb[i];
+          --d;
+        }
+        sh_prefix = prefix | ((uint64_t)d << shift);
+        sh_need = need - a;
+      }
     }
     __syncthreads();
     prefix = sh_prefix;
