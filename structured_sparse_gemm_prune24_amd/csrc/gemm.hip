@@ -726,12 +726,10 @@ static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
   switch (choose_tile(a.M, a.N)) {
     // The 256 x 256 tile runs 8 waves (2 x 4, each 128 x 64), two per SIMD:
     // while one wave waits on LDS reads or the stage barrier the other issues
-    // MFMAs.  The 128 x 256 smfmac tile keeps one wave row (each wave: all 128
-    // rows x 64 columns, a B fragment feeding 4 MFMAs), since its 4 metadata
-    // blocks cannot split over 8 waves.
+    // MFMAs.  The 128 x 256 smfmac tile does the same with 64 x 64 per wave.
     case Tile::T256x256: return launch_cfg<256, 256, 2, 4, AM, XM>(a, y_dtype, st);
     case Tile::T128x256:
-      if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 1, 4, AM, XM>(a, y_dtype, st);
+      if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 2, 4, AM, XM>(a, y_dtype, st);
       else return launch_cfg<128, 256, 2, 2, AM, XM>(a, y_dtype, st);
     case Tile::T128x128: return launch_cfg<128, 128, 2, 2, AM, XM>(a, y_dtype, st);
     case Tile::T64x128: return launch_cfg<64, 128, 1, 2, AM, XM>(a, y_dtype, st);
@@ -820,8 +818,8 @@ extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, 
   a.Kc = (int)keep_k;
   a.Kx = (int)K;
   a.tile_m = (int)tile_m;
-  // one block row = one 128-row slice of a TVW tile
-  return launch_cfg<128, 256, 1, 4, A_SPARSE, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
+  // one block row = one 128-row slice of a TVW tile; 8 waves (2 x 4, each 64 x 64)
+  return launch_cfg<128, 256, 2, 4, A_SPARSE, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
