@@ -731,15 +731,17 @@ static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
     case Tile::T128x256:
       if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 2, 4, AM, XM>(a, y_dtype, st);
       else return launch_cfg<128, 256, 2, 2, AM, XM>(a, y_dtype, st);
-    // The smaller smfmac tiles also take more waves than their dense
-    // counterparts (2 x 4 of 64 x 32, and 2 x 2 of 32 x 64): the skinny shapes
-    // that use them are latency-bound, and the extra waves hide LDS and load
-    // waits (measured 15 % and 9 % faster on the ResNet-50 1x1 and 3x3 shapes).
+    // The smaller tiles take as many waves as their shape allows (2 x 4 of
+    // 64 x 32, and 2 x 2 of 32 x 64): the skinny shapes that use them are
+    // latency-bound, and the extra waves hide LDS and load waits (measured
+    // 9-20 % faster on the ResNet-50 1x1 and 3x3 shapes, sparse and dense).
+    // The expanded-tile path keeps its 4 and 2 waves (its expansion splits row
+    // blocks over waves).
     case Tile::T128x128:
-      if constexpr (AM == A_SPARSE) return launch_cfg<128, 128, 2, 4, AM, XM>(a, y_dtype, st);
+      if constexpr (AM != A_DECOMP) return launch_cfg<128, 128, 2, 4, AM, XM>(a, y_dtype, st);
       else return launch_cfg<128, 128, 2, 2, AM, XM>(a, y_dtype, st);
     case Tile::T64x128:
-      if constexpr (AM == A_SPARSE) return launch_cfg<64, 128, 2, 2, AM, XM>(a, y_dtype, st);
+      if constexpr (AM != A_DECOMP) return launch_cfg<64, 128, 2, 2, AM, XM>(a, y_dtype, st);
       else return launch_cfg<64, 128, 1, 2, AM, XM>(a, y_dtype, st);
   }
   return P24_ERR_UNSUPPORTED;
