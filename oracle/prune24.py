@@ -37,6 +37,8 @@ Readings where the pages are silent (each one is listed in the design notes):
   * GEMM tolerance: |y - y_ref| <= 1e-3 * (|W|.|X|)_ij on the fp32 result; a
     bf16 result also gets the half-ulp of its final rounding,
     2^-8 * (|y_ref| + 1e-3 * (|W|.|X|)).
+  * fused epilogue: y = act(W X + b), b per output row, act none / ReLU / exact
+    GELU (see ``fused_ref``).
 
 Parity pins for every function here live in ``tests/test_oracle_*.py``.
 """
@@ -347,6 +349,70 @@ def spmm_ref_sparse(values: np.ndarray, meta: np.ndarray, K: int, X: np.ndarray,
         ks = 4 * (s // 2) + pos[i]
         y[i] = bf16_to_f64(values[m]) @ Xf[ks]
     return y
+
+
+# ----------------------------------------------------------------------------
+# Fused epilogue: y = act(W X + b).  "Accelerating Sparse DNNs Based on Tiled
+# GEMM" (TL;DR) names kernel fusion among its techniques without details; the
+# reading here: b holds one fp32 value per output row (feature), added to the
+# product before the activation; act is none, ReLU (z > 0 ? z : 0, so NaN -> 0)
+# or GELU in its exact form z * Phi(z) = z/2 (1 + erf(z / sqrt 2)), the one
+# BERT uses.
+# ----------------------------------------------------------------------------
+ACT_NONE, ACT_RELU, ACT_GELU = 0, 1, 2
+GELU_LIPSCHITZ = 1.13            # max |d/dz z Phi(z)| = 1.1289... (pinned in the tests)
+ACT_REL_ERR = 2.0 ** -20         # allowance for the kernel's fp32 evaluation of the activation
+
+
+def act_ref(z: np.ndarray, act: int) -> np.ndarray:
+    """Activation in fp64."""
+    z = np.asarray(z, dtype=np.float64)
+    if act == ACT_NONE:
+        return z.copy()
+    if act == ACT_RELU:
+        return np.where(z > 0, z, 0.0)
+    if act == ACT_GELU:
+        from scipy.special import erf
+        return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+    raise ValueError(act)
+
+
+def fused_ref(Wd: np.ndarray, X: np.ndarray, bias, act: int, rows=None):
+    """(y_ref, z_ref, bound): y = act(W X + b) in fp64, the pre-activation z and the GEMM bound."""
+    y, bnd = gemm_ref(Wd, X, rows=rows)
+    M = np.asarray(Wd).shape[0]
+    b = np.zeros(M) if bias is None else np.asarray(bias, dtype=np.float32).astype(np.float64)
+    if rows is not None:
+        b = b[np.asarray(rows)]
+    z = y + b[:, None]
+    return act_ref(z, act), z, bnd
+
+
+def fused_tolerance(y_ref: np.ndarray, z_ref: np.ndarray, bound: np.ndarray, act: int,
+                    out_dtype: str) -> np.ndarray:
+    """Bound on |y - y_ref| for the fused result: the GEMM bound plus one fp32
+    rounding of the bias add, carried through the activation's Lipschitz
+    constant, plus the activation's own evaluation error, then the output
+    rounding (bf16: half an ulp of the result)."""
+    lip = {ACT_NONE: 1.0, ACT_RELU: 1.0, ACT_GELU: GELU_LIPSCHITZ}[act]
+    pre = TOL_REL * bound + 2.0 ** -23 * np.abs(z_ref)
+    tol = lip * pre + (ACT_REL_ERR * np.abs(y_ref) if act == ACT_GELU else 0.0)
+    if out_dtype == "f32":
+        return tol
+    if out_dtype == "bf16":
+        return tol + BF16_HALF_ULP * (np.abs(y_ref) + tol)
+    raise ValueError(out_dtype)
+
+
+def check_fused(y, y_ref, z_ref, bound, act: int, out_dtype: str):
+    """(ok, worst err/tol ratio) for a fused result.  Non-finite outputs fail."""
+    y = np.asarray(y, dtype=np.float64)
+    tol = fused_tolerance(y_ref, z_ref, bound, act, out_dtype)
+    err = np.abs(y - y_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tol > 0, err / tol, np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return bool(np.isfinite(y).all() and worst <= 1.0), worst
 
 
 def tolerance(y_ref: np.ndarray, bound: np.ndarray, out_dtype: str) -> np.ndarray:
