@@ -144,6 +144,7 @@ def measured_traffic():
 
 
 COLD_BYTES = 512 << 20
+FUSED_ACT = {"c1": "gelu", "c2": "gelu", "c3a": "relu", "c3b": "relu", "c4": "gelu"}
 
 
 def prune24_bytes(wl):
@@ -199,6 +200,16 @@ def table(args):
             sets = [(p24.compress(W), X.clone(), torch.empty_like(Y)) for _ in range(nsets)]
             rec["spmm24_cold_us"] = timeit_rot([lambda s=s_: p24.spmm24(s[0], s[1], out=s[2]) for s_ in sets])
             del sets
+            # fused epilogue with the layer's usual activation (BERT: GELU, ResNet: ReLU), bias per
+            # output row; beside it (context only) the same result unfused: the product, then a
+            # separate bias + activation pass over Y in torch
+            act = FUSED_ACT.get(key, "gelu")
+            b = torch.randn(wl.M, device=dev, dtype=torch.float32) * 0.1
+            rec["fused_act"] = act
+            rec["spmm24_fused_us"] = timeit(lambda: p24.spmm24(c, X, out=Y, bias=b, act=act))
+            tact = torch.nn.functional.gelu if act == "gelu" else torch.relu
+            rec["unfused_torch_us"] = timeit(
+                lambda: Y.copy_(tact(p24.spmm24(c, X, out=Y).float() + b[:, None]).to(Y.dtype)))
             rec["spmm24_xt_us"] = timeit(lambda: p24.spmm24_xt(c, XT, out=Y))
             rec["spmm24_decomp_mfma_us"] = timeit(lambda: p24.spmm24(c, X, out=Y, algo="decomp_mfma"))
             rec["transpose_x_us"] = timeit(lambda: p24.transpose(X, out=XT))

@@ -86,6 +86,8 @@ enum {
 enum { P24_F32 = 0, P24_BF16 = 1 };                         /* element dtypes */
 enum { P24_LAYOUT_CANONICAL = 0, P24_LAYOUT_DEVICE = 1 };    /* compressed layouts */
 enum { P24_ALGO_AUTO = 0, P24_ALGO_SMFMAC = 1, P24_ALGO_DECOMP_MFMA = 2 };   /* spmm24 algorithms */
+enum { P24_X_KN = 0, P24_X_NK = 1 };                            /* spmm24_fused: X orientation */
+enum { P24_ACT_NONE = 0, P24_ACT_RELU = 1, P24_ACT_GELU = 2 };  /* spmm24_fused: activation */
 
 /* ABI version of the loaded library (PRUNE24_ABI_VERSION). */
 P24_API int32_t prune24_abi_version(void);
@@ -167,6 +169,29 @@ P24_API p24_status spmm24(const void* values, const void* meta, int32_t layout, 
 P24_API p24_status spmm24_xt(const void* values, const void* meta, int32_t layout, int64_t M,
                              int64_t K, const void* XT, int64_t ldxt, int64_t N, void* Y,
                              int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * spmm24_fused -- Y = act(W X + b) in one pass: the sparse-MFMA product with a
+ * bias add and an activation applied to the fp32 accumulator before the
+ * output rounding (kernel fusion, "Accelerating Sparse DNNs Based on Tiled
+ * GEMM", TL;DR).
+ *   x_order   P24_X_KN: X is K x N with the rules of spmm24 (ldx, alignment,
+ *             readable tail); P24_X_NK: X is given as N x K with the rules of
+ *             spmm24_xt (ldx is then its leading dimension, >= K).
+ *   bias      M fp32 values, one per output row (added to every column), 4 B
+ *             aligned; NULL adds nothing.
+ *   act       P24_ACT_NONE; P24_ACT_RELU: z > 0 ? z : 0 (NaN -> 0);
+ *             P24_ACT_GELU: z * Phi(z) = z/2 (1 + erf(z / sqrt 2)), evaluated
+ *             in fp32 with erf from Abramowitz & Stegun 7.1.26 (absolute error
+ *             <= 1.5e-7).  Other codes: P24_ERR_UNSUPPORTED.
+ * Everything else (layout, K % 64, Y, determinism) as for spmm24.  With
+ * bias == NULL and P24_ACT_NONE the result equals spmm24's (or spmm24_xt's)
+ * bit for bit.
+ */
+P24_API p24_status spmm24_fused(const void* values, const void* meta, int32_t layout, int64_t M,
+                                int64_t K, const void* X, int64_t ldx, int32_t x_order, int64_t N,
+                                void* Y, int32_t y_dtype, int64_t ldy, const float* bias,
+                                int32_t act, void* stream);
 
 /*
  * transpose_bf16 -- dst = src^T for 16-bit elements (a bit copy).

@@ -36,6 +36,9 @@ P24_F32, P24_BF16 = 0, 1
 P24_LAYOUT_CANONICAL, P24_LAYOUT_DEVICE = 0, 1
 P24_ALGO_AUTO, P24_ALGO_SMFMAC, P24_ALGO_DECOMP_MFMA = 0, 1, 2
 _ALGOS = {"auto": P24_ALGO_AUTO, "smfmac": P24_ALGO_SMFMAC, "decomp_mfma": P24_ALGO_DECOMP_MFMA}
+P24_X_KN, P24_X_NK = 0, 1
+P24_ACT_NONE, P24_ACT_RELU, P24_ACT_GELU = 0, 1, 2
+_ACTS = {"none": P24_ACT_NONE, "relu": P24_ACT_RELU, "gelu": P24_ACT_GELU}
 
 _c_i32, _c_i64, _c_size, _c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
 
@@ -56,6 +59,8 @@ _SIGNATURES = {
                           _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
     "spmm24_xt": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                            _c_i64, _c_vp]),
+    "spmm24_fused": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_vp,
+                              _c_i32, _c_i64, _c_vp, _c_i32, _c_vp]),
     "transpose_bf16": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
     "gemm_bf16_xt": (_c_i32, [_c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
     "gemm_bf16_packed_bytes": (_c_size, [_c_i64, _c_i64]),
@@ -205,11 +210,28 @@ def decompress(c: Compressed24):
     return out
 
 
-def spmm24(c: Compressed24, X, out_dtype=None, out=None, algo="auto"):
-    """Y = W X for compressed W (device layout) and X bf16 [K, N].
+def _fused_args(bias, act, M, device):
+    """(bias pointer, act code, needs fused) after checking bias and act."""
+    torch = _torch()
+    if act not in _ACTS:
+        raise ValueError(f"act must be one of {sorted(_ACTS)}")
+    if bias is None:
+        return None, _ACTS[act], act != "none"
+    _require_cuda(bias, "bias")
+    if bias.dtype != torch.float32 or bias.dim() != 1 or bias.shape[0] != M or not bias.is_contiguous():
+        raise ValueError(f"bias must be a contiguous fp32 vector of {M} values")
+    if bias.device != device:
+        raise ValueError("bias must be on the same device as X")
+    return _ptr(bias), _ACTS[act], True
+
+
+def spmm24(c: Compressed24, X, out_dtype=None, out=None, algo="auto", bias=None, act="none"):
+    """Y = act(W X + bias) for compressed W (device layout) and X bf16 [K, N].
 
     algo: "smfmac" (sparse MFMA on the compressed operand; what "auto" picks) or
-    "decomp_mfma" (operand expanded to a dense LDS tile, dense MFMA)."""
+    "decomp_mfma" (operand expanded to a dense LDS tile, dense MFMA).
+    bias (fp32 [M], one value per output row) and act ("none", "relu", "gelu")
+    run fused in the sparse-MFMA kernel's epilogue."""
     torch = _torch()
     if algo not in _ALGOS:
         raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
@@ -224,6 +246,14 @@ def spmm24(c: Compressed24, X, out_dtype=None, out=None, algo="auto"):
     if out is None:
         out = torch.empty((c.M, N), dtype=out_dtype, device=X.device)
     ldy = _rowmajor(out, "out")
+    bptr, act_code, fused = _fused_args(bias, act, c.M, X.device)
+    if fused:
+        if algo == "decomp_mfma":
+            raise ValueError("the fused epilogue runs with the sparse MFMA (algo 'auto' or 'smfmac')")
+        _check(lib().spmm24_fused(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(X), ldx, P24_X_KN, N,
+                                  _ptr(out), _out_code(out.dtype), ldy, bptr, act_code, _stream(X.device)),
+               "spmm24_fused")
+        return out
     _check(lib().spmm24(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(X), ldx, N, _ptr(out),
                         _out_code(out.dtype), ldy, _ALGOS[algo], _stream(X.device)), "spmm24")
     return out
@@ -317,8 +347,8 @@ def transpose(src, out=None):
     return out
 
 
-def spmm24_xt(c: Compressed24, XT, out_dtype=None, out=None):
-    """Y = W X for compressed W with X supplied transposed: XT bf16 [N, K]."""
+def spmm24_xt(c: Compressed24, XT, out_dtype=None, out=None, bias=None, act="none"):
+    """Y = act(W X + bias) for compressed W with X supplied transposed: XT bf16 [N, K]."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
     _require_cuda(XT, "XT")
@@ -331,6 +361,12 @@ def spmm24_xt(c: Compressed24, XT, out_dtype=None, out=None):
     if out is None:
         out = torch.empty((c.M, N), dtype=out_dtype, device=XT.device)
     ldy = _rowmajor(out, "out")
+    bptr, act_code, fused = _fused_args(bias, act, c.M, XT.device)
+    if fused:
+        _check(lib().spmm24_fused(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(XT), ldxt, P24_X_NK, N,
+                                  _ptr(out), _out_code(out.dtype), ldy, bptr, act_code, _stream(XT.device)),
+               "spmm24_fused")
+        return out
     _check(lib().spmm24_xt(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(XT), ldxt, N, _ptr(out),
                            _out_code(out.dtype), ldy, _stream(XT.device)), "spmm24_xt")
     return out

@@ -175,7 +175,34 @@ struct GemmArgs {
   int M, N, Kc, Kx;        // Kc: K of the W operand (compacted for TVW); Kx: rows of X
   int tile_m;              // TVW tile rows
   int nbm, nbn;            // block grid
+  const float* bias;       // fused epilogue: one value per output row, or nullptr
+  int act;                 // fused epilogue: P24_ACT_NONE / _RELU / _GELU
 };
+
+// GELU in its exact form z * Phi(z) = z/2 (1 + erf(z / sqrt 2)), fp32.  erf
+// comes from Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26: for x >= 0, erfc(x) = (a1 t + ... + a5 t^5) exp(-x^2) + e(x),
+// t = 1 / (1 + p x), |e(x)| <= 1.5e-7.  With q = erfc(|z| / sqrt 2) the result
+// is z/2 (2 - q) for z >= 0 and z/2 q below, which keeps the negative side
+// free of cancellation.
+__device__ __forceinline__ float gelu_f32(float z) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  const float q = poly * __builtin_amdgcn_exp2f(-x * x * 1.44269504088896341f);
+  return 0.5f * z * (z >= 0.0f ? 2.0f - q : q);
+}
+
+// Epilogue activation in fp32.
+__device__ __forceinline__ float apply_act(float v, int act) {
+  if (act == P24_ACT_RELU) return v > 0.0f ? v : 0.0f;
+  if (act == P24_ACT_GELU) return gelu_f32(v);
+  return v;
+}
 
 // Buffer resource over [base, base + bytes): raw (untyped) loads, no swizzle.
 // Loads past `bytes` return zero instead of faulting.
@@ -190,7 +217,7 @@ __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_dst, 4, voff, soff, 0, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, int AM, int XM, typename OutT>
+template <int BM, int BN, int WGM, int WGN, int AM, int XM, typename OutT, int EPI>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   using C = TileCfg<BM, BN, WGM, WGN, AM>;
   constexpr bool SPARSE = C::SPARSE, SMFMAC = AM == A_SPARSE, DECOMP = AM == A_DECOMP;
@@ -619,13 +646,18 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // MFMA result holds one column per lane, the store wants rows.  Slice i is
   // written as [32 rows][WTN cols] with a 16 B pad per row (the two row
   // halves a write instruction touches land on disjoint banks), read back as
-  // 16 B row pieces and stored with one 16 B store per piece when Y allows
-  // it, element by element at ragged edges or for an unaligned Y.
+  // 16 B row pieces and stored whole when Y allows it, element by element at
+  // ragged edges or for an unaligned Y.  The fused variants (EPI = 1: bias,
+  // ReLU; EPI = 2: bias, GELU) stage acc + bias in fp32 and apply the
+  // activation and the output rounding on the way out.
   __builtin_amdgcn_s_barrier();   // every wave's loads have landed and its reads are done
   asm volatile("" ::: "memory");
+  constexpr bool FUSED = EPI != 0;
+  using StageT = typename std::conditional<FUSED, float, OutT>::type;
   constexpr int ES = (int)sizeof(OutT);
-  constexpr int PITCH = C::WTN * ES + 16;           // bytes per staged row
-  constexpr int VEC = 16 / ES;                      // elements per 16 B piece
+  constexpr int SES = (int)sizeof(StageT);
+  constexpr int PITCH = C::WTN * SES + 16;          // bytes per staged row
+  constexpr int VEC = 16 / SES;                     // staged elements per 16 B piece
   constexpr int PPR = C::WTN / VEC;                 // pieces per row
   constexpr int PPL = 32 * PPR / 64;                // pieces per lane per slice
   static_assert(C::NWAVES * 32 * PITCH <= NSTAGE * C::STAGE + C::D_BYTES, "epilogue staging fits in LDS");
@@ -634,8 +666,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   uint8_t* region = lds + wave * 32 * PITCH;
   const int row_w = m0 + wm * C::WTM;
   const int col_w = n0 + wn * C::WTN;
-  const bool vec_ok = ((uintptr_t)Y % 16 == 0) && ((args.ldy * ES) % 16 == 0);
-  // The staged slice is written as OutT and read back as 16 B words: the
+  const bool vec_ok = ((uintptr_t)Y % 16 == 0) && ((args.ldy * ES) % 16 == 0);   // 16 B row stores
+  // fused: the bias of every row this lane stages, loaded once (16 rows per slice)
+  float bz[FUSED ? TM : 1][16];
+  if constexpr (FUSED) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = row_w + 32 * i + 8 * (e >> 2) + 4 * h + (e & 3);
+        bz[i][e] = args.bias ? args.bias[row < M ? row : M - 1] : 0.0f;
+      }
+  }
+  // The staged slice is written as StageT and read back as 16 B words: the
   // compiler barriers keep those differently typed accesses in program order
   // (the wave's LDS operations then execute in that order).
 #pragma unroll
@@ -646,27 +689,69 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
         const int r = 8 * (e >> 2) + 4 * h + (e & 3);
-        OutT v;
-        if constexpr (ES == 2) v = f32_to_bf16_rne(__float_as_uint(acc[i][j][e]));
+        StageT v;
+        if constexpr (FUSED) v = acc[i][j][e] + bz[i][e];
+        else if constexpr (ES == 2) v = f32_to_bf16_rne(__float_as_uint(acc[i][j][e]));
         else v = acc[i][j][e];
-        *reinterpret_cast<OutT*>(region + r * PITCH + (32 * j + (lane & 31)) * ES) = v;
+        *reinterpret_cast<StageT*>(region + r * PITCH + (32 * j + (lane & 31)) * SES) = v;
       }
     asm volatile("" ::: "memory");
+    if constexpr (FUSED) {
+      // VO outputs per 16 B store, read as VO staged fp32 values (32 B for a
+      // bf16 output, 16 B for fp32)
+      constexpr int VO = 16 / ES;
+      constexpr int PRO = C::WTN / VO;              // stores per row
+      constexpr int PLO = 32 * PRO / 64;            // stores per lane per slice
+      static_assert((32 * PRO) % 64 == 0, "whole stores per lane");
+      // the GELU variant keeps this loop rolled: unrolling it measured no
+      // faster and quadruples the code
+#pragma unroll(EPI == 2 ? 1 : PLO)
+      for (int t = 0; t < PLO; ++t) {
+        const int q = t * 64 + lane;
+        const int r = q / PRO, cc = (q % PRO) * VO;
+        const int row = row_w + 32 * i + r, col = col_w + cc;
+        float zf[VO];
 #pragma unroll
-    for (int t = 0; t < PPL; ++t) {
-      const int q = t * 64 + lane;
-      const int r = q / PPR, cc = (q % PPR) * VEC;
-      const u32x4 piece = *reinterpret_cast<const u32x4*>(region + r * PITCH + cc * ES);
-      const int row = row_w + 32 * i + r, col = col_w + cc;
-      if (row >= M) continue;
-      OutT* dst = Y + (int64_t)row * args.ldy + col;
-      if (vec_ok && col + VEC <= N) {
-        *reinterpret_cast<u32x4*>(dst) = piece;
-      } else {
-        const OutT* pv = reinterpret_cast<const OutT*>(&piece);
+        for (int w = 0; w < VO / 4; ++w) {
+          const u32x4 piece = *reinterpret_cast<const u32x4*>(region + r * PITCH + (cc + 4 * w) * 4);
 #pragma unroll
-        for (int u = 0; u < VEC; ++u)
-          if (col + u < N) dst[u] = pv[u];
+          for (int u = 0; u < 4; ++u) zf[4 * w + u] = __uint_as_float(piece[u]);
+        }
+        if (row >= M) continue;
+        OutT o[VO];
+#pragma unroll
+        for (int u = 0; u < VO; ++u) {
+          const float z = zf[u];
+          const float f = EPI == 2 ? apply_act(z, P24_ACT_GELU) : (args.act == P24_ACT_RELU ? (z > 0.0f ? z : 0.0f) : z);
+          if constexpr (ES == 2) o[u] = f32_to_bf16_rne(__float_as_uint(f));
+          else o[u] = f;
+        }
+        OutT* dst = Y + (int64_t)row * args.ldy + col;
+        if (vec_ok && col + VO <= N) {
+          *reinterpret_cast<u32x4*>(dst) = __builtin_bit_cast(u32x4, o);
+        } else {
+#pragma unroll
+          for (int u = 0; u < VO; ++u)
+            if (col + u < N) dst[u] = o[u];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int t = 0; t < PPL; ++t) {
+        const int q = t * 64 + lane;
+        const int r = q / PPR, cc = (q % PPR) * VEC;
+        const u32x4 piece = *reinterpret_cast<const u32x4*>(region + r * PITCH + cc * SES);
+        const int row = row_w + 32 * i + r, col = col_w + cc;
+        if (row >= M) continue;
+        OutT* dst = Y + (int64_t)row * args.ldy + col;
+        if (vec_ok && col + VEC <= N) {
+          *reinterpret_cast<u32x4*>(dst) = piece;
+        } else {
+          const OutT* pv = reinterpret_cast<const OutT*>(&piece);
+#pragma unroll
+          for (int u = 0; u < VEC; ++u)
+            if (col + u < N) dst[u] = pv[u];
+        }
       }
     }
   }
@@ -677,15 +762,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 // ---------------------------------------------------------------------------
 enum class Tile { T256x256, T128x256, T128x128, T64x128 };
 
-template <int BM, int BN, int WGM, int WGN, int AM, int XM>
+template <int BM, int BN, int WGM, int WGN, int AM, int XM, int EPI = 0>
 static p24_status launch_cfg(GemmArgs a, int32_t y_dtype, hipStream_t st) {
   a.nbm = (a.M + BM - 1) / BM;
   a.nbn = (a.N + BN - 1) / BN;
   const dim3 grid((unsigned)(a.nbm * a.nbn)), block(WGM * WGN * 64);
   if (y_dtype == P24_F32)
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, AM, XM, float>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, AM, XM, float, EPI>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, AM, XM, uint16_t>), grid, block, 0, st, a);
+    hipLaunchKernelGGL((k_gemm<BM, BN, WGM, WGN, AM, XM, uint16_t, EPI>), grid, block, 0, st, a);
   return launch_status();
 }
 
@@ -721,16 +806,16 @@ static Tile choose_tile(int64_t M, int64_t N) {
   return Tile::T64x128;
 }
 
-template <int AM, int XM>
+template <int AM, int XM, int EPI = 0>
 static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
   switch (choose_tile(a.M, a.N)) {
     // The 256 x 256 tile runs 8 waves (2 x 4, each 128 x 64), two per SIMD:
     // while one wave waits on LDS reads or the stage barrier the other issues
     // MFMAs.  The 128 x 256 smfmac tile does the same with 64 x 64 per wave.
-    case Tile::T256x256: return launch_cfg<256, 256, 2, 4, AM, XM>(a, y_dtype, st);
+    case Tile::T256x256: return launch_cfg<256, 256, 2, 4, AM, XM, EPI>(a, y_dtype, st);
     case Tile::T128x256:
-      if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 2, 4, AM, XM>(a, y_dtype, st);
-      else return launch_cfg<128, 256, 2, 2, AM, XM>(a, y_dtype, st);
+      if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 2, 4, AM, XM, EPI>(a, y_dtype, st);
+      else return launch_cfg<128, 256, 2, 2, AM, XM, EPI>(a, y_dtype, st);
     // The smaller tiles take as many waves as their shape allows (2 x 4 of
     // 64 x 32, and 2 x 2 of 32 x 64): the skinny shapes that use them are
     // latency-bound, and the extra waves hide LDS and load waits (measured
@@ -738,11 +823,11 @@ static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
     // The expanded-tile path keeps its 4 and 2 waves (its expansion splits row
     // blocks over waves).
     case Tile::T128x128:
-      if constexpr (AM != A_DECOMP) return launch_cfg<128, 128, 2, 4, AM, XM>(a, y_dtype, st);
-      else return launch_cfg<128, 128, 2, 2, AM, XM>(a, y_dtype, st);
+      if constexpr (AM != A_DECOMP) return launch_cfg<128, 128, 2, 4, AM, XM, EPI>(a, y_dtype, st);
+      else return launch_cfg<128, 128, 2, 2, AM, XM, EPI>(a, y_dtype, st);
     case Tile::T64x128:
-      if constexpr (AM != A_DECOMP) return launch_cfg<64, 128, 2, 2, AM, XM>(a, y_dtype, st);
-      else return launch_cfg<64, 128, 1, 2, AM, XM>(a, y_dtype, st);
+      if constexpr (AM != A_DECOMP) return launch_cfg<64, 128, 2, 2, AM, XM, EPI>(a, y_dtype, st);
+      else return launch_cfg<64, 128, 1, 2, AM, XM, EPI>(a, y_dtype, st);
   }
   return P24_ERR_UNSUPPORTED;
 }
@@ -898,6 +983,47 @@ extern "C" P24_API p24_status spmm24_xt(const void* values, const void* meta, in
   a.Kx = (int)K;
   a.tile_m = 1;
   return dispatch<A_SPARSE, X_NK>(a, y_dtype, (hipStream_t)stream);
+}
+
+// Fused epilogue: Y = act(W X + b), b one fp32 per output row.  X as K x N
+// (P24_X_KN, rules of spmm24) or as N x K (P24_X_NK, rules of spmm24_xt).
+extern "C" P24_API p24_status spmm24_fused(const void* values, const void* meta, int32_t layout, int64_t M,
+                                           int64_t K, const void* X, int64_t ldx, int32_t x_order, int64_t N,
+                                           void* Y, int32_t y_dtype, int64_t ldy, const float* bias, int32_t act,
+                                           void* stream) {
+  if (layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
+  if (x_order != P24_X_KN && x_order != P24_X_NK) return P24_ERR_UNSUPPORTED;
+  if (act != P24_ACT_NONE && act != P24_ACT_RELU && act != P24_ACT_GELU) return P24_ERR_UNSUPPORTED;
+  if (M < 0 || K < 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  p24_status s = x_order == P24_X_KN ? check_xy(X, ldx, N, Y, y_dtype, ldy) : check_xt(X, ldx, N, K, Y, y_dtype, ldy);
+  if (s != P24_OK) return s;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return P24_OK;
+  if (K == 0) return P24_ERR_UNSUPPORTED;
+  if (!values || !meta) return P24_ERR_NULL;
+  if (!aligned(values, 16) || !aligned(meta, 16) || (bias && !aligned(bias, 4))) return P24_ERR_ALIGN;
+  s = check_xy_ptrs(X, ldx, Y, y_dtype);
+  if (s != P24_OK) return s;
+  GemmArgs a{};
+  a.A = (const uint16_t*)values;
+  a.Ameta = (const uint32_t*)meta;
+  a.X = (const uint16_t*)X;
+  a.Y = Y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.Kc = (int)K;
+  a.Kx = (int)K;
+  a.tile_m = 1;
+  a.bias = bias;
+  a.act = act;
+  if (act == P24_ACT_GELU) {
+    if (x_order == P24_X_NK) return dispatch<A_SPARSE, X_NK, 2>(a, y_dtype, (hipStream_t)stream);
+    return dispatch<A_SPARSE, X_KN, 2>(a, y_dtype, (hipStream_t)stream);
+  }
+  if (x_order == P24_X_NK) return dispatch<A_SPARSE, X_NK, 1>(a, y_dtype, (hipStream_t)stream);
+  return dispatch<A_SPARSE, X_KN, 1>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16_xt(const void* Wp, int64_t M, int64_t K, const void* XT, int64_t ldxt,

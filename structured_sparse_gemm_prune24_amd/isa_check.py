@@ -8,9 +8,10 @@ while the compiler treats them as written at issue.  Any instruction that reads
 the compiler adds -- works on stale data, and the result depends on timing.
 
 `pending_lds_uses(asm)` scans every kernel of a device assembly file in program
-order and reports those instructions.  The scan is linear: a branch does not
-reset what is pending, and only `lgkmcnt(0)` clears it (the kernels wait with
-lgkmcnt(0) only), so it over-reports rather than misses.
+order and reports those instructions.  LDS operations complete in issue order,
+so `s_waitcnt lgkmcnt(N)` leaves only the newest N LDS / scalar-memory
+operations in flight; the scan keeps that queue.  It is linear: a branch does
+not reset what is pending, so it over-reports rather than misses.
 """
 from __future__ import annotations
 
@@ -39,24 +40,30 @@ def pending_lds_uses(asm: str) -> Dict[str, List[str]]:
     """Kernel name -> instructions that touch a VGPR with an LDS read still in flight."""
     out: Dict[str, List[str]] = {}
     for name, body in _KERNEL.findall(asm):
-        pending: set = set()
+        queue: List[set] = []        # in-flight LDS / scalar-memory operations, oldest first (read destinations)
         bad: List[str] = []
         for raw in body.split("\n"):
             line = raw.split(";")[0].strip()
             if not line or line.endswith(":") or line.startswith("."):
                 continue
             op, ops = _operands(line)
+            pending = set().union(*queue) if queue else set()
             if op == "s_waitcnt":
                 m = re.search(r"lgkmcnt\((\d+)\)", line)
-                if m and int(m.group(1)) == 0:
-                    pending.clear()
+                if m:
+                    n = int(m.group(1))
+                    del queue[:max(0, len(queue) - n)]
                 continue
-            if op.startswith("ds_read"):
-                dst = _vregs(ops[0]) if ops else set()
-                srcs = set().union(*(_vregs(o) for o in ops[1:])) if len(ops) > 1 else set()
+            if op.startswith("ds_"):
+                is_read = op.startswith("ds_read") or op.startswith("ds_bpermute") or op.startswith("ds_permute")
+                dst = _vregs(ops[0]) if (ops and is_read) else set()
+                srcs = set().union(*(_vregs(o) for o in (ops[1:] if is_read else ops))) if ops else set()
                 if srcs & pending:
                     bad.append(line)
-                pending |= dst
+                queue.append(dst)
+                continue
+            if op.startswith(("s_load", "s_buffer_load", "s_memtime", "s_memrealtime")):
+                queue.append(set())
                 continue
             if op.startswith("s_"):
                 continue

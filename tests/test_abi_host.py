@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 16
+    assert len(syms) == len(set(syms)) == 17
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -90,6 +90,26 @@ def test_spmm_validation(L):
     assert f(*args(v=NUL)) == p24.P24_ERR_NULL
     assert f(*args(M=0, v=NUL, m=NUL, X=NUL, Y=NUL)) == p24.P24_OK
     assert f(*args(N=0, ldx=0, ldy=0, v=NUL, m=NUL, X=NUL, Y=NUL)) == p24.P24_OK
+
+
+def test_fused_validation(L):
+    f = L.spmm24_fused
+    args = lambda **k: [k.get("v", FAKE), k.get("m", FAKE), k.get("layout", 1), k.get("M", 64),
+                        k.get("K", 128), k.get("X", FAKE), k.get("ldx", 128), k.get("xo", 0), k.get("N", 64),
+                        k.get("Y", FAKE), k.get("yd", 0), k.get("ldy", 64), k.get("bias", NUL),
+                        k.get("act", 0), NUL]
+    assert f(*args(layout=0)) == p24.P24_ERR_LAYOUT
+    assert f(*args(xo=2)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(act=3)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(act=-1)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(K=96)) == p24.P24_ERR_UNSUPPORTED
+    assert f(*args(yd=3)) == p24.P24_ERR_DTYPE
+    assert f(*args(bias=MISALIGNED)) == p24.P24_ERR_ALIGN
+    assert f(*args(v=NUL)) == p24.P24_ERR_NULL
+    assert f(*args(ldx=32, xo=0)) == p24.P24_ERR_SHAPE          # K x N: ldx < N
+    assert f(*args(ldx=96, xo=1)) == p24.P24_ERR_SHAPE          # N x K: ldx < K
+    assert f(*args(M=0, v=NUL, m=NUL, X=NUL, Y=NUL, act=2)) == p24.P24_OK
+    assert f(*args(N=0, ldy=0, v=NUL, m=NUL, X=NUL, Y=NUL, act=1)) == p24.P24_OK
 
 
 def test_tvw_validation(L):

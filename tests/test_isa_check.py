@@ -38,6 +38,17 @@ def test_partial_wait_keeps_pending():
     assert I.pending_lds_uses(asm)
 
 
+def test_partial_wait_completes_older_reads():
+    # two reads in flight; lgkmcnt(1) completes the older one only
+    asm = _k("\tds_read_b32 v10, v1\n\tds_read_b32 v11, v2\n\ts_waitcnt lgkmcnt(1)\n"
+             "\tv_add_u32_e32 v3, v10, v4\n\tv_add_u32_e32 v5, v11, v4\n\ts_waitcnt lgkmcnt(0)\n")
+    found = list(I.pending_lds_uses(asm).values())
+    assert len(found) == 1 and found[0] == ["v_add_u32_e32 v5, v11, v4"]
+    # an LDS write counts in the queue too
+    asm = _k("\tds_read_b32 v10, v1\n\tds_write_b32 v2, v3\n\ts_waitcnt lgkmcnt(1)\n\tv_mov_b32_e32 v5, v10\n")
+    assert I.pending_lds_uses(asm) == {}
+
+
 def test_built_kernels_are_clean():
     path = B.device_asm(os.path.join(B.CSRC, "gemm.hip"))
     if not os.path.exists(path):
