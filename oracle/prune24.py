@@ -326,6 +326,80 @@ def tvw_decompress(kept: np.ndarray, values: np.ndarray, meta: np.ndarray, M: in
 
 
 # ----------------------------------------------------------------------------
+# TVW with per-tile keep counts ("Accelerating Sparse DNNs Based on Tiled GEMM",
+# Abstract: a structured pattern inside each tile, irregular pruning across
+# tiles; TL;DR: load balancing through batching).  Reading, for tile_m = 128:
+#   * plan: rank every (tile, column) score of tvw_scores over the whole matrix
+#     (score descending, then flat index t*K + k ascending); tile t's raw count
+#     c_t is the number of its columns among the top total_keep; its keep count
+#     is c_t rounded to the nearest multiple of 64 (halves up), clamped to
+#     [64, K] -- 64 columns are one K step of the kernels, and every tile keeps
+#     at least one;
+#   * tile t keeps its count highest-scored columns (tvw_select's order),
+#     listed ascending, then 2:4 over its compacted axis;
+#   * storage: the tiles' device-layout blocks one after another in tile order;
+#   * batching order: tiles by keep count descending, then tile ascending.
+# ----------------------------------------------------------------------------
+VAR_STEP = 64
+
+
+def tvw_var_counts(W: np.ndarray, tile_m: int, total_keep: int) -> np.ndarray:
+    """Per-tile keep counts, int32 [T]."""
+    sc = tvw_scores(W, tile_m)
+    T, K = sc.shape
+    if K % VAR_STEP or not (0 < total_keep <= T * K):
+        raise ValueError("K must be a multiple of 64 and 0 < total_keep <= T*K")
+    key = sc.view(np.uint64).reshape(-1)
+    ranked = np.argsort(np.iinfo(np.uint64).max - key, kind="stable")
+    raw = np.bincount(ranked[:total_keep] // K, minlength=T)
+    counts = VAR_STEP * ((raw + VAR_STEP // 2) // VAR_STEP)
+    return np.clip(counts, VAR_STEP, K).astype(np.int32)
+
+
+def tvw_var_compress(W: np.ndarray, tile_m: int, counts):
+    """Per tile: (kept int32 [c_t] ascending, values u16 [rows_t, c_t/2], meta u32 [rows_t, c_t/32])."""
+    W = np.asarray(W, dtype=np.float32)
+    M, K = W.shape
+    key = tvw_scores(W, tile_m).view(np.uint64)
+    out = []
+    for t, c in enumerate(np.asarray(counts)):
+        order = np.argsort(np.iinfo(np.uint64).max - key[t], kind="stable")
+        kept = np.sort(order[:int(c)]).astype(np.int32)
+        r0, r1 = t * tile_m, min(M, (t + 1) * tile_m)
+        values, meta = compress_24(W[r0:r1][:, kept], "f32")
+        out.append((kept, values, meta))
+    return out
+
+
+def tvw_var_device(tiles, counts):
+    """(kept flat int32, device values flat u16, device meta flat u32, offsets int32 [T+1]):
+    each tile's device layout (128 rows) appended in tile order."""
+    kept = np.concatenate([k for k, _, _ in tiles]).astype(np.int32)
+    dv, dm = [], []
+    for (k, v, m), c in zip(tiles, counts):
+        a, b = to_device_layout(v, m, int(c))
+        dv.append(a)
+        dm.append(b)
+    offsets = np.concatenate([[0], np.cumsum(np.asarray(counts, dtype=np.int64))]).astype(np.int32)
+    return kept, np.concatenate(dv), np.concatenate(dm), offsets
+
+
+def tvw_var_order(counts) -> np.ndarray:
+    """Batching order: keep count descending, then tile ascending."""
+    counts = np.asarray(counts)
+    return np.lexsort((np.arange(len(counts)), -counts)).astype(np.int32)
+
+
+def tvw_var_decompress(tiles, M: int, K: int, tile_m: int) -> np.ndarray:
+    """Dense bf16 bits [M, K] with every tile's compacted columns scattered back."""
+    out = np.zeros((M, K), dtype=np.uint16)
+    for t, (kept, values, meta) in enumerate(tiles):
+        r0, r1 = t * tile_m, min(M, (t + 1) * tile_m)
+        out[r0:r1][:, kept] = decompress_24(values, meta, len(kept))
+    return out
+
+
+# ----------------------------------------------------------------------------
 # GEMM reference and bound (fp64; every bf16 x bf16 product is exact in fp64)
 # ----------------------------------------------------------------------------
 def gemm_ref(Wd: np.ndarray, X: np.ndarray, rows=None):
