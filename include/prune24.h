@@ -128,7 +128,9 @@ P24_API p24_status prune24_decompress(const void* values, const void* meta, int3
  *   values, meta  compressed W in P24_LAYOUT_DEVICE (the layout the sparse MFMA
  *                 reads directly; other layouts return P24_ERR_LAYOUT).
  *   M, K          logical shape of W; K % 64 == 0 (else P24_ERR_UNSUPPORTED).
- *   X             K x N bf16, leading dim ldx >= N, ldx % 8 == 0, 16 B aligned.
+ *   X             K x N bf16, leading dim ldx >= N, ldx % 8 == 0, 16 B aligned;
+ *                 128 * ldx < 2^32 (one K step of rows is addressed with 32 bits),
+ *                 else P24_ERR_UNSUPPORTED.
  *                 The kernel reads X in 16 B pieces: when N % 8 != 0 the last
  *                 row must stay readable up to column roundup(N, 8) - 1 (any
  *                 values there are ignored).
@@ -231,12 +233,54 @@ P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64_t M, int64
  *   (whole, contiguous N-slices).  Needs tile_m % 128 == 0 and keep_k % 64 == 0.
  *   kept entries must lie in [0, K); the kernel clamps out-of-range entries
  *   into that range (the result is then meaningless but no access leaves X).
- *   Other arguments as for spmm24.
+ *   Gathered rows are addressed with 32 bits from X: 2 * K * ldx < 2^32, else
+ *   P24_ERR_UNSUPPORTED.  Other arguments as for spmm24.
  */
 P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, const void* meta,
                             int32_t layout, int64_t M, int64_t K, int64_t tile_m,
                             int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
                             int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
+ * TVW with a keep count per tile ("Accelerating Sparse DNNs Based on Tiled
+ * GEMM", Abstract: regular structure inside a tile, irregular pruning across
+ * the matrix; TL;DR: load balancing through batching).  Tiles are 128 rows:
+ * T = ceil(M/128).
+ * tvw_var_compress -- scores as for tvw_compress (tile_m = 128).  All T*K
+ *   (tile, column) scores are ranked (score descending, then t*K + k
+ *   ascending) and the top total_keep taken; tile t keeps c_t columns, its
+ *   number of those rounded to the nearest multiple of 64 (halves up) and
+ *   clamped to [64, K].  Tile t's c_t highest-scored columns (ties -> lower k),
+ *   ascending, are compressed 2:4 along the compacted axis.
+ *   W            M x K fp32 (P24_F32), ldw % 4 == 0, 16 B aligned; K % 64 == 0;
+ *                M, K <= 2^31 - 1 and T*K <= 2^31 - 1.  0 < total_keep <= T*K.
+ *   offsets      output int64 [T + 1], 8 B aligned: offsets[t] = c_0 + ... + c_{t-1};
+ *                offsets[T] is the total of kept columns (at most T*K).
+ *   order        output int32 [T]: the tiles by c_t descending, then tile
+ *                ascending (the GEMM's block-row order: heavy tiles first).
+ *   kept         output int32, capacity T*K: tile t's columns at
+ *                [offsets[t], offsets[t+1]).
+ *   values       output, capacity T*K*128 bytes, 16 B aligned: tile t's 128 x c_t
+ *                compressed rows in P24_LAYOUT_DEVICE from byte 128*offsets[t].
+ *   meta         output, capacity T*K*16 bytes, 16 B aligned: the tile's device
+ *                metadata from byte 16*offsets[t].  Rows past M are padding
+ *                (zero values, positions 0 and 1).
+ *   workspace    device scratch, tvw_var_workspace_bytes(M, K) bytes, 256 B
+ *                aligned; contents on entry do not matter.
+ * spmm_tvw_var -- Y = W X for that storage: rows of tile t take
+ *   sum_j Wc_t[m][j] X[kept[offsets[t] + j]][n].  Block rows run in `order`.
+ *   offsets / order / kept as written by tvw_var_compress (out-of-range kept
+ *   entries are clamped into [0, K)); X, Y as for spmm_tvw (2 * K * ldx < 2^32).
+ */
+P24_API size_t tvw_var_workspace_bytes(int64_t M, int64_t K);
+P24_API p24_status tvw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                    int64_t total_keep, int64_t* offsets, int32_t* order, int32_t* kept,
+                                    void* values, void* meta, void* workspace, size_t ws_bytes,
+                                    void* stream);
+P24_API p24_status spmm_tvw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                                const void* values, const void* meta, int64_t M, int64_t K,
+                                const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
+                                int64_t ldy, void* stream);
 
 /*
  * Dense bf16 GEMM, the denominator of every speedup ("over the dense model",

@@ -57,6 +57,11 @@ _SIGNATURES = {
                               _c_i32, _c_vp, _c_size, _c_vp]),
     "spmm_tvw": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
                           _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
+    "tvw_var_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "tvw_var_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
+                                  _c_vp, _c_vp, _c_size, _c_vp]),
+    "spmm_tvw_var": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp,
+                              _c_i32, _c_i64, _c_vp]),
     "spmm24_xt": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                            _c_i64, _c_vp]),
     "spmm24_fused": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_vp,
@@ -175,6 +180,21 @@ class CompressedTVW:
     tile_m: int
     keep_k: int
     layout: int
+
+
+@dataclass
+class CompressedTVWVar:
+    """TVW with a keep count per 128-row tile: tile t's columns are
+    kept[offsets[t]:offsets[t+1]] and its device-layout storage starts at
+    column offsets[t] of the concatenation; `order` lists the tiles heaviest first."""
+    offsets: object      # torch.int64 [T + 1]
+    order: object        # torch.int32 [T]
+    kept: object         # torch.int32, capacity T*K
+    values: object       # torch.bfloat16, capacity T*K*64
+    meta: object         # torch.int32, capacity T*K*4
+    M: int
+    K: int
+    total_keep: int
 
 
 def compress(W, layout="device") -> Compressed24:
@@ -298,6 +318,52 @@ def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None):
     ldy = _rowmajor(out, "out")
     _check(lib().spmm_tvw(_ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.layout, t.M, t.K, t.tile_m, t.keep_k,
                           _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tvw")
+    return out
+
+
+def tvw_var_compress(W, total_keep: int | None = None) -> CompressedTVWVar:
+    """TVW with per-tile keep counts from one global ranking of the 128-row tiles'
+    column scores (total_keep columns over all tiles, default half of them)."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("tvw_var_compress takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    T = (M + 127) // 128
+    total_keep = T * K // 2 if total_keep is None else int(total_keep)
+    L = lib()
+    dev = W.device
+    cap = max(T * K, 1)
+    offsets = torch.empty(T + 1, dtype=torch.int64, device=dev)
+    order = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    kept = torch.empty(cap, dtype=torch.int32, device=dev)
+    values = torch.empty(cap * 64, dtype=torch.bfloat16, device=dev)
+    meta = torch.empty(cap * 4, dtype=torch.int32, device=dev)
+    wsb = L.tvw_var_workspace_bytes(M, K)
+    ws = torch.empty(max(wsb, 256), dtype=torch.uint8, device=dev)
+    _check(L.tvw_var_compress(_ptr(W), P24_F32, M, K, ldw, total_keep, _ptr(offsets), _ptr(order), _ptr(kept),
+                              _ptr(values), _ptr(meta), _ptr(ws), ws.numel(), _stream(dev)), "tvw_var_compress")
+    return CompressedTVWVar(offsets, order, kept, values, meta, M, K, total_keep)
+
+
+def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None):
+    """Y = W X for a per-tile-keep TVW matrix; X bf16 [K, N]."""
+    torch = _torch()
+    out_dtype = out_dtype or torch.bfloat16
+    _require_cuda(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    ldx = _rowmajor(X, "X")
+    if X.shape[0] != t.K:
+        raise ValueError(f"X has {X.shape[0]} rows, W has K = {t.K}")
+    N = X.shape[1]
+    if out is None:
+        out = torch.empty((t.M, N), dtype=out_dtype, device=X.device)
+    ldy = _rowmajor(out, "out")
+    _check(lib().spmm_tvw_var(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.M,
+                              t.K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)),
+           "spmm_tvw_var")
     return out
 
 

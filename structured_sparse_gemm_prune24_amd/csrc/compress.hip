@@ -3,6 +3,8 @@
 #include "p24_api_internal.hpp"
 #include "p24_device.hpp"
 
+#include <algorithm>
+
 namespace p24 {
 
 // --------------------------------------------------------------------------
@@ -93,20 +95,39 @@ constexpr int CMP_WAVES = 4;
 constexpr int CMP_BLK_WORDS = 264;    // 64 lanes x 4 words + 2 pads of 4
 constexpr int CMP_META_PITCH = 65;
 
-template <typename T, bool GATHER>
+// Gather modes: none; one kept list of K columns per tile_m rows; per-tile
+// keep counts (128-row tiles, tile t's list and storage start at column
+// offsets[t] of the concatenation, its compacted K is offsets[t+1] - offsets[t]).
+enum GatherMode { G_NONE = 0, G_FIXED = 1, G_VAR = 2 };
+
+template <typename T, int GM>
 __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __restrict__ W, int64_t ldw, int64_t M,
                                                                     int64_t K, uint16_t* __restrict__ dvals,
                                                                     uint32_t* __restrict__ dmeta,
                                                                     const int32_t* __restrict__ kept,
+                                                                    const int64_t* __restrict__ offsets,
                                                                     int64_t tile_m, int64_t kmax) {
+  constexpr bool GATHER = GM != G_NONE;
   __shared__ uint32_t sv[CMP_WAVES][8 * CMP_BLK_WORDS];
   __shared__ uint32_t sm[CMP_WAVES][4 * CMP_META_PITCH];
-  const int64_t RB = device_row_blocks(M), S = K / 32, T_ = K / 64, G = K / 4;
-  const int64_t NC = (K + 255) / 256;
+  const int64_t RB = device_row_blocks(M);
+  const int64_t NC = (K + 255) / 256;    // K: the widest compacted row
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t wid = (int64_t)blockIdx.x * CMP_WAVES + wv;
   if (wid >= RB * NC) return;            // wave-uniform
   const int64_t rb = wid / NC, c = wid % NC;
+  int64_t Kc = K, rbl = rb;              // compacted K, row block inside the storage
+  const int32_t* kept_tile = nullptr;
+  if constexpr (GM == G_VAR) {
+    const int64_t t = rb >> 2, p = offsets[t];
+    Kc = offsets[t + 1] - p;
+    if (256 * c >= Kc) return;           // wave-uniform: past this tile's columns
+    rbl = rb & 3;
+    kept_tile = kept + p;
+    dvals += p * 64;                     // 128 rows x Kc/2 values per tile
+    dmeta += p * 4;                      // 16 B of metadata per kept column
+  }
+  const int64_t S = Kc / 32, T_ = Kc / 64, G = Kc / 4;
   const int64_t g = 64 * c + lane;
   const bool gv = g < G;
   const int ns = (int)(S - 8 * c < 8 ? S - 8 * c : 8);     // steps in this chunk (even: K % 64 == 0)
@@ -116,7 +137,7 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
   // Branch-free rows: padding rows and lanes past K read a clamped in-range
   // group and then take the padding result (zero values, positions (0, 1)).
   const int64_t g_rd = gv ? g : G - 1;
-  u32x4* vout = reinterpret_cast<u32x4*>(dvals + (rb * S + 8 * c) * 64 * 8);
+  u32x4* vout = reinterpret_cast<u32x4*>(dvals + (rbl * S + 8 * c) * 64 * 8);
   for (int r0 = 0; r0 < 32; r0 += 8) {
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
@@ -124,7 +145,7 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
       const int64_t m = rb * 32 + r;
       const bool live = m < M && gv;
       const int64_t m_rd = m < M ? m : M - 1;
-      const int32_t* kept_row = GATHER ? kept + (m_rd / tile_m) * K : nullptr;
+      const int32_t* kept_row = GM == G_FIXED ? kept + (m_rd / tile_m) * K : kept_tile;
       uint32_t b[4];
       fetch_group<T, GATHER>(W, ldw, m_rd, g_rd, kept_row, kmax, b);
       uint16_t v0, v1;
@@ -154,7 +175,7 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
       }
     }
   }
-  uint32_t* mout = dmeta + (((rb >> 2) * T_ + 4 * c) * 4 + (rb & 3)) * 64;
+  uint32_t* mout = dmeta + (((rbl >> 2) * T_ + 4 * c) * 4 + (rbl & 3)) * 64;
   for (int j = 0; j < ns / 2; ++j) mout[j * 256 + lane] = mst[j * CMP_META_PITCH + lane];
 }
 
@@ -243,11 +264,13 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
 
-// Exclusive block-wide prefix of per-thread counts in thread order; returns
-// this thread's prefix and writes the block total.
-__device__ __forceinline__ int64_t block_exclusive_scan(uint32_t v, int64_t* total, uint32_t* wave_sums) {
+// Exclusive block-wide prefix of per-thread counts in thread order (blocks of
+// SEL_THREADS); returns this thread's prefix and writes the block total.
+template <typename U>
+__device__ __forceinline__ int64_t block_exclusive_scan(U v, int64_t* total, U* wave_sums) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
+  U incl = v;
+  static_assert(sizeof(U) == 4 || sizeof(U) == 8, "32- or 64-bit counts");
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     const uint32_t o = __shfl_up(incl, d);
@@ -265,8 +288,35 @@ __device__ __forceinline__ int64_t block_exclusive_scan(uint32_t v, int64_t* tot
   return before + incl - v;
 }
 
+// Lane l of one wave holds bins 4l .. 4l+3 of a 256-bin digit histogram.
+// The need-th largest key (need >= 1, at most the histogram total) has the
+// digit d at which the keys of bins >= d first reach `need`; the lane that
+// owns d returns true with d and that key's rank among the keys of bin d.
+__device__ __forceinline__ bool find_cut(const uint32_t (&hb)[4], int64_t need, int l, int* digit, int64_t* rest) {
+  const uint32_t own = hb[0] + hb[1] + hb[2] + hb[3];
+  uint32_t incl = own;                 // inclusive suffix sum over lanes l .. 63
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_down(incl, d);
+    if (l + d < 64) incl += o;
+  }
+  const int64_t above = incl - own;
+  if (!(above < need && above + own >= need)) return false;
+  // the cut lies in this lane's bins: walk them from the highest
+  int64_t a = above;
+  int d = 4 * l + 3;
+  for (int i = 3; i > 0 && a + hb[i] < need; --i) {
+    a += hb[i];
+    --d;
+  }
+  *digit = d;
+  *rest = need - a;
+  return true;
+}
+
 __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __restrict__ scores, int64_t K,
-                                                            int64_t keep_k, int32_t* __restrict__ kept) {
+                                                            int64_t keep_k, const int64_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ kept) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t wave_sums[SEL_WAVES];
   __shared__ uint64_t sh_prefix;
@@ -274,6 +324,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
   const int64_t t = blockIdx.x;
   const uint64_t* key = reinterpret_cast<const uint64_t*>(scores + t * K);
   const int tid = threadIdx.x;
+  // per-tile keep counts: this tile's count and list position from the offsets
+  int32_t* kept_out = kept + t * keep_k;
+  if (offsets) {
+    keep_k = offsets[t + 1] - offsets[t];
+    kept_out = kept + offsets[t];
+  }
   uint64_t prefix = 0;        // digits of the threshold found so far (high bits)
   int64_t need = keep_k;      // rank of the threshold among keys matching the prefix
   for (int shift = 56; shift >= 0; shift -= 8) {
@@ -286,29 +342,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
     }
     __syncthreads();
     if (tid < 64) {
-      // one wave finds the digit: lane l owns bins 4l .. 4l+3; `above` counts
-      // the keys in all higher bins (a suffix scan over lanes, high to low)
-      const int l = tid;
-      const uint32_t h0 = hist[4 * l], h1 = hist[4 * l + 1], h2 = hist[4 * l + 2], h3 = hist[4 * l + 3];
-      const uint32_t own = h0 + h1 + h2 + h3;
-      uint32_t incl = own;                 // inclusive suffix sum over lanes l .. 63
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t o = __shfl_down(incl, d);
-        if (l + d < 64) incl += o;
-      }
-      const int64_t above = incl - own;
-      if (above < need && above + own >= need) {
-        // the cut lies in this lane's bins: walk them from the highest
-        int64_t a = above;
-        int d = 4 * l + 3;
-        const uint32_t hb[4] = {h0, h1, h2, h3};
-        for (int i = 3; i > 0 && a + hb[i] < need; --i) {
-          a += hb[i];
-          --d;
-        }
+      const uint32_t hb[4] = {hist[4 * tid], hist[4 * tid + 1], hist[4 * tid + 2], hist[4 * tid + 3]};
+      int d;
+      int64_t rest;
+      if (find_cut(hb, need, tid, &d, &rest)) {
         sh_prefix = prefix | ((uint64_t)d << shift);
-        sh_need = need - a;
+        sh_need = rest;
       }
     }
     __syncthreads();
@@ -323,13 +362,171 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
     const bool gt = k < K && x > prefix;
     const bool eq = k < K && x == prefix;
     int64_t eq_total, keep_total;
-    const int64_t eq_rank = eq_base + block_exclusive_scan(eq ? 1u : 0u, &eq_total, wave_sums);
+    const int64_t eq_rank = eq_base + block_exclusive_scan<uint32_t>(eq ? 1u : 0u, &eq_total, wave_sums);
     const bool keep = gt || (eq && eq_rank < need);
-    const int64_t pos = out_base + block_exclusive_scan(keep ? 1u : 0u, &keep_total, wave_sums);
-    if (keep) kept[t * keep_k + pos] = (int32_t)k;
+    const int64_t pos = out_base + block_exclusive_scan<uint32_t>(keep ? 1u : 0u, &keep_total, wave_sums);
+    if (keep) kept_out[pos] = (int32_t)k;
     eq_base += eq_total;
     out_base += keep_total;
   }
+}
+
+// --------------------------------------------------------------------------
+// TVW with per-tile keep counts (128-row tiles).  Every (tile, column) score
+// of the matrix is ranked, score descending and then flat index t*K + k
+// ascending, and the top total_keep are taken; tile t keeps its number of
+// those rounded to a multiple of 64 (halves up), clamped to [64, K].
+//   * the global cut: the same MSB-first radix select as above, over all T*K
+//     keys; one launch per 8-bit digit, each block adds its LDS histogram to
+//     a global one and the last block to finish picks the digit;
+//   * per tile: keys above the cut and keys equal to it; the equal keys are
+//     taken in flat order, so tile t gets min(eq_t, need - (eq of tiles < t));
+//   * keep counts, their running sum (the tiles' column offsets in the
+//     concatenated storage) and the order of the tiles by count, heaviest first.
+// --------------------------------------------------------------------------
+struct VarSelect {
+  uint64_t prefix;        // the cut's digits found so far
+  int64_t need;           // rank of the cut among the keys matching the prefix
+  uint32_t ticket;        // blocks done in the current pass
+  uint32_t pad;
+  uint32_t hist[256];     // digit histogram of the current pass
+};
+constexpr int VAR_THREADS = 256;
+constexpr int64_t VAR_STEP = 64;
+
+__global__ __launch_bounds__(VAR_THREADS) void k_var_init(VarSelect* __restrict__ vs, int64_t total_keep) {
+  vs->hist[threadIdx.x] = 0u;
+  if (threadIdx.x == 0) {
+    vs->prefix = 0ull;
+    vs->need = total_keep;
+    vs->ticket = 0u;
+    vs->pad = 0u;
+  }
+}
+
+__global__ __launch_bounds__(VAR_THREADS) void k_var_radix(const uint64_t* __restrict__ keys, int64_t n, int shift,
+                                                           VarSelect* __restrict__ vs) {
+  __shared__ uint32_t h[256];
+  __shared__ uint32_t last;
+  const int tid = threadIdx.x;
+  const uint64_t prefix = vs->prefix;
+  const int64_t need = vs->need;
+  h[tid] = 0u;
+  __syncthreads();
+  const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+  for (int64_t i = (int64_t)blockIdx.x * VAR_THREADS + tid; i < n; i += (int64_t)gridDim.x * VAR_THREADS) {
+    const uint64_t x = keys[i];
+    if ((x & hi_mask) == prefix) atomicAdd(&h[(x >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (h[tid]) atomicAdd(&vs->hist[tid], h[tid]);
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&vs->ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  // the last block sees every block's histogram: pick the digit, then clear
+  // the histogram and the ticket for the next pass
+  __threadfence();
+  if (tid < 64) {
+    uint32_t hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      hb[i] = __hip_atomic_load(&vs->hist[4 * tid + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int d;
+    int64_t rest;
+    if (find_cut(hb, need, tid, &d, &rest)) {
+      vs->prefix = prefix | ((uint64_t)d << shift);
+      vs->need = rest;
+    }
+  }
+  __syncthreads();
+  vs->hist[tid] = 0u;
+  if (tid == 0) vs->ticket = 0u;
+}
+
+// keys of tile t above the cut and equal to it; one block per tile
+__global__ __launch_bounds__(VAR_THREADS) void k_var_tile_counts(const uint64_t* __restrict__ keys, int64_t K,
+                                                                 const VarSelect* __restrict__ vs,
+                                                                 int32_t* __restrict__ gt, int32_t* __restrict__ eq) {
+  __shared__ uint32_t sg[VAR_THREADS / 64], se[VAR_THREADS / 64];
+  const int64_t t = blockIdx.x;
+  const uint64_t v = vs->prefix;
+  const uint64_t* key = keys + t * K;
+  uint32_t g = 0, e = 0;
+  for (int64_t k = threadIdx.x; k < K; k += VAR_THREADS) {
+    const uint64_t x = key[k];
+    g += x > v ? 1u : 0u;
+    e += x == v ? 1u : 0u;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    g += __shfl_xor(g, d);
+    e += __shfl_xor(e, d);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sg[threadIdx.x >> 6] = g;
+    se[threadIdx.x >> 6] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t G = 0, E = 0;
+    for (int w = 0; w < VAR_THREADS / 64; ++w) {
+      G += sg[w];
+      E += se[w];
+    }
+    gt[t] = (int32_t)G;
+    eq[t] = (int32_t)E;
+  }
+}
+
+// keep counts and their offsets; one block of SEL_THREADS
+__global__ __launch_bounds__(SEL_THREADS) void k_var_plan(int64_t T, int64_t K, const VarSelect* __restrict__ vs,
+                                                          const int32_t* __restrict__ gt,
+                                                          const int32_t* __restrict__ eq,
+                                                          int64_t* __restrict__ offsets) {
+  __shared__ int64_t wave_sums[SEL_WAVES];
+  const int64_t need = vs->need;
+  int64_t eq_base = 0, off_base = 0;
+  for (int64_t t0 = 0; t0 < T; t0 += SEL_THREADS) {
+    const int64_t t = t0 + threadIdx.x;
+    const bool live = t < T;
+    const int64_t e = live ? eq[t] : 0;
+    int64_t eq_total, keep_total;
+    const int64_t before = eq_base + block_exclusive_scan<int64_t>(e, &eq_total, wave_sums);
+    int64_t take = need - before;
+    take = take < 0 ? 0 : (take > e ? e : take);
+    const int64_t c = live ? gt[t] + take : 0;
+    int64_t keep = VAR_STEP * ((c + VAR_STEP / 2) / VAR_STEP);
+    keep = keep < VAR_STEP ? VAR_STEP : (keep > K ? K : keep);
+    keep = live ? keep : 0;
+    const int64_t off = off_base + block_exclusive_scan<int64_t>(keep, &keep_total, wave_sums);
+    if (live) offsets[t] = off;
+    eq_base += eq_total;
+    off_base += keep_total;
+  }
+  if (threadIdx.x == 0) offsets[T] = off_base;
+}
+
+// order[r] = the tile of rank r by keep count descending, then tile ascending
+__global__ __launch_bounds__(VAR_THREADS) void k_var_order(const int64_t* __restrict__ offsets, int64_t T,
+                                                           int32_t* __restrict__ order) {
+  __shared__ int64_t sc[VAR_THREADS];
+  const int64_t t = (int64_t)blockIdx.x * VAR_THREADS + threadIdx.x;
+  const int64_t ct = t < T ? offsets[t + 1] - offsets[t] : 0;
+  int64_t rank = 0;
+  for (int64_t u0 = 0; u0 < T; u0 += VAR_THREADS) {
+    const int64_t u = u0 + threadIdx.x;
+    sc[threadIdx.x] = u < T ? offsets[u + 1] - offsets[u] : 0;
+    __syncthreads();
+    const int64_t n = T - u0 < VAR_THREADS ? T - u0 : VAR_THREADS;
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t cu = sc[i];
+      rank += (cu > ct || (cu == ct && u0 + i < t)) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  if (t < T) order[rank] = (int32_t)t;
 }
 
 }  // namespace p24
@@ -375,10 +572,11 @@ static p24_status check_compress_args(const void* W, int32_t w_dtype, int64_t M,
   return P24_OK;
 }
 
-template <bool GATHER>
+template <int GM>
 static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
                                   void* values, void* meta, int32_t layout, const int32_t* kept,
-                                  int64_t tile_m, int64_t kmax, hipStream_t st) {
+                                  int64_t tile_m, int64_t kmax, hipStream_t st, const int64_t* offsets = nullptr) {
+  constexpr bool GATHER = GM != G_NONE;
   if (M == 0 || K == 0) return P24_OK;
   if (layout == P24_LAYOUT_CANONICAL) {
     const int64_t n = M * ((K + 31) / 32);
@@ -392,11 +590,11 @@ static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int
     const int64_t waves = device_row_blocks(M) * ((K + 255) / 256);
     const dim3 grid(grid1d(waves, CMP_WAVES)), block(64 * CMP_WAVES);
     if (w_dtype == P24_F32)
-      hipLaunchKernelGGL((k_compress_device<float, GATHER>), grid, block, 0, st,
-                         (const float*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+      hipLaunchKernelGGL((k_compress_device<float, GM>), grid, block, 0, st, (const float*)W, ldw, M, K,
+                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax);
     else
-      hipLaunchKernelGGL((k_compress_device<uint16_t, GATHER>), grid, block, 0, st,
-                         (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+      hipLaunchKernelGGL((k_compress_device<uint16_t, GM>), grid, block, 0, st, (const uint16_t*)W, ldw, M, K,
+                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax);
   }
   return launch_status();
 }
@@ -406,7 +604,7 @@ extern "C" P24_API p24_status prune24_compress(const void* W, int32_t w_dtype, i
                                                void* stream) {
   const p24_status s = check_compress_args(W, w_dtype, M, K, ldw, values, meta, layout);
   if (s != P24_OK) return s;
-  return launch_compress<false>(W, w_dtype, M, K, ldw, values, meta, layout, nullptr, 1, K,
+  return launch_compress<G_NONE>(W, w_dtype, M, K, ldw, values, meta, layout, nullptr, 1, K,
                                 (hipStream_t)stream);
 }
 
@@ -473,9 +671,65 @@ extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64
   p24_status s = launch_status();
   if (s != P24_OK) return s;
   hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
-                     keep_k, kept);
+                     keep_k, (const int64_t*)nullptr, kept);
   s = launch_status();
   if (s != P24_OK) return s;
   // 2:4 along the compacted axis, reading W through the kept column lists
-  return launch_compress<true>(W, w_dtype, M, keep_k, ldw, values, meta, layout, kept, tile_m, K, st);
+  return launch_compress<G_FIXED>(W, w_dtype, M, keep_k, ldw, values, meta, layout, kept, tile_m, K, st);
+}
+
+static int64_t var_tiles(int64_t M) { return (M + 127) / 128; }
+
+extern "C" P24_API size_t tvw_var_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0) return 0;
+  const int64_t T_ = var_tiles(M);
+  const size_t scores = ((size_t)T_ * (size_t)K * sizeof(double) + 255) & ~(size_t)255;
+  const size_t sel = (sizeof(VarSelect) + 255) & ~(size_t)255;
+  return scores + sel + 2 * (size_t)T_ * sizeof(int32_t);
+}
+
+extern "C" P24_API p24_status tvw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                               int64_t total_keep, int64_t* offsets, int32_t* order,
+                                               int32_t* kept, void* values, void* meta, void* workspace,
+                                               size_t ws_bytes, void* stream) {
+  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
+  if (M < 0 || K <= 0 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0) return P24_OK;
+  const int64_t T_ = var_tiles(M);
+  if (T_ * K > INT32_MAX || total_keep <= 0 || total_keep > T_ * K) return P24_ERR_SHAPE;
+  if (!W || !offsets || !order || !kept || !values || !meta) return P24_ERR_NULL;
+  if (!workspace || ws_bytes < tvw_var_workspace_bytes(M, K)) return P24_ERR_WORKSPACE;
+  if (!aligned(W, 16) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4) ||
+      !aligned(offsets, 8) || !aligned(order, 4) || !aligned(workspace, 256))
+    return P24_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  double* scores = (double*)ws;
+  ws += ((size_t)T_ * (size_t)K * sizeof(double) + 255) & ~(size_t)255;
+  VarSelect* vs = (VarSelect*)ws;
+  ws += (sizeof(VarSelect) + 255) & ~(size_t)255;
+  int32_t* gt = (int32_t*)ws;
+  int32_t* eq = gt + T_;
+  const int64_t n = T_ * K;
+  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(n, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
+                     (int64_t)128, scores);
+  hipLaunchKernelGGL(k_var_init, dim3(1), dim3(VAR_THREADS), 0, st, vs, total_keep);
+  const int64_t per_block = (int64_t)VAR_THREADS * 8;
+  const unsigned radix_blocks = (unsigned)std::min<int64_t>((n + per_block - 1) / per_block, 1024);
+  for (int shift = 56; shift >= 0; shift -= 8)
+    hipLaunchKernelGGL(k_var_radix, dim3(radix_blocks), dim3(VAR_THREADS), 0, st, (const uint64_t*)scores, n,
+                       shift, vs);
+  hipLaunchKernelGGL(k_var_tile_counts, dim3((unsigned)T_), dim3(VAR_THREADS), 0, st, (const uint64_t*)scores, K,
+                     (const VarSelect*)vs, gt, eq);
+  hipLaunchKernelGGL(k_var_plan, dim3(1), dim3(SEL_THREADS), 0, st, T_, K, (const VarSelect*)vs,
+                     (const int32_t*)gt, (const int32_t*)eq, offsets);
+  hipLaunchKernelGGL(k_var_order, dim3(grid1d(T_, VAR_THREADS)), dim3(VAR_THREADS), 0, st,
+                     (const int64_t*)offsets, T_, order);
+  hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
+                     (int64_t)0, (const int64_t*)offsets, kept);
+  p24_status s = launch_status();
+  if (s != P24_OK) return s;
+  // 2:4 along each tile's compacted axis; K bounds the widest tile
+  return launch_compress<G_VAR>(W, w_dtype, M, K, ldw, values, meta, P24_LAYOUT_DEVICE, kept, 128, K, st, offsets);
 }

@@ -50,7 +50,7 @@ constexpr int LDS_LIMIT = 160 * 1024;  // gfx950 LDS per workgroup
 // How the X operand arrives: K x N row-major (N contiguous, transposed on the
 // LDS read), the same with a TVW row gather, or N x K row-major (X^T, K
 // contiguous: the operand order of the MFMA, read with plain 16-byte loads).
-enum XMode { X_KN = 0, X_KN_GATHER = 1, X_NK = 2 };
+enum XMode { X_KN = 0, X_KN_GATHER = 1, X_NK = 2, X_KN_GATHER_VAR = 3 };
 
 // How the W operand arrives and is multiplied: packed dense bf16 on dense MFMA;
 // compressed 2:4 values + metadata on the sparse MFMA (smfmac); or the same
@@ -168,7 +168,9 @@ template <> __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, flo
 struct GemmArgs {
   const uint16_t* A;       // sparse: device-layout values; dense: packed W
   const uint32_t* Ameta;   // sparse: device-layout metadata
-  const int32_t* kept;     // TVW: [T][Kc] gathered X rows (nullptr otherwise)
+  const int32_t* kept;     // TVW: [T][Kc] gathered X rows (nullptr otherwise); per-tile keep: all tiles' lists
+  const int64_t* offsets;  // per-tile keep: [T + 1] first kept column of each tile in the concatenated storage
+  const int32_t* order;    // per-tile keep: tile of each block-row slot (heaviest first)
   const uint16_t* X;
   void* Y;
   int64_t ldx, ldy;
@@ -221,7 +223,9 @@ template <int BM, int BN, int WGM, int WGN, int AM, int XM, typename OutT, int E
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   using C = TileCfg<BM, BN, WGM, WGN, AM>;
   constexpr bool SPARSE = C::SPARSE, SMFMAC = AM == A_SPARSE, DECOMP = AM == A_DECOMP;
-  constexpr bool GATHER = XM == X_KN_GATHER;
+  constexpr bool VAR = XM == X_KN_GATHER_VAR;
+  constexpr bool GATHER = XM == X_KN_GATHER || VAR;
+  static_assert(!VAR || BM == 128, "per-tile keep: one block row per 128-row tile");
   constexpr bool XT = XM == X_NK;
   constexpr int TM = C::TM, TN = C::TN, ASTEPS = C::ASTEPS, NSTAGE = C::NSTAGE;
   static_assert(!DECOMP || XM == X_KN, "the expanded-tile path reads X as K x N");
@@ -231,21 +235,48 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
 
-  // ---- block -> output tile (XCD-aware, grouped raster) ----
-  const uint32_t nblocks = (uint32_t)args.nbm * args.nbn;
-  const uint32_t b = xcd_remap(blockIdx.x, nblocks);
-  constexpr uint32_t GROUP = 8;
-  const uint32_t group_size = GROUP * args.nbn;
-  const uint32_t first_m = (b / group_size) * GROUP;
-  const uint32_t gsz = min((uint32_t)args.nbm - first_m, GROUP);
-  const int bm = first_m + (b % group_size) % gsz;
-  const int bn = (b % group_size) / gsz;
+  // ---- block -> output tile ----
+  int bm, bn;
+  if constexpr (VAR) {
+    // Per-tile keep counts: block-row slots in the order the host gives
+    // (heaviest tile first, so the light ones fill the tail), the N blocks of
+    // one slot back to back: the 8 XCDs, which take consecutive blocks in
+    // turn, work through the slots together and each keeps to the same
+    // eighth of the X column slices.
+    const int slot = (int)(blockIdx.x / (uint32_t)args.nbn);
+    bn = (int)(blockIdx.x % (uint32_t)args.nbn);
+    bm = args.order[slot];
+  } else {
+    // XCD-aware, grouped raster
+    const uint32_t nblocks = (uint32_t)args.nbm * args.nbn;
+    const uint32_t b = xcd_remap(blockIdx.x, nblocks);
+    constexpr uint32_t GROUP = 8;
+    const uint32_t group_size = GROUP * args.nbn;
+    const uint32_t first_m = (b / group_size) * GROUP;
+    const uint32_t gsz = min((uint32_t)args.nbm - first_m, GROUP);
+    bm = first_m + (b % group_size) % gsz;
+    bn = (b % group_size) / gsz;
+  }
   const int m0 = bm * BM, n0 = bn * BN;
 
-  const int M = args.M, N = args.N, Kc = args.Kc;
+  const int M = args.M, N = args.N;
+  // The W operand of this block: with per-tile keep counts the tile's own
+  // storage (128 rows, its own compacted K), else the whole matrix.
+  const uint16_t* A = args.A;
+  const uint32_t* Ameta = args.Ameta;
+  int Kc = args.Kc, a_rows = M, a_m0 = m0;
+  int64_t var_p = 0;
+  if constexpr (VAR) {
+    var_p = args.offsets[bm];
+    Kc = (int)(args.offsets[bm + 1] - var_p);
+    A += var_p * 64;              // 128 rows x Kc/2 values per tile
+    Ameta += var_p * 4;           // 16 B of metadata per kept column
+    a_rows = M - m0 < BM ? M - m0 : BM;
+    a_m0 = 0;
+  }
   const int nk = Kc / BK;
-  const int nrb = (M + 31) / 32;
-  const int rb0 = m0 / 32;
+  const int nrb = (a_rows + 31) / 32;
+  const int rb0 = a_m0 / 32;
   const int64_t S = SPARSE ? Kc / 32 : Kc / 16;    // A blocks per row block
   const int64_t T_ = Kc / 64;
   const int n_hi = ((N + 7) & ~7) - 8;             // last 8-aligned column start inside the readable row
@@ -297,12 +328,12 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   const bool meta_wave = wave < C::MG;
   const int rb_end = nrb < rb0 + C::RB ? nrb : rb0 + C::RB;
   const __amdgpu_buffer_rsrc_t a_rsrc =
-      make_rsrc(args.A + (int64_t)rb0 * S * 512, (uint32_t)((rb_end - rb0) * S * 1024));
-  const int ngroups = (int)(device_row_blocks(M) / 4);       // metadata groups in the array
+      make_rsrc(A + (int64_t)rb0 * S * 512, (uint32_t)((rb_end - rb0) * S * 1024));
+  const int ngroups = (int)(device_row_blocks(a_rows) / 4);  // metadata groups in the array
   const int g0 = rb0 / 4;
   const int g_end = ngroups < g0 + C::MG ? ngroups : g0 + C::MG;
   const __amdgpu_buffer_rsrc_t m_rsrc =
-      SPARSE ? make_rsrc(args.Ameta + (int64_t)g0 * T_ * 256, (uint32_t)((g_end - g0) * T_ * 1024)) : a_rsrc;
+      SPARSE ? make_rsrc(Ameta + (int64_t)g0 * T_ * 256, (uint32_t)((g_end - g0) * T_ * 1024)) : a_rsrc;
   const int m_in_group = C::RB < 4 ? (rb0 & 3) : 0;         // a 64-row block's row blocks inside its group
   const int n_rows = N - n0 < BN ? N - n0 : BN;
   const __amdgpu_buffer_rsrc_t xt_rsrc =
@@ -311,7 +342,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   const __amdgpu_buffer_rsrc_t xg_rsrc = make_rsrc(args.X, (uint32_t)(GATHER ? (int64_t)args.Kx * ldx * 2 : 0));
 
   const int32_t* kept_tile = nullptr;
-  if constexpr (GATHER) kept_tile = args.kept + (int64_t)(m0 / args.tile_m) * Kc;
+  if constexpr (VAR) kept_tile = args.kept + var_p;
+  else if constexpr (GATHER) kept_tile = args.kept + (int64_t)(m0 / args.tile_m) * Kc;
   // TVW: the gathered X rows of step g are read one step before their loads
   // are issued (and are issued before them), so waiting for the indices never
   // waits for a tile in flight.
@@ -836,6 +868,7 @@ static p24_status check_xy(const void* X, int64_t ldx, int64_t N, const void* Y,
                            int64_t ldy) {
   if (y_dtype != P24_F32 && y_dtype != P24_BF16) return P24_ERR_DTYPE;
   if (N < 0 || ldx < N || ldy < N || N > INT32_MAX) return P24_ERR_SHAPE;
+  if (N > 0 && (uint64_t)ldx * 2 * 64 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;   // one K step's rows in a 32-bit range
   (void)X;
   (void)Y;
   return P24_OK;
@@ -896,6 +929,7 @@ extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, 
     return P24_ERR_SHAPE;
   if (tile_m % 128 || keep_k % 64) return P24_ERR_UNSUPPORTED;
   if (M == 0 || N == 0) return P24_OK;
+  if ((uint64_t)K * ldx * 2 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;   // gathered rows: all of X in a 32-bit range
   if (!kept || !values || !meta) return P24_ERR_NULL;
   if (!aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4)) return P24_ERR_ALIGN;
   s = check_xy_ptrs(X, ldx, Y, y_dtype);
@@ -915,6 +949,40 @@ extern "C" P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, 
   a.tile_m = (int)tile_m;
   // one block row = one 128-row slice of a TVW tile; 8 waves (2 x 4, each 64 x 64)
   return launch_cfg<128, 256, 2, 4, A_SPARSE, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status spmm_tvw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                                           const void* values, const void* meta, int64_t M, int64_t K,
+                                           const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
+                                           int64_t ldy, void* stream) {
+  p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
+  if (s != P24_OK) return s;
+  if (M < 0 || K <= 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return P24_OK;
+  if ((uint64_t)K * ldx * 2 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;   // gathered rows: all of X in a 32-bit range
+  if (!offsets || !order || !kept || !values || !meta) return P24_ERR_NULL;
+  if (!aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4) || !aligned(offsets, 8) ||
+      !aligned(order, 4))
+    return P24_ERR_ALIGN;
+  s = check_xy_ptrs(X, ldx, Y, y_dtype);
+  if (s != P24_OK) return s;
+  GemmArgs a{};
+  a.A = (const uint16_t*)values;
+  a.Ameta = (const uint32_t*)meta;
+  a.kept = kept;
+  a.offsets = offsets;
+  a.order = order;
+  a.X = (const uint16_t*)X;
+  a.Y = Y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.Kc = 0;            // per tile, from the offsets
+  a.Kx = (int)K;
+  a.tile_m = 128;
+  return launch_cfg<128, 256, 2, 4, A_SPARSE, X_KN_GATHER_VAR>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,

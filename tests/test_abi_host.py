@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 17
+    assert len(syms) == len(set(syms)) == 20
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -130,6 +130,45 @@ def test_tvw_validation(L):
     g = L.spmm_tvw
     assert g(FAKE, FAKE, FAKE, 1, 256, 256, 64, 128, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_UNSUPPORTED
     assert g(FAKE, FAKE, FAKE, 0, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_LAYOUT
+
+
+def test_tvw_var_validation(L):
+    # T = ceil(M / 128) tiles: scores (T*K fp64, 256 B rounded) + selection state + 2 counts per tile
+    assert L.tvw_var_workspace_bytes(4096, 4096) == 32 * 4096 * 8 + 1280 + 2 * 32 * 4
+    assert L.tvw_var_workspace_bytes(300, 64) == 3 * 64 * 8 + 1280 + 2 * 3 * 4   # 1536 B of scores
+    f = L.tvw_var_compress
+    base = dict(W=FAKE, wd=0, M=256, K=256, ldw=256, total=256, off=FAKE, order=FAKE, kept=FAKE, v=FAKE, m=FAKE,
+                ws=FAKE, wsb=1 << 30)
+    def call(**k):
+        a = {**base, **k}
+        return f(a["W"], a["wd"], a["M"], a["K"], a["ldw"], a["total"], a["off"], a["order"], a["kept"], a["v"],
+                 a["m"], a["ws"], a["wsb"], NUL)
+    assert call(wd=1) == p24.P24_ERR_DTYPE
+    assert call(K=160, ldw=160) == p24.P24_ERR_UNSUPPORTED           # K % 64
+    assert call(ldw=128) == p24.P24_ERR_SHAPE
+    assert call(total=0) == p24.P24_ERR_SHAPE
+    assert call(total=2 * 256 + 1) == p24.P24_ERR_SHAPE               # more than T*K
+    assert call(off=NUL) == p24.P24_ERR_NULL
+    assert call(order=NUL) == p24.P24_ERR_NULL
+    assert call(wsb=16) == p24.P24_ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 64)) == p24.P24_ERR_ALIGN   # workspace 256 B aligned
+    assert call(off=ctypes.c_void_p((1 << 20) + 4)) == p24.P24_ERR_ALIGN
+    assert call(M=0, W=NUL, off=NUL, order=NUL, kept=NUL, v=NUL, m=NUL, ws=NUL) == p24.P24_OK
+    g = L.spmm_tvw_var
+    gargs = lambda **k: [k.get("off", FAKE), k.get("order", FAKE), k.get("kept", FAKE), k.get("v", FAKE),
+                         k.get("m", FAKE), k.get("M", 256), k.get("K", 256), k.get("X", FAKE), k.get("ldx", 64),
+                         k.get("N", 64), k.get("Y", FAKE), k.get("yd", 0), k.get("ldy", 64), NUL]
+    assert g(*gargs(K=96)) == p24.P24_ERR_UNSUPPORTED
+    assert g(*gargs(order=NUL)) == p24.P24_ERR_NULL
+    assert g(*gargs(off=ctypes.c_void_p((1 << 20) + 4))) == p24.P24_ERR_ALIGN
+    assert g(*gargs(yd=5)) == p24.P24_ERR_DTYPE
+    assert g(*gargs(M=0, off=NUL, order=NUL, kept=NUL, v=NUL, m=NUL, X=NUL, Y=NUL)) == p24.P24_OK
+    # X addressed with 32 bits: 2 * K * ldx < 2^32
+    assert g(*gargs(K=65536, ldx=32768, N=64)) == p24.P24_ERR_UNSUPPORTED
+    assert L.spmm_tvw(FAKE, FAKE, FAKE, 1, 256, 65536, 128, 128, FAKE, 32768, 64, FAKE, 0, 64, NUL) \
+        == p24.P24_ERR_UNSUPPORTED
+    # one K step of X rows: 128 * ldx < 2^32
+    assert L.spmm24(FAKE, FAKE, 1, 64, 128, FAKE, 1 << 25, 64, FAKE, 0, 64, 0, NUL) == p24.P24_ERR_UNSUPPORTED
 
 
 def test_dense_validation(L):

@@ -36,7 +36,8 @@ class Workload:
     x_dist: str            # "normal" or "halfnormal"
     out_dtype: str         # "f32" or "bf16"
     tile_m: int = 0        # TVW tile rows (0: plain 2:4)
-    keep_k: int = 0        # TVW kept columns per tile
+    keep_k: int = 0        # TVW kept columns per tile (with per-tile keep counts: the average)
+    tile_spread: float = 0.0   # per-tile keep counts: row scale of tile t is 1 + tile_spread * U(-1, 1)
 
     @property
     def dense_flops(self) -> float:
@@ -48,6 +49,11 @@ class Workload:
         """Flops the sparse method actually performs (kept multiply-adds x 2)."""
         k_eff = self.keep_k if self.tile_m else self.K
         return 2.0 * self.M * self.N * (k_eff // 2)
+
+    @property
+    def total_keep(self) -> int:
+        """Per-tile keep counts: columns kept over all tiles (keep_k per tile on average)."""
+        return -(-self.M // self.tile_m) * self.keep_k
 
 
 WORKLOADS = {
@@ -62,7 +68,12 @@ WORKLOADS = {
                    "normal", "bf16"),
     "c5": Workload("c5", "TVW 4096x4096 . 4096x4096, tile 128 rows, keep 2048 columns", 4096, 4096,
                    4096, 0.02, "normal", "bf16", tile_m=128, keep_k=2048),
+    "c5v": Workload("c5v", "TVW with per-tile keep counts 4096x4096 . 4096x4096, tile 128 rows, "
+                           "2048 columns per tile on average", 4096, 4096, 4096, 0.02, "normal", "bf16",
+                    tile_m=128, keep_k=2048, tile_spread=0.1),
 }
+
+TILE_SCALE_SEED = 2
 
 
 def weights(wl: Workload, seed: int = W_SEED, rows: int | None = None) -> np.ndarray:
@@ -70,7 +81,17 @@ def weights(wl: Workload, seed: int = W_SEED, rows: int | None = None) -> np.nda
     rng = np.random.default_rng(seed)
     m = wl.M if rows is None else rows
     w = rng.standard_normal((m, wl.K), dtype=np.float32)
-    return (w * np.float32(wl.w_sigma)).astype(np.float32)
+    w = (w * np.float32(wl.w_sigma)).astype(np.float32)
+    if wl.tile_spread:
+        w *= tile_scales(wl)[np.arange(m) // wl.tile_m][:, None]
+    return w
+
+
+def tile_scales(wl: Workload) -> np.ndarray:
+    """fp32 row scale per tile: 1 + tile_spread * U(-1, 1), so that tiles differ in importance."""
+    T = -(-wl.M // wl.tile_m)
+    u = np.random.default_rng(TILE_SCALE_SEED).uniform(-1.0, 1.0, T)
+    return (1.0 + wl.tile_spread * u).astype(np.float32)
 
 
 def truncate_to_bf16_bits(x: np.ndarray) -> np.ndarray:
