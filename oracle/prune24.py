@@ -400,6 +400,65 @@ def tvw_var_decompress(tiles, M: int, K: int, tile_m: int) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# TW alone ("Accelerating Sparse DNNs Based on Tiled GEMM", Abstract and
+# Figure 3: the tile-level column drop without the 2:4 step inside the tile).
+# The kept columns are chosen exactly as for TVW (fixed keep_k per tile, or the
+# per-tile counts of tvw_var_counts) and multiplied densely: each tile's rows
+# restricted to its kept columns, rounded to bf16 (nearest even).
+# Dense device layout (the dense MFMA's A operand order): blocks of 32 rows
+# (padding rows zero) and 16 columns; block (rb, s) is 64 lanes x 8 bf16, lane
+# L's 8 values are W[32 rb + L % 32][16 s + 8 (L // 32) .. +8]; rb-major.
+# ----------------------------------------------------------------------------
+def dense_device_layout(Wbits: np.ndarray, rows: int) -> np.ndarray:
+    """bf16 bits [R, K] (R <= rows, rows % 32 == 0, K % 16 == 0) -> flat u16 in the dense device layout."""
+    Wbits = np.asarray(Wbits, dtype=np.uint16)
+    R, K = Wbits.shape
+    if rows % 32 or K % 16 or R > rows:
+        raise ValueError("rows must be a multiple of 32 covering W, K a multiple of 16")
+    pad = np.zeros((rows, K), dtype=np.uint16)
+    pad[:R] = Wbits
+    # row = 32 rb + r, column = 16 s + 8 h + i  ->  [rb, s, L = 32 h + r, i]
+    return pad.reshape(rows // 32, 32, K // 16, 2, 8).transpose(0, 2, 3, 1, 4).reshape(-1).copy()
+
+
+def tw_compress(W: np.ndarray, tile_m: int, keep_k: int):
+    """(kept int32 [T, keep_k], Wc bf16 bits [M, keep_k]): tile t's rows on its kept columns."""
+    W = np.asarray(W, dtype=np.float32)
+    kept = tvw_select(W, tile_m, keep_k)
+    Wc = np.zeros((W.shape[0], keep_k), dtype=np.uint16)
+    for t in range(kept.shape[0]):
+        r0, r1 = t * tile_m, min(W.shape[0], (t + 1) * tile_m)
+        Wc[r0:r1] = bf16_rne(W[r0:r1][:, kept[t]])
+    return kept, Wc
+
+
+def tw_var_compress(W: np.ndarray, tile_m: int, counts):
+    """Per tile (kept int32 [c_t] ascending, Wc bf16 bits [rows_t, c_t])."""
+    W = np.asarray(W, dtype=np.float32)
+    out = []
+    for t, (kept, _, _) in enumerate(tvw_var_compress(W, tile_m, counts)):
+        r0, r1 = t * tile_m, min(W.shape[0], (t + 1) * tile_m)
+        out.append((kept, bf16_rne(W[r0:r1][:, kept])))
+    return out
+
+
+def tw_var_device(tiles, counts):
+    """(kept flat int32, dense device values flat u16): each tile's 128-row dense layout in tile order."""
+    kept = np.concatenate([k for k, _ in tiles]).astype(np.int32)
+    dv = np.concatenate([dense_device_layout(w, 128) for _, w in tiles])
+    return kept, dv
+
+
+def tw_decompress(kept_list, Wc_list, M: int, K: int, tile_m: int) -> np.ndarray:
+    """Dense bf16 bits [M, K] with every tile's columns scattered back (dropped columns zero)."""
+    out = np.zeros((M, K), dtype=np.uint16)
+    for t, (kept, Wc) in enumerate(zip(kept_list, Wc_list)):
+        r0, r1 = t * tile_m, min(M, (t + 1) * tile_m)
+        out[r0:r1][:, kept] = Wc[: r1 - r0]
+    return out
+
+
+# ----------------------------------------------------------------------------
 # GEMM reference and bound (fp64; every bf16 x bf16 product is exact in fp64)
 # ----------------------------------------------------------------------------
 def gemm_ref(Wd: np.ndarray, X: np.ndarray, rows=None):
