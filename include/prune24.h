@@ -283,6 +283,36 @@ P24_API p24_status spmm_tvw_var(const int64_t* offsets, const int32_t* order, co
                                 int64_t ldy, void* stream);
 
 /*
+ * TW alone -- the tile column drop without the 2:4 step ("Accelerating Sparse
+ * DNNs Based on Tiled GEMM", Abstract, Figure 3); the kept columns are
+ * multiplied with the dense MFMA.
+ * tw_compress -- the kept lists exactly as tvw_compress chooses them
+ *   (tile_m % 32 == 0, keep_k % 64 == 0, W fp32 as there, workspace
+ *   tvw_workspace_bytes(...)), and Wp: the M x keep_k matrix of tile rows on
+ *   their kept columns, bf16 (round to nearest even), in the dense operand
+ *   order of gemm_bf16_pack (gemm_bf16_packed_bytes(M, keep_k) bytes, 16 B aligned).
+ * spmm_tw -- Y = W X with Y[m][n] = sum_j Wc[m][j] X[kept[t][j]][n];
+ *   tile_m % 128 == 0; other rules of spmm_tvw.
+ * tw_var_compress -- per-tile keep counts, offsets, order and kept lists
+ *   exactly as tvw_var_compress; Wp (capacity T*K*256 bytes, 16 B aligned)
+ *   holds tile t's 128 x c_t dense operand (rows past M zero) from element
+ *   128*offsets[t].  Workspace tvw_var_workspace_bytes(M, K).
+ * spmm_tw_var -- Y = W X for that storage; block rows run in `order`.
+ */
+P24_API p24_status tw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                               int64_t tile_m, int64_t keep_k, int32_t* kept, void* Wp, void* workspace,
+                               size_t ws_bytes, void* stream);
+P24_API p24_status spmm_tw(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,
+                           int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
+                           int32_t y_dtype, int64_t ldy, void* stream);
+P24_API p24_status tw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                   int64_t total_keep, int64_t* offsets, int32_t* order, int32_t* kept,
+                                   void* Wp, void* workspace, size_t ws_bytes, void* stream);
+P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                               const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
+                               int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream);
+
+/*
  * Dense bf16 GEMM, the denominator of every speedup ("over the dense model",
  * "Accelerating Sparse DNNs Based on Tiled GEMM", Abstract).  It runs the same
  * tile loop as spmm24 with the dense MFMA v_mfma_f32_32x32x16_bf16.

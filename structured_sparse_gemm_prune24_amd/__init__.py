@@ -62,6 +62,14 @@ _SIGNATURES = {
                                   _c_vp, _c_vp, _c_size, _c_vp]),
     "spmm_tvw_var": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp,
                               _c_i32, _c_i64, _c_vp]),
+    "tw_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_size,
+                             _c_vp]),
+    "spmm_tw": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i64,
+                         _c_vp]),
+    "tw_var_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_vp,
+                                 _c_size, _c_vp]),
+    "spmm_tw_var": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
+                             _c_i64, _c_vp]),
     "spmm24_xt": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                            _c_i64, _c_vp]),
     "spmm24_fused": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_vp,
@@ -192,6 +200,29 @@ class CompressedTVWVar:
     kept: object         # torch.int32, capacity T*K
     values: object       # torch.bfloat16, capacity T*K*64
     meta: object         # torch.int32, capacity T*K*4
+    M: int
+    K: int
+    total_keep: int
+
+
+@dataclass
+class CompressedTW:
+    """TW (tile column drop, no 2:4): kept lists per tile + the dense bf16 operand of the kept columns."""
+    kept: object         # torch.int32 [T, keep_k]
+    Wp: object           # torch.bfloat16, dense operand order
+    M: int
+    K: int
+    tile_m: int
+    keep_k: int
+
+
+@dataclass
+class CompressedTWVar:
+    """TW with a keep count per 128-row tile (storage as CompressedTVWVar, dense per tile)."""
+    offsets: object      # torch.int64 [T + 1]
+    order: object        # torch.int32 [T]
+    kept: object         # torch.int32, capacity T*K
+    Wp: object           # torch.bfloat16, capacity T*K*128
     M: int
     K: int
     total_keep: int
@@ -364,6 +395,78 @@ def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None):
     _check(lib().spmm_tvw_var(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.M,
                               t.K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)),
            "spmm_tvw_var")
+    return out
+
+
+def _x_out(X, K, M, out_dtype, out):
+    torch = _torch()
+    _require_cuda(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise ValueError("X must be bfloat16")
+    ldx = _rowmajor(X, "X")
+    if X.shape[0] != K:
+        raise ValueError(f"X has {X.shape[0]} rows, W has K = {K}")
+    if out is None:
+        out = torch.empty((M, X.shape[1]), dtype=out_dtype or torch.bfloat16, device=X.device)
+    return ldx, X.shape[1], out, _rowmajor(out, "out")
+
+
+def tw_compress(W, tile_m: int = 128, keep_k: int | None = None) -> CompressedTW:
+    """TW: per tile_m-row tile keep keep_k columns by L1 norm; the kept columns stay dense (bf16)."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("tw_compress takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    keep_k = K // 2 if keep_k is None else int(keep_k)
+    L = lib()
+    T = (M + tile_m - 1) // tile_m
+    kept = torch.empty((T, keep_k), dtype=torch.int32, device=W.device)
+    Wp = torch.empty(max(L.gemm_bf16_packed_bytes(M, keep_k) // 2, 1), dtype=torch.bfloat16, device=W.device)
+    wsb = L.tvw_workspace_bytes(M, K, tile_m, keep_k)
+    ws = torch.empty(max(wsb, 8), dtype=torch.uint8, device=W.device)
+    _check(L.tw_compress(_ptr(W), P24_F32, M, K, ldw, tile_m, keep_k, _ptr(kept), _ptr(Wp), _ptr(ws), ws.numel(),
+                         _stream(W.device)), "tw_compress")
+    return CompressedTW(kept, Wp, M, K, tile_m, keep_k)
+
+
+def spmm_tw(t: CompressedTW, X, out_dtype=None, out=None):
+    """Y = W X for a TW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
+    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    _check(lib().spmm_tw(_ptr(t.kept), _ptr(t.Wp), t.M, t.K, t.tile_m, t.keep_k, _ptr(X), ldx, N, _ptr(out),
+                         _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tw")
+    return out
+
+
+def tw_var_compress(W, total_keep: int | None = None) -> CompressedTWVar:
+    """TW with per-tile keep counts (the plan of tvw_var_compress), kept columns dense (bf16)."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("tw_var_compress takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    T = (M + 127) // 128
+    total_keep = T * K // 2 if total_keep is None else int(total_keep)
+    L = lib()
+    dev = W.device
+    cap = max(T * K, 1)
+    offsets = torch.empty(T + 1, dtype=torch.int64, device=dev)
+    order = torch.empty(max(T, 1), dtype=torch.int32, device=dev)
+    kept = torch.empty(cap, dtype=torch.int32, device=dev)
+    Wp = torch.empty(cap * 128, dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(L.tvw_var_workspace_bytes(M, K), 256), dtype=torch.uint8, device=dev)
+    _check(L.tw_var_compress(_ptr(W), P24_F32, M, K, ldw, total_keep, _ptr(offsets), _ptr(order), _ptr(kept),
+                             _ptr(Wp), _ptr(ws), ws.numel(), _stream(dev)), "tw_var_compress")
+    return CompressedTWVar(offsets, order, kept, Wp, M, K, total_keep)
+
+
+def spmm_tw_var(t: CompressedTWVar, X, out_dtype=None, out=None):
+    """Y = W X for a per-tile-keep TW matrix; X bf16 [K, N]."""
+    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    _check(lib().spmm_tw_var(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.Wp), t.M, t.K, _ptr(X), ldx, N,
+                             _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tw_var")
     return out
 
 

@@ -529,6 +529,53 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_order(const int64_t* __rest
   if (t < T) order[rank] = (int32_t)t;
 }
 
+// --------------------------------------------------------------------------
+// TW: a tile's rows on its kept columns, rounded to bf16, in the dense MFMA
+// operand order (block (rb, s) of 64 lanes x 8 values, lane L holding row
+// 32 rb + L % 32, columns 16 s + 8 (L / 32) .. +8).  One thread per (row, 8
+// consecutive kept columns): its 8 gathered reads walk one row in ascending
+// column order and its result is one 16 B store.  With one kept list per tile
+// (VAR false) the rows are padded to 32 and row m uses kept[m / tile_m][0 ..
+// Kc); with per-tile counts each 128-row tile is laid out on its own from
+// element 128 * offsets[t] and Kc is the widest tile (K).  Padding rows are zero.
+// --------------------------------------------------------------------------
+template <bool VAR>
+__global__ __launch_bounds__(256) void k_pack_tw(const float* __restrict__ W, int64_t ldw, int64_t M, int64_t K,
+                                                 int64_t Kc, const int32_t* __restrict__ kept,
+                                                 const int64_t* __restrict__ offsets, int64_t tile_m, int64_t rows,
+                                                 uint16_t* __restrict__ Wp) {
+  const int64_t C8 = Kc / 8;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= rows * C8) return;
+  const int64_t m = id / C8, j8 = id % C8;
+  int64_t kc = Kc, r = m;
+  const int32_t* kr;
+  uint16_t* out = Wp;
+  if constexpr (VAR) {
+    const int64_t t = m / 128, p = offsets[t];
+    kc = offsets[t + 1] - p;
+    if (8 * j8 >= kc) return;
+    kr = kept + p;
+    r = m % 128;
+    out += p * 128;               // 128 rows x kc bf16 per tile
+  } else {
+    kr = kept + (m < M ? m / tile_m : 0) * Kc;
+  }
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (m < M) {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      int64_t k = kr[8 * j8 + i];
+      k = k < 0 ? 0 : (k >= K ? K - 1 : k);
+      b[i] = f32_to_bf16_rne(__float_as_uint(W[m * ldw + k]));
+    }
+    v = u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+  }
+  const int64_t S = kc / 16, rb = r / 32, st = j8 / 2, L = 32 * (j8 % 2) + r % 32;
+  *reinterpret_cast<u32x4*>(out + ((rb * S + st) * 64 + L) * 8) = v;
+}
+
 }  // namespace p24
 
 // ============================================================================
@@ -688,22 +735,12 @@ extern "C" P24_API size_t tvw_var_workspace_bytes(int64_t M, int64_t K) {
   return scores + sel + 2 * (size_t)T_ * sizeof(int32_t);
 }
 
-extern "C" P24_API p24_status tvw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
-                                               int64_t total_keep, int64_t* offsets, int32_t* order,
-                                               int32_t* kept, void* values, void* meta, void* workspace,
-                                               size_t ws_bytes, void* stream) {
-  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
-  if (M < 0 || K <= 0 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
-  if (K % 64) return P24_ERR_UNSUPPORTED;
-  if (M == 0) return P24_OK;
+// Scores, the global cut, keep counts, offsets, order and the kept lists of
+// per-tile-keep TVW / TW (arguments already validated).
+static p24_status launch_var_plan(const void* W, int64_t M, int64_t K, int64_t ldw, int64_t total_keep,
+                                  int64_t* offsets, int32_t* order, int32_t* kept, void* workspace,
+                                  hipStream_t st) {
   const int64_t T_ = var_tiles(M);
-  if (T_ * K > INT32_MAX || total_keep <= 0 || total_keep > T_ * K) return P24_ERR_SHAPE;
-  if (!W || !offsets || !order || !kept || !values || !meta) return P24_ERR_NULL;
-  if (!workspace || ws_bytes < tvw_var_workspace_bytes(M, K)) return P24_ERR_WORKSPACE;
-  if (!aligned(W, 16) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4) ||
-      !aligned(offsets, 8) || !aligned(order, 4) || !aligned(workspace, 256))
-    return P24_ERR_ALIGN;
-  hipStream_t st = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
   double* scores = (double*)ws;
   ws += ((size_t)T_ * (size_t)K * sizeof(double) + 255) & ~(size_t)255;
@@ -728,8 +765,79 @@ extern "C" P24_API p24_status tvw_var_compress(const void* W, int32_t w_dtype, i
                      (const int64_t*)offsets, T_, order);
   hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
                      (int64_t)0, (const int64_t*)offsets, kept);
-  p24_status s = launch_status();
+  return launch_status();
+}
+
+static p24_status check_var_args(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                 int64_t total_keep, const void* offsets, const void* order, const void* kept,
+                                 const void* values, const void* meta, const void* workspace, size_t ws_bytes) {
+  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
+  if (M < 0 || K <= 0 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0) return P24_OK;
+  const int64_t T_ = var_tiles(M);
+  if (T_ * K > INT32_MAX || total_keep <= 0 || total_keep > T_ * K) return P24_ERR_SHAPE;
+  if (!W || !offsets || !order || !kept || !values || !meta) return P24_ERR_NULL;
+  if (!workspace || ws_bytes < tvw_var_workspace_bytes(M, K)) return P24_ERR_WORKSPACE;
+  if (!aligned(W, 16) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4) ||
+      !aligned(offsets, 8) || !aligned(order, 4) || !aligned(workspace, 256))
+    return P24_ERR_ALIGN;
+  return P24_OK;
+}
+
+extern "C" P24_API p24_status tvw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                               int64_t total_keep, int64_t* offsets, int32_t* order,
+                                               int32_t* kept, void* values, void* meta, void* workspace,
+                                               size_t ws_bytes, void* stream) {
+  p24_status s = check_var_args(W, w_dtype, M, K, ldw, total_keep, offsets, order, kept, values, meta, workspace,
+                                ws_bytes);
+  if (s != P24_OK || M == 0) return s;
+  hipStream_t st = (hipStream_t)stream;
+  s = launch_var_plan(W, M, K, ldw, total_keep, offsets, order, kept, workspace, st);
   if (s != P24_OK) return s;
   // 2:4 along each tile's compacted axis; K bounds the widest tile
   return launch_compress<G_VAR>(W, w_dtype, M, K, ldw, values, meta, P24_LAYOUT_DEVICE, kept, 128, K, st, offsets);
+}
+
+extern "C" P24_API p24_status tw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                          int64_t tile_m, int64_t keep_k, int32_t* kept, void* Wp,
+                                          void* workspace, size_t ws_bytes, void* stream) {
+  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
+  if (M < 0 || K <= 0 || ldw < K || tile_m <= 0 || tile_m % 32 || keep_k <= 0 || keep_k > K)
+    return P24_ERR_SHAPE;
+  if (M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (keep_k % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0) return P24_OK;
+  if (!W || !kept || !Wp) return P24_ERR_NULL;
+  if (!workspace || ws_bytes < tvw_workspace_bytes(M, K, tile_m, keep_k)) return P24_ERR_WORKSPACE;
+  if (!aligned(W, 16) || ldw % 4 || !aligned(Wp, 16) || !aligned(kept, 4) || !aligned(workspace, 8))
+    return P24_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t T_ = (M + tile_m - 1) / tile_m;
+  double* scores = (double*)workspace;
+  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
+                     tile_m, scores);
+  hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
+                     keep_k, (const int64_t*)nullptr, kept);
+  const int64_t rows = (M + 31) / 32 * 32;
+  hipLaunchKernelGGL(k_pack_tw<false>, dim3(grid1d(rows * (keep_k / 8), 256)), dim3(256), 0, st, (const float*)W,
+                     ldw, M, K, keep_k, (const int32_t*)kept, (const int64_t*)nullptr, tile_m, rows,
+                     (uint16_t*)Wp);
+  return launch_status();
+}
+
+extern "C" P24_API p24_status tw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                              int64_t total_keep, int64_t* offsets, int32_t* order,
+                                              int32_t* kept, void* Wp, void* workspace, size_t ws_bytes,
+                                              void* stream) {
+  p24_status s = check_var_args(W, w_dtype, M, K, ldw, total_keep, offsets, order, kept, Wp, Wp, workspace,
+                                ws_bytes);
+  if (s != P24_OK || M == 0) return s;
+  hipStream_t st = (hipStream_t)stream;
+  s = launch_var_plan(W, M, K, ldw, total_keep, offsets, order, kept, workspace, st);
+  if (s != P24_OK) return s;
+  const int64_t rows = var_tiles(M) * 128;
+  hipLaunchKernelGGL(k_pack_tw<true>, dim3(grid1d(rows * (K / 8), 256)), dim3(256), 0, st, (const float*)W, ldw,
+                     M, K, K, (const int32_t*)kept, (const int64_t*)offsets, (int64_t)128, rows, (uint16_t*)Wp);
+  return launch_status();
 }

@@ -269,8 +269,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   if constexpr (VAR) {
     var_p = args.offsets[bm];
     Kc = (int)(args.offsets[bm + 1] - var_p);
-    A += var_p * 64;              // 128 rows x Kc/2 values per tile
-    Ameta += var_p * 4;           // 16 B of metadata per kept column
+    A += var_p * (SPARSE ? 64 : 128);   // 128 rows x Kc/2 values (sparse) or Kc values (dense) per tile
+    Ameta += var_p * 4;                 // sparse: 16 B of metadata per kept column
     a_rows = M - m0 < BM ? M - m0 : BM;
     a_m0 = 0;
   }
@@ -983,6 +983,67 @@ extern "C" P24_API p24_status spmm_tvw_var(const int64_t* offsets, const int32_t
   a.Kx = (int)K;
   a.tile_m = 128;
   return launch_cfg<128, 256, 2, 4, A_SPARSE, X_KN_GATHER_VAR>(a, y_dtype, (hipStream_t)stream);
+}
+
+// TW alone: the dense MFMA on each tile's packed kept columns, X rows gathered
+// by the tile's kept list; one block row per 128-row slice, 8 waves (2 x 4).
+extern "C" P24_API p24_status spmm_tw(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,
+                                      int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
+                                      int32_t y_dtype, int64_t ldy, void* stream) {
+  p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
+  if (s != P24_OK) return s;
+  if (M < 0 || K <= 0 || tile_m <= 0 || keep_k <= 0 || keep_k > K || M > INT32_MAX || K > INT32_MAX)
+    return P24_ERR_SHAPE;
+  if (tile_m % 128 || keep_k % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return P24_OK;
+  if ((uint64_t)K * ldx * 2 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;   // gathered rows: all of X in a 32-bit range
+  if (!kept || !Wp) return P24_ERR_NULL;
+  if (!aligned(Wp, 16) || !aligned(kept, 4)) return P24_ERR_ALIGN;
+  s = check_xy_ptrs(X, ldx, Y, y_dtype);
+  if (s != P24_OK) return s;
+  GemmArgs a{};
+  a.A = (const uint16_t*)Wp;
+  a.kept = kept;
+  a.X = (const uint16_t*)X;
+  a.Y = Y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.Kc = (int)keep_k;
+  a.Kx = (int)K;
+  a.tile_m = (int)tile_m;
+  return launch_cfg<128, 256, 2, 4, A_DENSE, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                                          const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
+                                          int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream) {
+  p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
+  if (s != P24_OK) return s;
+  if (M < 0 || K <= 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || N == 0) return P24_OK;
+  if ((uint64_t)K * ldx * 2 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;
+  if (!offsets || !order || !kept || !Wp) return P24_ERR_NULL;
+  if (!aligned(Wp, 16) || !aligned(kept, 4) || !aligned(offsets, 8) || !aligned(order, 4)) return P24_ERR_ALIGN;
+  s = check_xy_ptrs(X, ldx, Y, y_dtype);
+  if (s != P24_OK) return s;
+  GemmArgs a{};
+  a.A = (const uint16_t*)Wp;
+  a.kept = kept;
+  a.offsets = offsets;
+  a.order = order;
+  a.X = (const uint16_t*)X;
+  a.Y = Y;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.M = (int)M;
+  a.N = (int)N;
+  a.Kc = 0;            // per tile, from the offsets
+  a.Kx = (int)K;
+  a.tile_m = 128;
+  return launch_cfg<128, 256, 2, 4, A_DENSE, X_KN_GATHER_VAR>(a, y_dtype, (hipStream_t)stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 20
+    assert len(syms) == len(set(syms)) == 24
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -169,6 +169,42 @@ def test_tvw_var_validation(L):
         == p24.P24_ERR_UNSUPPORTED
     # one K step of X rows: 128 * ldx < 2^32
     assert L.spmm24(FAKE, FAKE, 1, 64, 128, FAKE, 1 << 25, 64, FAKE, 0, 64, 0, NUL) == p24.P24_ERR_UNSUPPORTED
+
+
+def test_tw_validation(L):
+    f = L.tw_compress
+    base = dict(W=FAKE, wd=0, M=256, K=256, ldw=256, tile=128, keep=128, kept=FAKE, wp=FAKE, ws=FAKE, wsb=1 << 30)
+    def call(**k):
+        a = {**base, **k}
+        return f(a["W"], a["wd"], a["M"], a["K"], a["ldw"], a["tile"], a["keep"], a["kept"], a["wp"], a["ws"],
+                 a["wsb"], NUL)
+    assert call(wd=1) == p24.P24_ERR_DTYPE
+    assert call(tile=100) == p24.P24_ERR_SHAPE
+    assert call(keep=300) == p24.P24_ERR_SHAPE
+    assert call(keep=96) == p24.P24_ERR_UNSUPPORTED          # keep % 64
+    assert call(wsb=16) == p24.P24_ERR_WORKSPACE
+    assert call(wp=MISALIGNED) == p24.P24_ERR_ALIGN
+    assert call(kept=NUL) == p24.P24_ERR_NULL
+    assert call(M=0, W=NUL, kept=NUL, wp=NUL, ws=NUL) == p24.P24_OK
+    g = L.spmm_tw
+    gargs = lambda **k: [k.get("kept", FAKE), k.get("wp", FAKE), k.get("M", 256), k.get("K", 256),
+                         k.get("tile", 128), k.get("keep", 128), k.get("X", FAKE), k.get("ldx", 64),
+                         k.get("N", 64), k.get("Y", FAKE), k.get("yd", 0), k.get("ldy", 64), NUL]
+    assert g(*gargs(tile=64)) == p24.P24_ERR_UNSUPPORTED
+    assert g(*gargs(keep=96)) == p24.P24_ERR_UNSUPPORTED
+    assert g(*gargs(keep=512)) == p24.P24_ERR_SHAPE
+    assert g(*gargs(wp=NUL)) == p24.P24_ERR_NULL
+    assert g(*gargs(K=65536, ldx=32768)) == p24.P24_ERR_UNSUPPORTED
+    assert g(*gargs(M=0, kept=NUL, wp=NUL, X=NUL, Y=NUL)) == p24.P24_OK
+    h = L.tw_var_compress
+    assert h(FAKE, 0, 256, 160, 160, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert h(FAKE, 0, 256, 256, 256, 0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_SHAPE
+    assert h(FAKE, 0, 256, 256, 256, 100, FAKE, FAKE, FAKE, NUL, FAKE, 1 << 30, NUL) == p24.P24_ERR_NULL
+    assert h(FAKE, 0, 256, 256, 256, 100, FAKE, FAKE, FAKE, FAKE, FAKE, 64, NUL) == p24.P24_ERR_WORKSPACE
+    v = L.spmm_tw_var
+    assert v(FAKE, NUL, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_NULL
+    assert v(FAKE, FAKE, FAKE, FAKE, 256, 96, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert v(NUL, NUL, NUL, NUL, 0, 256, NUL, 64, 64, NUL, 0, 64, NUL) == p24.P24_OK
 
 
 def test_dense_validation(L):
