@@ -11,6 +11,8 @@ Beside the headline, the same run times (HIP events on the launch stream):
   - this project's dense bf16 GEMM of the unpruned W (the speedup denominator),
   - torch.matmul (hipBLASLt) of the same shapes, as context only,
   - the TVW workload (4096^3, tile 128, keep 2048): tvw_compress + spmm_tvw,
+  - TVW with per-tile keep counts (same shape and total of kept columns, tile
+    rows scaled 1 +- 0.1): tvw_var_compress + spmm_tvw_var,
 and the CPU oracle on a bounded sample of the headline workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
@@ -20,6 +22,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -39,6 +42,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workloads", default=None, help="--table: comma-separated workload keys (default all)")
     ap.add_argument("--only", choices=["spmm", "xt", "decomp", "dense", "compress", "tvw", "copy"], default=None)
     ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
     ap.add_argument("--table", action="store_true",
@@ -173,7 +177,9 @@ def table(args):
         calls = [fns[i % len(fns)] for i in range(max(args.steps, 2 * len(fns)))]
         return graph_time_us(torch, lambda: [f() for f in calls], reps=1) / len(calls)
 
-    for key, wl in workloads.WORKLOADS.items():
+    keys = args.workloads.split(",") if args.workloads else list(workloads.WORKLOADS)
+    for key in keys:
+        wl = workloads.WORKLOADS[key]
         W = torch.from_numpy(workloads.weights(wl)).to(dev)
         Xb = workloads.activations(wl)
         X = to_bf16(Xb)
@@ -186,12 +192,39 @@ def table(args):
         set_bytes = (prune24_bytes(wl) + wl.K * wl.N * 2 + wl.M * wl.N * Y.element_size())
         nsets = int(min(32, max(2, -(-COLD_BYTES // set_bytes))))
         rec["cold_sets"] = nsets
-        if wl.tile_m:
+        kept_flops = wl.kept_flops
+        if wl.tile_spread:
+            # per-tile keep counts; beside the batched (heaviest-first) block order,
+            # the same storage run in plain tile order
+            t = p24.tvw_var_compress(W, total_keep=wl.total_keep)
+            counts = np.diff(t.offsets.cpu().numpy())
+            rows_t = np.minimum(wl.tile_m, wl.M - wl.tile_m * np.arange(len(counts)))
+            kept_flops = float(2 * wl.N * np.sum(rows_t * (counts // 2)))
+            rec["keep_min"], rec["keep_max"], rec["keep_mean"] = int(counts.min()), int(counts.max()), float(counts.mean())
+            rec["spmm_tvw_var_us"] = timeit(lambda: p24.spmm_tvw_var(t, X, out=Y))
+            tn = dataclasses.replace(t, order=torch.arange(len(counts), dtype=torch.int32, device=dev))
+            rec["spmm_tvw_var_tile_order_us"] = timeit(lambda: p24.spmm_tvw_var(tn, X, out=Y))
+            sets = [(p24.tvw_var_compress(W, total_keep=wl.total_keep), X.clone(), torch.empty_like(Y))
+                    for _ in range(nsets)]
+            rec["spmm_tvw_var_cold_us"] = timeit_rot(
+                [lambda s=s_: p24.spmm_tvw_var(s[0], s[1], out=s[2]) for s_ in sets])
+            del sets
+            ev = event_times_ms(torch, lambda: p24.tvw_var_compress(W, total_keep=wl.total_keep), 5)
+            rec["tvw_var_compress_us"] = sum(ev) / len(ev) * 1e3
+            # TW alone on the same plan (kept columns dense, dense MFMA)
+            tw = p24.tw_var_compress(W, total_keep=wl.total_keep)
+            rec["spmm_tw_var_us"] = timeit(lambda: p24.spmm_tw_var(tw, X, out=Y))
+            del tw
+            sparse_us = rec["spmm_tvw_var_us"]
+        elif wl.tile_m:
             t = p24.tvw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
             rec["spmm_tvw_us"] = timeit(lambda: p24.spmm_tvw(t, X, out=Y))
             sets = [(p24.tvw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k), X.clone(), torch.empty_like(Y))
                     for _ in range(nsets)]
             rec["spmm_tvw_cold_us"] = timeit_rot([lambda s=s_: p24.spmm_tvw(s[0], s[1], out=s[2]) for s_ in sets])
+            tw = p24.tw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
+            rec["spmm_tw_us"] = timeit(lambda: p24.spmm_tw(tw, X, out=Y))
+            del tw
             sparse_us = rec["spmm_tvw_us"]
             del sets
         else:
@@ -222,9 +255,9 @@ def table(args):
         bytes_alg = prune24_bytes(wl) + wl.K * wl.N * 2 + wl.M * wl.N * (2 if wl.out_dtype == "bf16" else 4)
         rec["algorithmic_bytes"] = bytes_alg
         rec["hbm_frac"] = bytes_alg / (sparse_us * 1e-6) / (PEAK_HBM_GBS * 1e9)
-        cold_us = rec.get("spmm24_cold_us", rec.get("spmm_tvw_cold_us"))
+        cold_us = rec.get("spmm24_cold_us", rec.get("spmm_tvw_cold_us", rec.get("spmm_tvw_var_cold_us")))
         rec["hbm_frac_cold"] = bytes_alg / (cold_us * 1e-6) / (PEAK_HBM_GBS * 1e9)
-        rec["mfma_frac"] = wl.kept_flops / (sparse_us * 1e-6) / (PEAK_BF16_MFMA_TFLOPS * 1e12)
+        rec["mfma_frac"] = kept_flops / (sparse_us * 1e-6) / (PEAK_BF16_MFMA_TFLOPS * 1e12)
         print(json.dumps({k: (round(v, 4) if isinstance(v, float) else v) for k, v in rec.items()}), flush=True)
         del W, X, XT, Y, Wp
         torch.cuda.empty_cache()
@@ -380,6 +413,19 @@ def main():
         rows["spmm_tvw_c5_dense_eq_tflops"] = wt.dense_flops / (rows["spmm_tvw_c5_us_mean"] * 1e-6) / 1e12
         ev5c = event_times_ms(torch, lambda: p24.tvw_compress(W5, tile_m=wt.tile_m, keep_k=wt.keep_k), 3)
         rows["tvw_compress_c5_us_mean"] = sum(ev5c) / len(ev5c) * 1e3
+        # per-tile keep counts (same total of kept columns, tiles of different importance)
+        wv = workloads.WORKLOADS["c5v"]
+        W5v = torch.from_numpy(workloads.weights(wv)).to(dev)
+        t5v = p24.tvw_var_compress(W5v, total_keep=wv.total_keep)
+        vstep = lambda: p24.spmm_tvw_var(t5v, X5, out=Y5)
+        for _ in range(args.warmup):
+            vstep()
+        ev5v = event_times_ms(torch, vstep, max(args.steps, 5))
+        rows["spmm_tvw_var_c5v_us_mean"] = sum(ev5v) / len(ev5v) * 1e3
+        rows["spmm_tvw_var_c5v_dense_eq_tflops"] = wv.dense_flops / (rows["spmm_tvw_var_c5v_us_mean"] * 1e-6) / 1e12
+        ev5vc = event_times_ms(torch, lambda: p24.tvw_var_compress(W5v, total_keep=wv.total_keep), 3)
+        rows["tvw_var_compress_c5v_us_mean"] = sum(ev5vc) / len(ev5vc) * 1e3
+        del W5v, t5v
         if args.only == "tvw":
             print(json.dumps(rows))
             return
