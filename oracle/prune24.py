@@ -262,6 +262,37 @@ def from_device_layout(dvals: np.ndarray, dmeta: np.ndarray, M: int, K: int):
 
 
 # ----------------------------------------------------------------------------
+# Masked fine-tuning ("Accelerating Sparse Deep Neural Networks", Abstract: the
+# trained network is pruned to the 2:4 pattern and then retrained with it).
+# Between re-prunes the master weights keep the stored pattern: every entry
+# the metadata does not select is set to +0 after each update, kept entries
+# are left bit for bit.  A re-prune is selection + compression of the current
+# weights with the same zeroing, i.e. (prune_24(W), compress_24(W)).
+# ----------------------------------------------------------------------------
+def mask_from_meta(meta: np.ndarray, K: int) -> np.ndarray:
+    """bool [M, K]: True at the two stored positions of every group of four."""
+    pos = meta_positions(meta, K)                     # [M, K/2], positions in group order
+    M = pos.shape[0]
+    mask = np.zeros((M, K // 4, 4), dtype=bool)
+    np.put_along_axis(mask, pos.reshape(M, K // 4, 2), True, axis=-1)
+    return mask.reshape(M, K)
+
+
+def mask_apply(W: np.ndarray, meta: np.ndarray, dtype: str = "f32") -> np.ndarray:
+    """W (fp32, or bf16 bits) with every entry outside the stored positions set to +0."""
+    W = np.asarray(W)
+    bits = W.view(np.uint32) if dtype == "f32" else np.asarray(W, dtype=np.uint16)
+    out = np.where(mask_from_meta(meta, W.shape[1]), bits, bits.dtype.type(0)).astype(bits.dtype)
+    return out.view(np.float32) if dtype == "f32" else out
+
+
+def refresh(W: np.ndarray, dtype: str = "f32"):
+    """Re-prune: (W with its dropped entries set to +0, values, canonical meta)."""
+    values, meta = compress_24(W, dtype)
+    return prune_24(W, dtype), values, meta
+
+
+# ----------------------------------------------------------------------------
 # Tile-vector-wise sparsity ("Accelerating Sparse DNNs Based on Tiled GEMM",
 # Abstract and Figure 3: TW drop at the tile level, then 2:4 inside the tile)
 # ----------------------------------------------------------------------------
