@@ -196,6 +196,25 @@ P24_API p24_status spmm24_fused(const void* values, const void* meta, int32_t la
                                 int32_t act, void* stream);
 
 /*
+ * Masked fine-tuning ("Accelerating Sparse Deep Neural Networks", Abstract:
+ * prune the trained network to 2:4, then retrain it with that pattern).
+ * prune24_refresh -- prune24_compress of W and, in the same pass, every
+ *   dropped entry of W set to +0 in place (kept entries are left bit for
+ *   bit), so W equals its pruned self afterwards.  Arguments and rules as for
+ *   prune24_compress; W is read and written.  The re-prune a fine-tuning loop
+ *   runs every few steps.
+ * prune24_mask_apply -- W[m][k] := +0 for every k the stored metadata `meta`
+ *   (in `layout`, as written for an M x K matrix) does not select; selected
+ *   entries are left bit for bit.  W fp32 (16 B aligned) or bf16 (8 B
+ *   aligned), ldw >= K, ldw % 4 == 0; meta 4 B aligned; K % 4 == 0 (% 64 for
+ *   the device layout).  The per-step masking between re-prunes.
+ */
+P24_API p24_status prune24_refresh(void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                   void* values, void* meta, int32_t layout, void* stream);
+P24_API p24_status prune24_mask_apply(void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                      const void* meta, int32_t layout, void* stream);
+
+/*
  * transpose_bf16 -- dst = src^T for 16-bit elements (a bit copy).
  *   src   rows x cols, leading dim ld_src >= cols;  dst  cols x rows, ld_dst >= rows.
  *   Both 4 B aligned; rows <= 65535 * 64.  Turns X (K x N) into XT for spmm24_xt.

@@ -49,6 +49,8 @@ _SIGNATURES = {
     "prune24_values_bytes": (_c_size, [_c_i64, _c_i64, _c_i32]),
     "prune24_meta_bytes": (_c_size, [_c_i64, _c_i64, _c_i32]),
     "prune24_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i32, _c_vp]),
+    "prune24_refresh": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_i32, _c_vp]),
+    "prune24_mask_apply": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp]),
     "prune24_decompress": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp]),
     "spmm24": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                         _c_i64, _c_i32, _c_vp]),
@@ -228,17 +230,21 @@ class CompressedTWVar:
     total_keep: int
 
 
-def compress(W, layout="device") -> Compressed24:
+def _w_code(W):
+    torch = _torch()
+    if W.dtype == torch.float32:
+        return P24_F32
+    if W.dtype == torch.bfloat16:
+        return P24_BF16
+    raise ValueError("W must be float32 or bfloat16")
+
+
+def compress(W, layout="device", _refresh=False) -> Compressed24:
     """Magnitude 2:4 prune + compress of W (cuda fp32 or bf16, [M, K])."""
     torch = _torch()
     _require_cuda(W, "W")
     ldw = _rowmajor(W, "W")
-    if W.dtype == torch.float32:
-        wd = P24_F32
-    elif W.dtype == torch.bfloat16:
-        wd = P24_BF16
-    else:
-        raise ValueError("W must be float32 or bfloat16")
+    wd = _w_code(W)
     M, K = W.shape
     lc = _layout_code(layout)
     L = lib()
@@ -247,9 +253,26 @@ def compress(W, layout="device") -> Compressed24:
         raise P24Error(P24_ERR_SHAPE if K % 4 else P24_ERR_UNSUPPORTED, "prune24_compress")
     values = torch.empty(max(vb // 2, 1), dtype=torch.bfloat16, device=W.device)
     meta = torch.empty(max(mb // 4, 1), dtype=torch.int32, device=W.device)
-    _check(L.prune24_compress(_ptr(W), wd, M, K, ldw, _ptr(values), _ptr(meta), lc, _stream(W.device)),
-           "prune24_compress")
+    f, name = (L.prune24_refresh, "prune24_refresh") if _refresh else (L.prune24_compress, "prune24_compress")
+    _check(f(_ptr(W), wd, M, K, ldw, _ptr(values), _ptr(meta), lc, _stream(W.device)), name)
     return Compressed24(values, meta, M, K, lc)
+
+
+def refresh(W, layout="device") -> Compressed24:
+    """Re-prune for masked fine-tuning: compress(W) and, in the same pass, W's dropped entries
+    set to +0 in place."""
+    return compress(W, layout, _refresh=True)
+
+
+def mask_apply(W, c: Compressed24):
+    """W[m][k] := +0 wherever c's stored positions do not select k (in place); returns W."""
+    _require_cuda(W, "W")
+    ldw = _rowmajor(W, "W")
+    if tuple(W.shape) != (c.M, c.K):
+        raise ValueError(f"W is {tuple(W.shape)}, the mask is for {(c.M, c.K)}")
+    _check(lib().prune24_mask_apply(_ptr(W), _w_code(W), c.M, c.K, ldw, _ptr(c.meta), c.layout,
+                                    _stream(W.device)), "prune24_mask_apply")
+    return W
 
 
 def decompress(c: Compressed24):

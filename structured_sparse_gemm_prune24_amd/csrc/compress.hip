@@ -44,15 +44,36 @@ __device__ __forceinline__ void fetch_group(const T* __restrict__ W, int64_t ldw
   }
 }
 
+// The group of four back in place with only positions p0 = code & 3 and
+// p1 = code >> 2 kept: the other two become +0 (masked fine-tuning).
+template <typename T> __device__ __forceinline__ void store_masked_group(T* p, const uint32_t b[4], uint32_t code);
+template <> __device__ __forceinline__ void store_masked_group<float>(float* p, const uint32_t b[4], uint32_t code) {
+  const uint32_t p0 = code & 3u, p1 = code >> 2;
+  uint32_t o[4];
+#pragma unroll
+  for (uint32_t i = 0; i < 4; ++i) o[i] = (i == p0 || i == p1) ? b[i] : 0u;
+  *reinterpret_cast<u32x4*>(p) = u32x4{o[0], o[1], o[2], o[3]};
+}
+template <> __device__ __forceinline__ void store_masked_group<uint16_t>(uint16_t* p, const uint32_t b[4],
+                                                                         uint32_t code) {
+  const uint32_t p0 = code & 3u, p1 = code >> 2;
+  uint32_t o[4];
+#pragma unroll
+  for (uint32_t i = 0; i < 4; ++i) o[i] = (i == p0 || i == p1) ? b[i] : 0u;
+  *reinterpret_cast<u32x2*>(p) = u32x2{o[0] | (o[1] << 16), o[2] | (o[3] << 16)};
+}
+
 // --------------------------------------------------------------------------
 // Canonical layout: one thread per (row, metadata word) = 8 groups.
+// With WB (re-prune in place) the dropped entries of W are also set to +0:
+// W is then read and written through the same rows, hence no restrict on it.
 // --------------------------------------------------------------------------
-template <typename T, bool GATHER>
-__global__ __launch_bounds__(256) void k_compress_canonical(const T* __restrict__ W, int64_t ldw, int64_t M,
+template <typename T, bool GATHER, bool WB = false>
+__global__ __launch_bounds__(256) void k_compress_canonical(const T* W, int64_t ldw, int64_t M,
                                                             int64_t K, uint16_t* __restrict__ values,
                                                             uint32_t* __restrict__ meta,
                                                             const int32_t* __restrict__ kept, int64_t tile_m,
-                                                            int64_t kmax) {
+                                                            int64_t kmax, T* Wout) {
   const int64_t nw = (K + 31) / 32;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= M * nw) return;
@@ -70,6 +91,7 @@ __global__ __launch_bounds__(256) void k_compress_canonical(const T* __restrict_
       uint16_t v0, v1;
       const uint32_t code = compress_group<T>(b, v0, v1);
       vrow[g] = (uint32_t)v0 | ((uint32_t)v1 << 16);
+      if constexpr (WB) store_masked_group<T>(Wout + m * ldw + 4 * g, b, code);
       word |= code << (4 * q);
     }
   }
@@ -100,14 +122,15 @@ constexpr int CMP_META_PITCH = 65;
 // offsets[t] of the concatenation, its compacted K is offsets[t+1] - offsets[t]).
 enum GatherMode { G_NONE = 0, G_FIXED = 1, G_VAR = 2 };
 
-template <typename T, int GM>
-__global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __restrict__ W, int64_t ldw, int64_t M,
+template <typename T, int GM, bool WB = false>
+__global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, int64_t ldw, int64_t M,
                                                                     int64_t K, uint16_t* __restrict__ dvals,
                                                                     uint32_t* __restrict__ dmeta,
                                                                     const int32_t* __restrict__ kept,
                                                                     const int64_t* __restrict__ offsets,
-                                                                    int64_t tile_m, int64_t kmax) {
+                                                                    int64_t tile_m, int64_t kmax, T* Wout) {
   constexpr bool GATHER = GM != G_NONE;
+  static_assert(!WB || GM == G_NONE, "re-prune in place works on the whole matrix");
   __shared__ uint32_t sv[CMP_WAVES][8 * CMP_BLK_WORDS];
   __shared__ uint32_t sm[CMP_WAVES][4 * CMP_META_PITCH];
   const int64_t RB = device_row_blocks(M);
@@ -150,6 +173,9 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* __r
       fetch_group<T, GATHER>(W, ldw, m_rd, g_rd, kept_row, kmax, b);
       uint16_t v0, v1;
       uint32_t code = compress_group<T>(b, v0, v1);
+      if constexpr (WB) {
+        if (live) store_masked_group<T>(Wout + m * ldw + 4 * g, b, code);
+      }
       const uint32_t packed = live ? ((uint32_t)v0 | ((uint32_t)v1 << 16)) : 0u;
       code = live ? code : 0x4u;
       const int L = r + 32 * hl;
@@ -209,6 +235,32 @@ __global__ __launch_bounds__(256) void k_decompress(const uint16_t* __restrict__
   uint16_t* o = out + m * ldo + 4 * g;
 #pragma unroll
   for (uint32_t i = 0; i < 4; ++i) o[i] = (i == p0) ? v0 : ((i == p1) ? v1 : (uint16_t)0);
+}
+
+// --------------------------------------------------------------------------
+// Masked fine-tuning: W keeps only the positions the stored metadata selects.
+// One thread per (row, group): the group's 16 B (fp32) or 8 B (bf16) are read
+// and written back with the two unselected entries set to +0.
+// --------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_mask_apply(T* W, int64_t ldw, int64_t M, int64_t K,
+                                                    const uint32_t* __restrict__ meta, int layout) {
+  const int64_t G = K / 4;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= M * G) return;
+  const int64_t m = id / G, g = id % G;
+  uint32_t code;
+  if (layout == P24_LAYOUT_CANONICAL) {
+    code = (meta[m * ((K + 31) / 32) + g / 8] >> (4 * (g % 8))) & 0xFu;
+  } else {
+    const int64_t T_ = K / 64, s = g / 8, h = (g % 8) / 4, q = g % 4;
+    const int64_t rb = m / 32, L = m % 32 + 32 * h;
+    code = (meta[(((rb >> 2) * T_ + s / 2) * 4 + (rb & 3)) * 64 + L] >> (16 * (s % 2) + 4 * q)) & 0xFu;
+  }
+  T* p = W + m * ldw + 4 * g;
+  uint32_t b[4];
+  load_group<T>(p, b);
+  store_masked_group<T>(p, b, code);
 }
 
 // --------------------------------------------------------------------------
@@ -619,29 +671,33 @@ static p24_status check_compress_args(const void* W, int32_t w_dtype, int64_t M,
   return P24_OK;
 }
 
-template <int GM>
+template <int GM, bool WB = false>
 static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
                                   void* values, void* meta, int32_t layout, const int32_t* kept,
                                   int64_t tile_m, int64_t kmax, hipStream_t st, const int64_t* offsets = nullptr) {
   constexpr bool GATHER = GM != G_NONE;
+  // WB: W is written back in place (dropped entries -> +0)
   if (M == 0 || K == 0) return P24_OK;
   if (layout == P24_LAYOUT_CANONICAL) {
     const int64_t n = M * ((K + 31) / 32);
     if (w_dtype == P24_F32)
-      hipLaunchKernelGGL((k_compress_canonical<float, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
-                         (const float*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+      hipLaunchKernelGGL((k_compress_canonical<float, GATHER, WB>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+                         (const float*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax,
+                         WB ? (float*)W : nullptr);
     else
-      hipLaunchKernelGGL((k_compress_canonical<uint16_t, GATHER>), dim3(grid1d(n, 256)), dim3(256), 0, st,
-                         (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax);
+      hipLaunchKernelGGL((k_compress_canonical<uint16_t, GATHER, WB>), dim3(grid1d(n, 256)), dim3(256), 0, st,
+                         (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax,
+                         WB ? (uint16_t*)W : nullptr);
   } else {
     const int64_t waves = device_row_blocks(M) * ((K + 255) / 256);
     const dim3 grid(grid1d(waves, CMP_WAVES)), block(64 * CMP_WAVES);
     if (w_dtype == P24_F32)
-      hipLaunchKernelGGL((k_compress_device<float, GM>), grid, block, 0, st, (const float*)W, ldw, M, K,
-                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax);
+      hipLaunchKernelGGL((k_compress_device<float, GM, WB>), grid, block, 0, st, (const float*)W, ldw, M, K,
+                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax, WB ? (float*)W : nullptr);
     else
-      hipLaunchKernelGGL((k_compress_device<uint16_t, GM>), grid, block, 0, st, (const uint16_t*)W, ldw, M, K,
-                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax);
+      hipLaunchKernelGGL((k_compress_device<uint16_t, GM, WB>), grid, block, 0, st, (const uint16_t*)W, ldw, M, K,
+                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax,
+                         WB ? (uint16_t*)W : nullptr);
   }
   return launch_status();
 }
@@ -653,6 +709,34 @@ extern "C" P24_API p24_status prune24_compress(const void* W, int32_t w_dtype, i
   if (s != P24_OK) return s;
   return launch_compress<G_NONE>(W, w_dtype, M, K, ldw, values, meta, layout, nullptr, 1, K,
                                 (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status prune24_refresh(void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                              void* values, void* meta, int32_t layout, void* stream) {
+  const p24_status s = check_compress_args(W, w_dtype, M, K, ldw, values, meta, layout);
+  if (s != P24_OK) return s;
+  return launch_compress<G_NONE, true>(W, w_dtype, M, K, ldw, values, meta, layout, nullptr, 1, K,
+                                       (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status prune24_mask_apply(void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                                 const void* meta, int32_t layout, void* stream) {
+  if (w_dtype != P24_F32 && w_dtype != P24_BF16) return P24_ERR_DTYPE;
+  if (layout != P24_LAYOUT_CANONICAL && layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
+  if (M < 0 || K < 0 || K % 4 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (layout == P24_LAYOUT_DEVICE && K % 64) return P24_ERR_UNSUPPORTED;
+  if (M == 0 || K == 0) return P24_OK;
+  if (!W || !meta) return P24_ERR_NULL;
+  const size_t wal = w_dtype == P24_F32 ? 16 : 8;
+  if (!aligned(W, wal) || ldw % 4 || !aligned(meta, 4)) return P24_ERR_ALIGN;
+  const int64_t n = M * (K / 4);
+  if (w_dtype == P24_F32)
+    hipLaunchKernelGGL(k_mask_apply<float>, dim3(grid1d(n, 256)), dim3(256), 0, (hipStream_t)stream, (float*)W,
+                       ldw, M, K, (const uint32_t*)meta, (int)layout);
+  else
+    hipLaunchKernelGGL(k_mask_apply<uint16_t>, dim3(grid1d(n, 256)), dim3(256), 0, (hipStream_t)stream,
+                       (uint16_t*)W, ldw, M, K, (const uint32_t*)meta, (int)layout);
+  return launch_status();
 }
 
 extern "C" P24_API p24_status prune24_decompress(const void* values, const void* meta, int32_t layout,

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 24
+    assert len(syms) == len(set(syms)) == 26
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -67,6 +67,25 @@ def test_compress_validation(L):
     assert f(MISALIGNED, 0, 4, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_ALIGN
     assert f(FAKE, 0, 4, 8, 10, FAKE, FAKE, 0, NUL) == p24.P24_ERR_ALIGN          # ldw % 4
     assert f(NUL, 0, 0, 8, 8, NUL, NUL, 0, NUL) == p24.P24_OK                     # M == 0: no-op
+
+
+def test_mask_validation(L):
+    f = L.prune24_refresh            # same rules as prune24_compress
+    assert f(FAKE, 7, 4, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_DTYPE
+    assert f(FAKE, 0, 4, 6, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_SHAPE
+    assert f(FAKE, 0, 4, 96, 96, FAKE, FAKE, 1, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert f(MISALIGNED, 0, 4, 8, 8, FAKE, FAKE, 0, NUL) == p24.P24_ERR_ALIGN
+    assert f(NUL, 0, 0, 8, 8, NUL, NUL, 0, NUL) == p24.P24_OK
+    g = L.prune24_mask_apply
+    assert g(FAKE, 5, 4, 8, 8, FAKE, 0, NUL) == p24.P24_ERR_DTYPE
+    assert g(FAKE, 0, 4, 8, 8, FAKE, 3, NUL) == p24.P24_ERR_LAYOUT
+    assert g(FAKE, 0, 4, 6, 8, FAKE, 0, NUL) == p24.P24_ERR_SHAPE           # K % 4
+    assert g(FAKE, 0, 4, 8, 4, FAKE, 0, NUL) == p24.P24_ERR_SHAPE           # ldw < K
+    assert g(FAKE, 0, 4, 96, 96, FAKE, 1, NUL) == p24.P24_ERR_UNSUPPORTED   # device layout: K % 64
+    assert g(FAKE, 0, 4, 8, 8, NUL, 0, NUL) == p24.P24_ERR_NULL
+    assert g(MISALIGNED, 0, 4, 8, 8, FAKE, 0, NUL) == p24.P24_ERR_ALIGN
+    assert g(FAKE, 0, 4, 8, 10, FAKE, 0, NUL) == p24.P24_ERR_ALIGN          # ldw % 4
+    assert g(NUL, 0, 0, 8, 8, NUL, 0, NUL) == p24.P24_OK
 
 
 def test_spmm_validation(L):
