@@ -490,6 +490,81 @@ def tw_decompress(kept_list, Wc_list, M: int, K: int, tile_m: int) -> np.ndarray
 
 
 # ----------------------------------------------------------------------------
+# Comparison patterns ("Accelerating Sparse DNNs Based on Tiled GEMM",
+# Abstract: TVW against block sparsity and unstructured sparsity; Figure 5
+# names the element-wise (EW) and block-wise (BW) patterns, caption only).
+# BW: blocks of 128 rows (a tile) x 64 columns (a K step); a block's score is
+#   the fp64 sum of its 64 tile column scores (tvw_scores) in ascending column
+#   order; each tile keeps its keep_blocks highest-scored blocks (ties -> lower
+#   block), and their columns, ascending, are multiplied densely as in TW.
+# EW: every weight ranked by magnitude (sign-cleared bit pattern, as for 2:4)
+#   over the whole matrix, ties -> lower flat index m*K + k; the top
+#   keep_total are kept, in CSR form (row pointers, ascending columns, bf16
+#   values rounded to nearest even).
+# ----------------------------------------------------------------------------
+BW_COLS = 64
+
+
+def bw_block_scores(W: np.ndarray) -> np.ndarray:
+    """fp64 [T, K/64]: per 128-row tile and 64-column block, the sum of the tile column scores."""
+    sc = tvw_scores(W, 128)
+    T, K = sc.shape
+    if K % BW_COLS:
+        raise ValueError("K must be a multiple of 64")
+    out = np.zeros((T, K // BW_COLS), dtype=np.float64)
+    for j in range(K // BW_COLS):
+        acc = np.zeros(T, dtype=np.float64)
+        for c in range(BW_COLS):
+            acc = acc + sc[:, BW_COLS * j + c]
+        out[:, j] = acc
+    return out
+
+
+def bw_select(W: np.ndarray, keep_blocks: int) -> np.ndarray:
+    """Kept columns per tile, int32 [T, keep_blocks * 64], ascending."""
+    bs = bw_block_scores(W)
+    if not (0 < keep_blocks <= bs.shape[1]):
+        raise ValueError("keep_blocks must be in (0, K/64]")
+    order = np.argsort(np.iinfo(np.uint64).max - bs.view(np.uint64), axis=1, kind="stable")
+    blocks = np.sort(order[:, :keep_blocks], axis=1)
+    cols = (blocks[:, :, None] * BW_COLS + np.arange(BW_COLS)[None, None, :]).reshape(bs.shape[0], -1)
+    return cols.astype(np.int32)
+
+
+def bw_compress(W: np.ndarray, keep_blocks: int):
+    """(kept int32 [T, keep_blocks*64], Wc bf16 bits [M, keep_blocks*64]) as for TW."""
+    W = np.asarray(W, dtype=np.float32)
+    kept = bw_select(W, keep_blocks)
+    Wc = np.zeros((W.shape[0], kept.shape[1]), dtype=np.uint16)
+    for t in range(kept.shape[0]):
+        r0, r1 = 128 * t, min(W.shape[0], 128 * t + 128)
+        Wc[r0:r1] = bf16_rne(W[r0:r1][:, kept[t]])
+    return kept, Wc
+
+
+def ew_compress(W: np.ndarray, keep_total: int):
+    """(row_ptr int64 [M+1], cols int32 [keep_total], vals bf16 bits [keep_total])."""
+    W = np.asarray(W, dtype=np.float32)
+    M, K = W.shape
+    if not (0 < keep_total <= M * K):
+        raise ValueError("keep_total must be in (0, M*K]")
+    key = magnitude_key(W, "f32").reshape(-1)
+    ranked = np.argsort(np.iinfo(np.uint64).max - key.astype(np.uint64), kind="stable")
+    chosen = np.sort(ranked[:keep_total])                  # flat indices, row-major = CSR order
+    rows, cols = chosen // K, chosen % K
+    row_ptr = np.concatenate([[0], np.cumsum(np.bincount(rows, minlength=M))]).astype(np.int64)
+    return row_ptr, cols.astype(np.int32), bf16_rne(W.reshape(-1)[chosen])
+
+
+def ew_decompress(row_ptr, cols, vals, M: int, K: int) -> np.ndarray:
+    """Dense bf16 bits [M, K] from the CSR form."""
+    out = np.zeros((M, K), dtype=np.uint16)
+    for m in range(M):
+        out[m, cols[row_ptr[m]:row_ptr[m + 1]]] = vals[row_ptr[m]:row_ptr[m + 1]]
+    return out
+
+
+# ----------------------------------------------------------------------------
 # GEMM reference and bound (fp64; every bf16 x bf16 product is exact in fp64)
 # ----------------------------------------------------------------------------
 def gemm_ref(Wd: np.ndarray, X: np.ndarray, rows=None):
