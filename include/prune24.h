@@ -332,6 +332,43 @@ P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, con
                                int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream);
 
 /*
+ * Comparison patterns ("Accelerating Sparse DNNs Based on Tiled GEMM",
+ * Abstract: TVW against block and unstructured sparsity; Figure 5 names the
+ * element-wise and block-wise patterns).
+ * bw_compress -- block-wise: blocks of 128 rows (T = ceil(M/128) tiles) x 64
+ *   columns.  A block's score is the fp64 sum, in ascending column order, of
+ *   the tile column scores of tvw_compress (tile_m = 128); each tile keeps its
+ *   keep_blocks highest-scored blocks (ties -> lower block).  kept: int32
+ *   [T][keep_blocks*64], the kept blocks' columns ascending; Wp as for
+ *   tw_compress with keep_k = keep_blocks*64 (gemm_bf16_packed_bytes(M,
+ *   keep_k) bytes).  W fp32 as for tvw_compress, K % 64 == 0,
+ *   0 < keep_blocks <= K/64; workspace bw_workspace_bytes(M, K), 8 B aligned.
+ *   The product is spmm_tw(kept, Wp, M, K, 128, keep_blocks*64, ...).
+ * ew_compress -- unstructured: every weight ranked by magnitude (the fp32
+ *   bit pattern with the sign cleared) over the whole matrix, ties -> lower
+ *   m*K + k; the top keep_total (0 < keep_total <= M*K <= 2^32 - 1) are kept
+ *   in CSR form: row_ptr int64 [M+1] (8 B aligned), cols int32 [keep_total]
+ *   ascending within a row, vals bf16 [keep_total] (round to nearest even).
+ *   W fp32, 4 B aligned, ldw >= K; workspace ew_workspace_bytes(M, K), 256 B
+ *   aligned.
+ * spmm_ew -- Y = W X for that CSR form on the fp32 vector ALUs (row m:
+ *   sum over its entries in column order).  X bf16 K x N, 16 B aligned,
+ *   ldx >= N, ldx % 8 == 0; Y as for spmm24.  Column indices outside [0, K)
+ *   are clamped into it.
+ */
+P24_API size_t bw_workspace_bytes(int64_t M, int64_t K);
+P24_API p24_status bw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                               int64_t keep_blocks, int32_t* kept, void* Wp, void* workspace,
+                               size_t ws_bytes, void* stream);
+P24_API size_t ew_workspace_bytes(int64_t M, int64_t K);
+P24_API p24_status ew_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                               int64_t keep_total, int64_t* row_ptr, int32_t* cols, void* vals,
+                               void* workspace, size_t ws_bytes, void* stream);
+P24_API p24_status spmm_ew(const int64_t* row_ptr, const int32_t* cols, const void* vals, int64_t M,
+                           int64_t K, const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
+                           int64_t ldy, void* stream);
+
+/*
  * Dense bf16 GEMM, the denominator of every speedup ("over the dense model",
  * "Accelerating Sparse DNNs Based on Tiled GEMM", Abstract).  It runs the same
  * tile loop as spmm24 with the dense MFMA v_mfma_f32_32x32x16_bf16.

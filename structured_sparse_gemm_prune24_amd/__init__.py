@@ -72,6 +72,12 @@ _SIGNATURES = {
                                  _c_size, _c_vp]),
     "spmm_tw_var": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                              _c_i64, _c_vp]),
+    "bw_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "bw_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
+    "ew_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
+    "ew_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp, _c_size,
+                             _c_vp]),
+    "spmm_ew": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
     "spmm24_xt": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                            _c_i64, _c_vp]),
     "spmm24_fused": (_c_i32, [_c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_vp, _c_i64, _c_i32, _c_i64, _c_vp,
@@ -237,6 +243,17 @@ def _w_code(W):
     if W.dtype == torch.bfloat16:
         return P24_BF16
     raise ValueError("W must be float32 or bfloat16")
+
+
+@dataclass
+class CompressedEW:
+    """Unstructured sparsity in CSR form (bf16 values)."""
+    row_ptr: object      # torch.int64 [M + 1]
+    cols: object         # torch.int32 [keep_total]
+    vals: object         # torch.bfloat16 [keep_total]
+    M: int
+    K: int
+    keep_total: int
 
 
 def compress(W, layout="device", _refresh=False) -> Compressed24:
@@ -490,6 +507,54 @@ def spmm_tw_var(t: CompressedTWVar, X, out_dtype=None, out=None):
     ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
     _check(lib().spmm_tw_var(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.Wp), t.M, t.K, _ptr(X), ldx, N,
                              _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tw_var")
+    return out
+
+
+def bw_compress(W, keep_blocks: int) -> CompressedTW:
+    """Block-wise: per 128-row tile keep the keep_blocks 64-column blocks of largest L1 norm;
+    the result runs with spmm_tw."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("bw_compress takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    keep = int(keep_blocks) * 64
+    L = lib()
+    T = (M + 127) // 128
+    kept = torch.empty((T, keep), dtype=torch.int32, device=W.device)
+    Wp = torch.empty(max(L.gemm_bf16_packed_bytes(M, keep) // 2, 1), dtype=torch.bfloat16, device=W.device)
+    ws = torch.empty(max(L.bw_workspace_bytes(M, K), 8), dtype=torch.uint8, device=W.device)
+    _check(L.bw_compress(_ptr(W), P24_F32, M, K, ldw, int(keep_blocks), _ptr(kept), _ptr(Wp), _ptr(ws),
+                         ws.numel(), _stream(W.device)), "bw_compress")
+    return CompressedTW(kept, Wp, M, K, 128, keep)
+
+
+def ew_compress(W, keep_total: int) -> CompressedEW:
+    """Unstructured: the keep_total largest-magnitude weights of the whole matrix, in CSR form."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("ew_compress takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    keep_total = int(keep_total)
+    L = lib()
+    dev = W.device
+    row_ptr = torch.empty(M + 1, dtype=torch.int64, device=dev)
+    cols = torch.empty(max(keep_total, 1), dtype=torch.int32, device=dev)
+    vals = torch.empty(max(keep_total, 1), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(L.ew_workspace_bytes(M, K), 256), dtype=torch.uint8, device=dev)
+    _check(L.ew_compress(_ptr(W), P24_F32, M, K, ldw, keep_total, _ptr(row_ptr), _ptr(cols), _ptr(vals), _ptr(ws),
+                         ws.numel(), _stream(dev)), "ew_compress")
+    return CompressedEW(row_ptr, cols, vals, M, K, keep_total)
+
+
+def spmm_ew(t: CompressedEW, X, out_dtype=None, out=None):
+    """Y = W X for an unstructured (CSR) W; X bf16 [K, N]."""
+    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    _check(lib().spmm_ew(_ptr(t.row_ptr), _ptr(t.cols), _ptr(t.vals), t.M, t.K, _ptr(X), ldx, N, _ptr(out),
+                         _out_code(out.dtype), ldy, _stream(X.device)), "spmm_ew")
     return out
 
 

@@ -628,6 +628,172 @@ __global__ __launch_bounds__(256) void k_pack_tw(const float* __restrict__ W, in
   *reinterpret_cast<u32x4*>(out + ((rb * S + st) * 64 + L) * 8) = v;
 }
 
+// --------------------------------------------------------------------------
+// Comparison patterns.
+// BW: the score of block (tile t, 64 columns j) is the fp64 sum of the tile's
+// column scores 64j .. 64j+63 in ascending order (one thread per block); the
+// kept blocks (k_tvw_select over the block scores) expand to their columns.
+// --------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_bw_block_scores(const double* __restrict__ scores, int64_t T, int64_t K,
+                                                         double* __restrict__ bscores) {
+  const int64_t nb = K / 64;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= T * nb) return;
+  const int64_t t = id / nb, j = id % nb;
+  const double* sc = scores + t * K + 64 * j;
+  double acc = 0.0;
+  for (int c = 0; c < 64; ++c) acc = acc + sc[c];
+  bscores[id] = acc;
+}
+
+__global__ __launch_bounds__(256) void k_bw_expand(const int32_t* __restrict__ kept_blocks, int64_t T,
+                                                   int64_t keep_blocks, int32_t* __restrict__ kept) {
+  const int64_t n = keep_blocks * 64;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= T * n) return;
+  const int64_t t = id / n, i = id % n;
+  kept[id] = kept_blocks[t * keep_blocks + i / 64] * 64 + (int32_t)(i % 64);
+}
+
+// EW: the magnitude keys (sign-cleared fp32 bits) of the whole matrix; the
+// same MSB-first radix select as the per-tile-keep plan (4 digit passes), then
+// per row the keys above the cut and equal to it, the row pointers (equal keys
+// taken in row-major order), and a per-row compaction into CSR.
+__device__ __forceinline__ uint32_t ew_key(const float* W, int64_t ldw, int64_t K, int64_t i) {
+  return __float_as_uint(W[(i / K) * ldw + i % K]) & 0x7FFFFFFFu;
+}
+
+__global__ __launch_bounds__(VAR_THREADS) void k_ew_radix(const float* __restrict__ W, int64_t ldw, int64_t M,
+                                                          int64_t K, int shift, VarSelect* __restrict__ vs) {
+  __shared__ uint32_t h[256];
+  __shared__ uint32_t last;
+  const int tid = threadIdx.x;
+  const uint64_t prefix = vs->prefix;
+  const int64_t need = vs->need;
+  h[tid] = 0u;
+  __syncthreads();
+  const uint64_t hi_mask = shift == 24 ? 0ull : (0xFFFFFFFFull << (shift + 8)) & 0xFFFFFFFFull;
+  const int64_t n = M * K;
+  for (int64_t i = (int64_t)blockIdx.x * VAR_THREADS + tid; i < n; i += (int64_t)gridDim.x * VAR_THREADS) {
+    const uint64_t x = ew_key(W, ldw, K, i);
+    if ((x & hi_mask) == prefix) atomicAdd(&h[(x >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  if (h[tid]) atomicAdd(&vs->hist[tid], h[tid]);
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) last = atomicAdd(&vs->ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
+  __syncthreads();
+  if (!last) return;
+  __threadfence();
+  if (tid < 64) {
+    uint32_t hb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      hb[i] = __hip_atomic_load(&vs->hist[4 * tid + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int d;
+    int64_t rest;
+    if (find_cut(hb, need, tid, &d, &rest)) {
+      vs->prefix = prefix | ((uint64_t)d << shift);
+      vs->need = rest;
+    }
+  }
+  __syncthreads();
+  vs->hist[tid] = 0u;
+  if (tid == 0) vs->ticket = 0u;
+}
+
+__global__ __launch_bounds__(VAR_THREADS) void k_ew_row_counts(const float* __restrict__ W, int64_t ldw, int64_t K,
+                                                               const VarSelect* __restrict__ vs,
+                                                               int32_t* __restrict__ gt, int32_t* __restrict__ eq) {
+  __shared__ uint32_t sg[VAR_THREADS / 64], se[VAR_THREADS / 64];
+  const int64_t m = blockIdx.x;
+  const uint32_t v = (uint32_t)vs->prefix;
+  const float* row = W + m * ldw;
+  uint32_t g = 0, e = 0;
+  for (int64_t k = threadIdx.x; k < K; k += VAR_THREADS) {
+    const uint32_t x = __float_as_uint(row[k]) & 0x7FFFFFFFu;
+    g += x > v ? 1u : 0u;
+    e += x == v ? 1u : 0u;
+  }
+#pragma unroll
+  for (int d = 32; d > 0; d >>= 1) {
+    g += __shfl_xor(g, d);
+    e += __shfl_xor(e, d);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    sg[threadIdx.x >> 6] = g;
+    se[threadIdx.x >> 6] = e;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t G = 0, E = 0;
+    for (int w = 0; w < VAR_THREADS / 64; ++w) {
+      G += sg[w];
+      E += se[w];
+    }
+    gt[m] = (int32_t)G;
+    eq[m] = (int32_t)E;
+  }
+}
+
+// row pointers; eq[m] is replaced by the number of row m's equal keys taken
+__global__ __launch_bounds__(SEL_THREADS) void k_ew_plan(int64_t M, const VarSelect* __restrict__ vs,
+                                                         const int32_t* __restrict__ gt, int32_t* __restrict__ eq,
+                                                         int64_t* __restrict__ row_ptr) {
+  __shared__ int64_t wave_sums[SEL_WAVES];
+  const int64_t need = vs->need;
+  int64_t eq_base = 0, off_base = 0;
+  for (int64_t m0 = 0; m0 < M; m0 += SEL_THREADS) {
+    const int64_t m = m0 + threadIdx.x;
+    const bool live = m < M;
+    const int64_t e = live ? eq[m] : 0;
+    int64_t eq_total, cnt_total;
+    const int64_t before = eq_base + block_exclusive_scan<int64_t>(e, &eq_total, wave_sums);
+    int64_t take = need - before;
+    take = take < 0 ? 0 : (take > e ? e : take);
+    const int64_t cnt = live ? gt[m] + take : 0;
+    const int64_t off = off_base + block_exclusive_scan<int64_t>(cnt, &cnt_total, wave_sums);
+    if (live) {
+      row_ptr[m] = off;
+      eq[m] = (int32_t)take;
+    }
+    eq_base += eq_total;
+    off_base += cnt_total;
+  }
+  if (threadIdx.x == 0) row_ptr[M] = off_base;
+}
+
+__global__ __launch_bounds__(SEL_THREADS) void k_ew_compact(const float* __restrict__ W, int64_t ldw, int64_t K,
+                                                            const VarSelect* __restrict__ vs,
+                                                            const int32_t* __restrict__ take,
+                                                            const int64_t* __restrict__ row_ptr,
+                                                            int32_t* __restrict__ cols, uint16_t* __restrict__ vals) {
+  __shared__ uint32_t wave_sums[SEL_WAVES];
+  const int64_t m = blockIdx.x;
+  const uint32_t v = (uint32_t)vs->prefix;
+  const int64_t need = take[m];
+  const float* row = W + m * ldw;
+  int64_t eq_base = 0, out_base = row_ptr[m];
+  for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS) {
+    const int64_t k = k0 + threadIdx.x;
+    const uint32_t bits = k < K ? __float_as_uint(row[k]) : 0u;
+    const uint32_t x = bits & 0x7FFFFFFFu;
+    const bool gt = k < K && x > v;
+    const bool eqk = k < K && x == v;
+    int64_t eq_total, keep_total;
+    const int64_t eq_rank = eq_base + block_exclusive_scan<uint32_t>(eqk ? 1u : 0u, &eq_total, wave_sums);
+    const bool keep = gt || (eqk && eq_rank < need);
+    const int64_t pos = out_base + block_exclusive_scan<uint32_t>(keep ? 1u : 0u, &keep_total, wave_sums);
+    if (keep) {
+      cols[pos] = (int32_t)k;
+      vals[pos] = f32_to_bf16_rne(bits);
+    }
+    eq_base += eq_total;
+    out_base += keep_total;
+  }
+}
+
 }  // namespace p24
 
 // ============================================================================
@@ -923,5 +1089,82 @@ extern "C" P24_API p24_status tw_var_compress(const void* W, int32_t w_dtype, in
   const int64_t rows = var_tiles(M) * 128;
   hipLaunchKernelGGL(k_pack_tw<true>, dim3(grid1d(rows * (K / 8), 256)), dim3(256), 0, st, (const float*)W, ldw,
                      M, K, K, (const int32_t*)kept, (const int64_t*)offsets, (int64_t)128, rows, (uint16_t*)Wp);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------------------
+// Comparison patterns (block-wise, unstructured)
+// ---------------------------------------------------------------------------
+extern "C" P24_API size_t bw_workspace_bytes(int64_t M, int64_t K) {
+  if (M < 0 || K <= 0) return 0;
+  const int64_t T_ = var_tiles(M);
+  return (size_t)T_ * (size_t)K * sizeof(double) + (size_t)T_ * (size_t)(K / 64) * (sizeof(double) + 4);
+}
+
+extern "C" P24_API p24_status bw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                          int64_t keep_blocks, int32_t* kept, void* Wp, void* workspace,
+                                          size_t ws_bytes, void* stream) {
+  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
+  if (M < 0 || K <= 0 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (keep_blocks <= 0 || keep_blocks > K / 64) return P24_ERR_SHAPE;
+  if (M == 0) return P24_OK;
+  if (!W || !kept || !Wp) return P24_ERR_NULL;
+  if (!workspace || ws_bytes < bw_workspace_bytes(M, K)) return P24_ERR_WORKSPACE;
+  if (!aligned(W, 16) || ldw % 4 || !aligned(Wp, 16) || !aligned(kept, 4) || !aligned(workspace, 8))
+    return P24_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t T_ = var_tiles(M), nb = K / 64, keep = keep_blocks * 64;
+  double* scores = (double*)workspace;
+  double* bscores = scores + T_ * K;
+  int32_t* kept_blocks = (int32_t*)(bscores + T_ * nb);
+  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
+                     (int64_t)128, scores);
+  hipLaunchKernelGGL(k_bw_block_scores, dim3(grid1d(T_ * nb, 256)), dim3(256), 0, st, (const double*)scores, T_, K,
+                     bscores);
+  hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)bscores, nb,
+                     keep_blocks, (const int64_t*)nullptr, kept_blocks);
+  hipLaunchKernelGGL(k_bw_expand, dim3(grid1d(T_ * keep, 256)), dim3(256), 0, st, (const int32_t*)kept_blocks, T_,
+                     keep_blocks, kept);
+  const int64_t rows = (M + 31) / 32 * 32;
+  hipLaunchKernelGGL(k_pack_tw<false>, dim3(grid1d(rows * (keep / 8), 256)), dim3(256), 0, st, (const float*)W, ldw,
+                     M, K, keep, (const int32_t*)kept, (const int64_t*)nullptr, (int64_t)128, rows, (uint16_t*)Wp);
+  return launch_status();
+}
+
+extern "C" P24_API size_t ew_workspace_bytes(int64_t M, int64_t K) {
+  (void)K;
+  if (M < 0) return 0;
+  return ((sizeof(VarSelect) + 255) & ~(size_t)255) + 2 * (size_t)M * sizeof(int32_t);
+}
+
+extern "C" P24_API p24_status ew_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                          int64_t keep_total, int64_t* row_ptr, int32_t* cols, void* vals,
+                                          void* workspace, size_t ws_bytes, void* stream) {
+  if (w_dtype != P24_F32) return P24_ERR_DTYPE;
+  if (M < 0 || K <= 0 || ldw < K || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
+  if (M * K > UINT32_MAX || keep_total <= 0 || keep_total > M * K) return P24_ERR_SHAPE;
+  if (M == 0) return P24_OK;
+  if (!W || !row_ptr || !cols || !vals) return P24_ERR_NULL;
+  if (!workspace || ws_bytes < ew_workspace_bytes(M, K)) return P24_ERR_WORKSPACE;
+  if (!aligned(W, 4) || !aligned(row_ptr, 8) || !aligned(cols, 4) || !aligned(vals, 2) || !aligned(workspace, 256))
+    return P24_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  VarSelect* vs = (VarSelect*)ws;
+  ws += (sizeof(VarSelect) + 255) & ~(size_t)255;
+  int32_t* gt = (int32_t*)ws;
+  int32_t* eq = gt + M;
+  hipLaunchKernelGGL(k_var_init, dim3(1), dim3(VAR_THREADS), 0, st, vs, keep_total);
+  const int64_t n = M * K, per_block = (int64_t)VAR_THREADS * 16;
+  const unsigned blocks = (unsigned)std::min<int64_t>((n + per_block - 1) / per_block, 2048);
+  for (int shift = 24; shift >= 0; shift -= 8)
+    hipLaunchKernelGGL(k_ew_radix, dim3(blocks), dim3(VAR_THREADS), 0, st, (const float*)W, ldw, M, K, shift, vs);
+  hipLaunchKernelGGL(k_ew_row_counts, dim3((unsigned)M), dim3(VAR_THREADS), 0, st, (const float*)W, ldw, K,
+                     (const VarSelect*)vs, gt, eq);
+  hipLaunchKernelGGL(k_ew_plan, dim3(1), dim3(SEL_THREADS), 0, st, M, (const VarSelect*)vs, (const int32_t*)gt, eq,
+                     row_ptr);
+  hipLaunchKernelGGL(k_ew_compact, dim3((unsigned)M), dim3(SEL_THREADS), 0, st, (const float*)W, ldw, K,
+                     (const VarSelect*)vs, (const int32_t*)eq, (const int64_t*)row_ptr, cols, (uint16_t*)vals);
   return launch_status();
 }

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 26
+    assert len(syms) == len(set(syms)) == 31
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -224,6 +224,33 @@ def test_tw_validation(L):
     assert v(FAKE, NUL, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_NULL
     assert v(FAKE, FAKE, FAKE, FAKE, 256, 96, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_UNSUPPORTED
     assert v(NUL, NUL, NUL, NUL, 0, 256, NUL, 64, 64, NUL, 0, 64, NUL) == p24.P24_OK
+
+
+def test_pattern_validation(L):
+    assert L.bw_workspace_bytes(300, 256) == 3 * 256 * 8 + 3 * 4 * 12
+    f = L.bw_compress
+    assert f(FAKE, 1, 256, 256, 256, 2, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_DTYPE
+    assert f(FAKE, 0, 256, 200, 200, 2, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_UNSUPPORTED   # K % 64
+    assert f(FAKE, 0, 256, 256, 256, 5, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_SHAPE         # > K/64 blocks
+    assert f(FAKE, 0, 256, 256, 256, 0, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_SHAPE
+    assert f(FAKE, 0, 256, 256, 256, 2, NUL, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_NULL
+    assert f(FAKE, 0, 256, 256, 256, 2, FAKE, FAKE, FAKE, 64, NUL) == p24.P24_ERR_WORKSPACE
+    assert f(NUL, 0, 0, 256, 256, 2, NUL, NUL, NUL, 0, NUL) == p24.P24_OK
+    g = L.ew_compress
+    assert g(FAKE, 1, 64, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_DTYPE
+    assert g(FAKE, 0, 64, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_SHAPE
+    assert g(FAKE, 0, 64, 64, 64, 64 * 64 + 1, FAKE, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_SHAPE
+    assert g(FAKE, 0, 1 << 17, 1 << 16, 1 << 16, 10, FAKE, FAKE, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_SHAPE
+    assert g(FAKE, 0, 64, 64, 64, 10, FAKE, NUL, FAKE, FAKE, 1 << 30, NUL) == p24.P24_ERR_NULL
+    assert g(FAKE, 0, 64, 64, 64, 10, FAKE, FAKE, FAKE, FAKE, 16, NUL) == p24.P24_ERR_WORKSPACE
+    assert g(FAKE, 0, 64, 64, 64, 10, FAKE, FAKE, FAKE, ctypes.c_void_p((1 << 20) + 64), 1 << 30, NUL) \
+        == p24.P24_ERR_ALIGN
+    h = L.spmm_ew
+    assert h(FAKE, FAKE, FAKE, 64, 64, FAKE, 64, 64, FAKE, 7, 64, NUL) == p24.P24_ERR_DTYPE
+    assert h(FAKE, FAKE, FAKE, 64, 64, FAKE, 32, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_SHAPE          # ldx < N
+    assert h(FAKE, FAKE, FAKE, 64, 64, FAKE, 68, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_ALIGN          # ldx % 8
+    assert h(FAKE, NUL, FAKE, 64, 64, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_NULL
+    assert h(NUL, NUL, NUL, 0, 64, NUL, 64, 64, NUL, 0, 64, NUL) == p24.P24_OK
 
 
 def test_dense_validation(L):
