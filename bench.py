@@ -7,7 +7,8 @@ resident in HBM.  Dense-equivalent flops = 2 M N K; the sparse kernel performs
 half of them (M N K).
 
 Beside the headline, the same run times (HIP events on the launch stream):
-  - prune24_compress of the same W (the offline prune + compress step),
+  - prune24_compress of the same W (the offline prune + compress step), and
+    the masked fine-tuning pieces (prune24_refresh, prune24_mask_apply),
   - this project's dense bf16 GEMM of the unpruned W (the speedup denominator),
   - torch.matmul (hipBLASLt) of the same shapes, as context only,
   - the TVW workload (4096^3, tile 128, keep 2048): tvw_compress + spmm_tvw,
@@ -224,7 +225,18 @@ def table(args):
             rec["spmm_tvw_cold_us"] = timeit_rot([lambda s=s_: p24.spmm_tvw(s[0], s[1], out=s[2]) for s_ in sets])
             tw = p24.tw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
             rec["spmm_tw_us"] = timeit(lambda: p24.spmm_tw(tw, X, out=Y))
-            del tw
+            # the page's comparison patterns at TVW's density (a quarter of the weights):
+            # TW keeping a quarter of the columns, block-wise 128 x 64 blocks, unstructured
+            d4 = wl.K // 4
+            tw4 = p24.tw_compress(W, tile_m=wl.tile_m, keep_k=d4)
+            rec["spmm_tw_quarter_us"] = timeit(lambda: p24.spmm_tw(tw4, X, out=Y))
+            bw4 = p24.bw_compress(W, d4 // 64)
+            rec["spmm_bw_quarter_us"] = timeit(lambda: p24.spmm_tw(bw4, X, out=Y))
+            ew4 = p24.ew_compress(W, wl.M * wl.K // 4)
+            rec["spmm_ew_quarter_us"] = timeit(lambda: p24.spmm_ew(ew4, X, out=Y))
+            rec["tvw_speedup_vs_bw"] = rec["spmm_bw_quarter_us"] / rec["spmm_tvw_us"]
+            rec["tvw_speedup_vs_ew"] = rec["spmm_ew_quarter_us"] / rec["spmm_tvw_us"]
+            del tw, tw4, bw4, ew4
             sparse_us = rec["spmm_tvw_us"]
             del sets
         else:
@@ -397,6 +409,14 @@ def main():
             p24.compress(Wt, layout="device")
         ev_c = event_times_ms(torch, lambda: p24.compress(Wt, layout="device"), 5)
         rows["prune24_compress_us_mean"] = sum(ev_c) / len(ev_c) * 1e3
+        # masked fine-tuning on the headline W: re-prune in place, and the per-step masking
+        Wr = Wt.clone()
+        c_r = p24.refresh(Wr)
+        ev_r = event_times_ms(torch, lambda: p24.refresh(Wr), 5)
+        rows["prune24_refresh_us_mean"] = sum(ev_r) / len(ev_r) * 1e3
+        ev_m = event_times_ms(torch, lambda: p24.mask_apply(Wr, c_r), 5)
+        rows["prune24_mask_apply_us_mean"] = sum(ev_m) / len(ev_m) * 1e3
+        del Wr, c_r
 
     # ---------------- TVW workload ----------------
     if args.only in (None, "tvw"):
