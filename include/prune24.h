@@ -290,6 +290,10 @@ P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, const void*
  *   sum_j Wc_t[m][j] X[kept[offsets[t] + j]][n].  Block rows run in `order`.
  *   offsets / order / kept as written by tvw_var_compress (out-of-range kept
  *   entries are clamped into [0, K)); X, Y as for spmm_tvw (2 * K * ldx < 2^32).
+ *   offsets and order are device data the call cannot check without a
+ *   synchronization: offsets must be non-decreasing multiples of 64 with steps
+ *   of at most K, and order a permutation of 0 .. T-1; anything else is
+ *   undefined behaviour (the kernels address W through them).
  */
 P24_API size_t tvw_var_workspace_bytes(int64_t M, int64_t K);
 P24_API p24_status tvw_var_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
@@ -316,7 +320,8 @@ P24_API p24_status spmm_tvw_var(const int64_t* offsets, const int32_t* order, co
  *   exactly as tvw_var_compress; Wp (capacity T*K*256 bytes, 16 B aligned)
  *   holds tile t's 128 x c_t dense operand (rows past M zero) from element
  *   128*offsets[t].  Workspace tvw_var_workspace_bytes(M, K).
- * spmm_tw_var -- Y = W X for that storage; block rows run in `order`.
+ * spmm_tw_var -- Y = W X for that storage; block rows run in `order`
+ *   (same requirements on offsets and order as spmm_tvw_var).
  */
 P24_API p24_status tw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
                                int64_t tile_m, int64_t keep_k, int32_t* kept, void* Wp, void* workspace,
@@ -353,8 +358,10 @@ P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, con
  *   aligned.
  * spmm_ew -- Y = W X for that CSR form on the fp32 vector ALUs (row m:
  *   sum over its entries in column order).  X bf16 K x N, 16 B aligned,
- *   ldx >= N, ldx % 8 == 0; Y as for spmm24.  Column indices outside [0, K)
- *   are clamped into it.
+ *   ldx >= N, ldx % 8 == 0; Y as for spmm24.  row_ptr must be non-decreasing
+ *   from 0 (device data, not checked; the kernel reads cols and vals through
+ *   it); columns must ascend within a row and lie in [0, K) -- others add
+ *   unspecified terms but no access leaves X or the kernel's LDS tile.
  */
 P24_API size_t bw_workspace_bytes(int64_t M, int64_t K);
 P24_API p24_status bw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
