@@ -10,6 +10,12 @@ not been built this module raises on first use -- there is no fallback.
     Y = p24.spmm24(c, X)                # X: cuda bf16 [K, N] -> Y bf16 [M, N]
     t = p24.tvw_compress(W, 128, K // 2)
     Y = p24.spmm_tvw(t, X)
+    v = p24.tvw_var_compress(W)         # per-tile keep counts from one global ranking
+    Y = p24.spmm_tvw_var(v, X)
+    w = p24.tw_compress(W, 128, K // 2) # tile column drop only, dense MFMA
+    Y = p24.spmm_tw(w, X)
+    c = p24.refresh(W); p24.mask_apply(W, c)   # masked fine-tuning
+    b = p24.bw_compress(W, 16); e = p24.ew_compress(W, W.numel() // 4)   # comparison patterns
 """
 from __future__ import annotations
 
@@ -256,8 +262,12 @@ class CompressedEW:
     keep_total: int
 
 
-def compress(W, layout="device", _refresh=False) -> Compressed24:
+def compress(W, layout="device") -> Compressed24:
     """Magnitude 2:4 prune + compress of W (cuda fp32 or bf16, [M, K])."""
+    return _compress(W, layout, refresh=False)
+
+
+def _compress(W, layout, refresh: bool) -> Compressed24:
     torch = _torch()
     _require_cuda(W, "W")
     ldw = _rowmajor(W, "W")
@@ -270,7 +280,7 @@ def compress(W, layout="device", _refresh=False) -> Compressed24:
         raise P24Error(P24_ERR_SHAPE if K % 4 else P24_ERR_UNSUPPORTED, "prune24_compress")
     values = torch.empty(max(vb // 2, 1), dtype=torch.bfloat16, device=W.device)
     meta = torch.empty(max(mb // 4, 1), dtype=torch.int32, device=W.device)
-    f, name = (L.prune24_refresh, "prune24_refresh") if _refresh else (L.prune24_compress, "prune24_compress")
+    f, name = (L.prune24_refresh, "prune24_refresh") if refresh else (L.prune24_compress, "prune24_compress")
     _check(f(_ptr(W), wd, M, K, ldw, _ptr(values), _ptr(meta), lc, _stream(W.device)), name)
     return Compressed24(values, meta, M, K, lc)
 
@@ -278,7 +288,7 @@ def compress(W, layout="device", _refresh=False) -> Compressed24:
 def refresh(W, layout="device") -> Compressed24:
     """Re-prune for masked fine-tuning: compress(W) and, in the same pass, W's dropped entries
     set to +0 in place."""
-    return compress(W, layout, _refresh=True)
+    return _compress(W, layout, refresh=True)
 
 
 def mask_apply(W, c: Compressed24):
