@@ -339,6 +339,19 @@ def main():
         launch_ms = sum(ev) / len(ev)
         rows["spmm24_us_mean"] = launch_ms * 1e3
         rows["spmm24_us_median"] = median(ev) * 1e3
+        rows["spmm24_us_min"] = min(ev) * 1e3
+    if args.only is None:
+        # context: the same launches alternating between two full input/output sets
+        # (688 MB, beyond the 256 MB MALL), so each launch finds its inputs only in HBM
+        c2, X2, Y2 = p24.compress(Wt, layout="device"), Xt.clone(), torch.empty_like(Y)
+        alt = [lambda: p24.spmm24(c, Xt, out=Y), lambda: p24.spmm24(c2, X2, out=Y2)]
+        for i in range(4):
+            alt[i % 2]()
+        ev_cold = []
+        for i in range(max(args.steps // 2, 10)):
+            ev_cold += event_times_ms(torch, alt[i % 2], 1)
+        rows["spmm24_cold_us_mean"] = sum(ev_cold) / len(ev_cold) * 1e3
+        del c2, X2, Y2, alt
     if args.only == "spmm":
         print(json.dumps(rows))
         return
