@@ -281,7 +281,8 @@ def main():
         return table(args)
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "see DESIGN.md for how the path would shard", file=sys.stderr)
+              "across GPUs the product would split by tokens (N) or by output rows (M) with no exchange step",
+              file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
