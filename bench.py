@@ -280,7 +280,7 @@ def main():
     if args.table:
         return table(args)
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); "
               "across GPUs the product would split by tokens (N) or by output rows (M) with no exchange step",
               file=sys.stderr)
         sys.exit(2)

@@ -77,7 +77,7 @@ enum {
   P24_ERR_SHAPE = -2,        /* negative size, ld too small, K % 4 != 0, bad tile/keep */
   P24_ERR_ALIGN = -3,        /* pointer or leading dimension not aligned as required */
   P24_ERR_DTYPE = -4,        /* unknown dtype code */
-  P24_ERR_UNSUPPORTED = -5,  /* valid request this build does not implement (e.g. K % 64) */
+  P24_ERR_UNSUPPORTED = -5,  /* valid request the library does not implement (e.g. K % 64) */
   P24_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
   P24_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required */
   P24_ERR_LAYOUT = -8        /* unknown layout code, or layout not accepted here */

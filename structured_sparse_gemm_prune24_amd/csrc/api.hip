@@ -10,7 +10,7 @@ extern "C" P24_API const char* prune24_strerror(p24_status s) {
     case P24_ERR_SHAPE: return "invalid shape, leading dimension, tile or keep count";
     case P24_ERR_ALIGN: return "pointer or leading dimension not aligned as required";
     case P24_ERR_DTYPE: return "unknown or unsupported dtype";
-    case P24_ERR_UNSUPPORTED: return "request not supported by this build (see shape rules)";
+    case P24_ERR_UNSUPPORTED: return "request not supported by the library (see the shape rules)";
     case P24_ERR_HIP: return "HIP runtime error at kernel launch";
     case P24_ERR_WORKSPACE: return "workspace missing or too small";
     case P24_ERR_LAYOUT: return "unknown layout, or layout not accepted by this entry point";
