@@ -87,7 +87,7 @@ enum { P24_F32 = 0, P24_BF16 = 1 };                         /* element dtypes */
 enum { P24_LAYOUT_CANONICAL = 0, P24_LAYOUT_DEVICE = 1 };    /* compressed layouts */
 enum { P24_ALGO_AUTO = 0, P24_ALGO_SMFMAC = 1, P24_ALGO_DECOMP_MFMA = 2 };   /* spmm24 algorithms */
 enum { P24_X_KN = 0, P24_X_NK = 1 };                            /* spmm24_fused: X orientation */
-enum { P24_ACT_NONE = 0, P24_ACT_RELU = 1, P24_ACT_GELU = 2 };  /* spmm24_fused: activation */
+enum { P24_ACT_NONE = 0, P24_ACT_RELU = 1, P24_ACT_GELU = 2 };  /* fused epilogues: activation */
 
 /* ABI version of the loaded library (PRUNE24_ABI_VERSION). */
 P24_API int32_t prune24_abi_version(void);
@@ -261,6 +261,18 @@ P24_API p24_status spmm_tvw(const int32_t* kept, const void* values, const void*
                             int32_t y_dtype, int64_t ldy, void* stream);
 
 /*
+ * spmm_tvw_fused -- spmm_tvw with the epilogue of spmm24_fused:
+ *   Y = act(W X + bias), bias fp32 [M] (one value per output row, nullptr for
+ *   none, 4 B aligned), act P24_ACT_NONE / _RELU / _GELU (else
+ *   P24_ERR_UNSUPPORTED); other arguments and rules as for spmm_tvw.
+ */
+P24_API p24_status spmm_tvw_fused(const int32_t* kept, const void* values, const void* meta,
+                                  int32_t layout, int64_t M, int64_t K, int64_t tile_m,
+                                  int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
+                                  int32_t y_dtype, int64_t ldy, const float* bias, int32_t act,
+                                  void* stream);
+
+/*
  * TVW with a keep count per tile ("Accelerating Sparse DNNs Based on Tiled
  * GEMM", Abstract: regular structure inside a tile, irregular pruning across
  * the matrix; TL;DR: load balancing through batching).  Tiles are 128 rows:
@@ -304,6 +316,12 @@ P24_API p24_status spmm_tvw_var(const int64_t* offsets, const int32_t* order, co
                                 const void* values, const void* meta, int64_t M, int64_t K,
                                 const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
                                 int64_t ldy, void* stream);
+/* spmm_tvw_var_fused -- spmm_tvw_var with bias + activation, as spmm_tvw_fused. */
+P24_API p24_status spmm_tvw_var_fused(const int64_t* offsets, const int32_t* order,
+                                      const int32_t* kept, const void* values, const void* meta,
+                                      int64_t M, int64_t K, const void* X, int64_t ldx, int64_t N,
+                                      void* Y, int32_t y_dtype, int64_t ldy, const float* bias,
+                                      int32_t act, void* stream);
 
 /*
  * TW alone -- the tile column drop without the 2:4 step ("Accelerating Sparse

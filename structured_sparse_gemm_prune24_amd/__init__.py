@@ -65,6 +65,10 @@ _SIGNATURES = {
                               _c_i32, _c_vp, _c_size, _c_vp]),
     "spmm_tvw": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
                           _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
+    "spmm_tvw_fused": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
+                                _c_i64, _c_vp, _c_i32, _c_i64, _c_vp, _c_i32, _c_vp]),
+    "spmm_tvw_var_fused": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64,
+                                    _c_vp, _c_i32, _c_i64, _c_vp, _c_i32, _c_vp]),
     "tvw_var_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "tvw_var_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_vp,
                                   _c_vp, _c_vp, _c_size, _c_vp]),
@@ -383,8 +387,8 @@ def tvw_compress(W, tile_m: int = 128, keep_k: int | None = None, layout="device
     return CompressedTVW(kept, values, meta, M, K, tile_m, keep_k, lc)
 
 
-def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None):
-    """Y = W X for a TVW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
+def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None, bias=None, act="none"):
+    """Y = act(W X + bias) for a TVW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
     _require_cuda(X, "X")
@@ -397,6 +401,12 @@ def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None):
     if out is None:
         out = torch.empty((t.M, N), dtype=out_dtype, device=X.device)
     ldy = _rowmajor(out, "out")
+    bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
+    if fused:
+        _check(lib().spmm_tvw_fused(_ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.layout, t.M, t.K, t.tile_m,
+                                    t.keep_k, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, bptr, act_code,
+                                    _stream(X.device)), "spmm_tvw_fused")
+        return out
     _check(lib().spmm_tvw(_ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.layout, t.M, t.K, t.tile_m, t.keep_k,
                           _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tvw")
     return out
@@ -428,8 +438,8 @@ def tvw_var_compress(W, total_keep: int | None = None) -> CompressedTVWVar:
     return CompressedTVWVar(offsets, order, kept, values, meta, M, K, total_keep)
 
 
-def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None):
-    """Y = W X for a per-tile-keep TVW matrix; X bf16 [K, N]."""
+def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None, bias=None, act="none"):
+    """Y = act(W X + bias) for a per-tile-keep TVW matrix; X bf16 [K, N]."""
     torch = _torch()
     out_dtype = out_dtype or torch.bfloat16
     _require_cuda(X, "X")
@@ -442,6 +452,12 @@ def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None):
     if out is None:
         out = torch.empty((t.M, N), dtype=out_dtype, device=X.device)
     ldy = _rowmajor(out, "out")
+    bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
+    if fused:
+        _check(lib().spmm_tvw_var_fused(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.values), _ptr(t.meta),
+                                        t.M, t.K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, bptr,
+                                        act_code, _stream(X.device)), "spmm_tvw_var_fused")
+        return out
     _check(lib().spmm_tvw_var(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.M,
                               t.K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)),
            "spmm_tvw_var")

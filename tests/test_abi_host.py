@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 31
+    assert len(syms) == len(set(syms)) == 33
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -149,6 +149,16 @@ def test_tvw_validation(L):
     g = L.spmm_tvw
     assert g(FAKE, FAKE, FAKE, 1, 256, 256, 64, 128, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_UNSUPPORTED
     assert g(FAKE, FAKE, FAKE, 0, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL) == p24.P24_ERR_LAYOUT
+    h = L.spmm_tvw_fused      # spmm_tvw's rules plus the epilogue's
+    assert h(FAKE, FAKE, FAKE, 1, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL, 3, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert h(FAKE, FAKE, FAKE, 1, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, MISALIGNED, 1, NUL) \
+        == p24.P24_ERR_ALIGN
+    assert h(FAKE, FAKE, FAKE, 0, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_LAYOUT
+    assert h(NUL, NUL, NUL, 1, 0, 256, 128, 128, NUL, 64, 64, NUL, 0, 64, NUL, 2, NUL) == p24.P24_OK
+    v = L.spmm_tvw_var_fused
+    assert v(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL, -1, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert v(FAKE, NUL, FAKE, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_NULL
+    assert v(NUL, NUL, NUL, NUL, NUL, 0, 256, NUL, 64, 64, NUL, 0, 64, NUL, 1, NUL) == p24.P24_OK
 
 
 def test_tvw_var_validation(L):

@@ -118,3 +118,41 @@ def test_gelu_activation_sweep():
         assert not bnd.any()
         ok, worst = O.check_fused(y_host(Y), y_ref, z_ref, bnd, ACTS[act], "f32")
         assert ok, f"{act}: worst err/tol {worst}"
+
+
+@pytest.mark.parametrize("var", [False, True])
+@pytest.mark.parametrize("act", ["relu", "gelu", "none"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_tvw_fused_parity(var, act, out):
+    """The TVW products with the fused epilogue (fixed keep and per-tile keep), ragged M and N."""
+    need_gpu()
+    M, K, N = 300, 512, 1000
+    print(f"[fused] tvw var={var} {act} {out}", flush=True)
+    W = workloads.random_matrix((M, K), seed=41, sigma=0.05)
+    W[:128] *= 1.2
+    Xb = workloads.random_bf16((K, N), seed=42)
+    bias = np.random.default_rng(43).standard_normal(M).astype(np.float32)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    b = torch.from_numpy(bias).cuda()
+    X = bf16_dev(Xb)
+    if var:
+        t = p24.tvw_var_compress(f32_dev(W), total_keep=3 * 256)
+        Y = p24.spmm_tvw_var(t, X, out_dtype=dt, bias=b, act=act)
+        Yp = p24.spmm_tvw_var(t, X, out_dtype=dt)
+        counts = O.tvw_var_counts(W, 128, 3 * 256)
+        Wd = O.tvw_var_decompress(O.tvw_var_compress(W, 128, counts), M, K, 128)
+    else:
+        t = p24.tvw_compress(f32_dev(W), tile_m=128, keep_k=256)
+        Y = p24.spmm_tvw(t, X, out_dtype=dt, bias=b, act=act)
+        Yp = p24.spmm_tvw(t, X, out_dtype=dt)
+        kept, v, m = O.tvw_compress(W, 128, 256)
+        Wd = O.tvw_decompress(kept, v, m, M, K, 128)
+    torch.cuda.synchronize()
+    y_ref, z_ref, bnd = O.fused_ref(Wd, Xb, bias, ACTS[act], rows=None)
+    ok, worst = O.check_fused(y_host(Y), y_ref, z_ref, bnd, ACTS[act], out)
+    assert ok, f"worst err/tol {worst}"
+    # no bias and no activation: the fused kernel reproduces the plain product bit for bit
+    Yn = (p24.spmm_tvw_var(t, X, out_dtype=dt, bias=torch.zeros_like(b)) if var
+          else p24.spmm_tvw(t, X, out_dtype=dt, bias=torch.zeros_like(b)))
+    torch.cuda.synchronize()
+    assert torch.equal(Yn, Yp)
