@@ -223,6 +223,8 @@ def table(args):
             sets = [(p24.tvw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k), X.clone(), torch.empty_like(Y))
                     for _ in range(nsets)]
             rec["spmm_tvw_cold_us"] = timeit_rot([lambda s=s_: p24.spmm_tvw(s[0], s[1], out=s[2]) for s_ in sets])
+            bt = torch.randn(wl.M, device=dev, dtype=torch.float32) * 0.1
+            rec["spmm_tvw_fused_gelu_us"] = timeit(lambda: p24.spmm_tvw(t, X, out=Y, bias=bt, act="gelu"))
             tw = p24.tw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
             rec["spmm_tw_us"] = timeit(lambda: p24.spmm_tw(tw, X, out=Y))
             # the page's comparison patterns at TVW's density (a quarter of the weights):
