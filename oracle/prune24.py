@@ -1,4 +1,5 @@
-"""CPU oracle for 2:4 structured-sparse GEMM and tile-vector-wise (TVW) sparsity.
+"""CPU oracle for 2:4 structured-sparse GEMM, tile-wise (TW) and tile-vector-wise
+(TVW) sparsity, masked fine-tuning and the block-wise / unstructured comparisons.
 
 TEST INFRASTRUCTURE ONLY.  Nothing in the product path imports, calls or links
 this module: only ``tests/``, ``__graft_entry__.smoke()`` and the
@@ -18,7 +19,7 @@ Sources (the method's definition):
     Figure 3: tile-wise (TW) sparsity removes whole reduction-axis rows per GEMM
     tile in global memory, and TVW applies 2:4 on top of it inside the tile.
 
-Readings where the pages are silent (each one is listed in the design notes):
+Readings where the pages are silent:
   * criterion: magnitude; order: key descending, index ascending (ties go to
     the lower index); key = IEEE bit pattern with the sign bit cleared, read as
     an unsigned integer (monotone in |w|, -0 == +0, NaN above +Inf).
@@ -39,6 +40,14 @@ Readings where the pages are silent (each one is listed in the design notes):
     2^-8 * (|y_ref| + 1e-3 * (|W|.|X|)).
   * fused epilogue: y = act(W X + b), b per output row, act none / ReLU / exact
     GELU (see ``fused_ref``).
+  * per-tile keep counts: one global ranking of every (tile, column) score,
+    a tile's share of the top total_keep rounded to a multiple of 64 and
+    clamped to [64, K] (see ``tvw_var_counts``); TW alone keeps the same
+    columns without the 2:4 step.
+  * masked fine-tuning: unselected weights become +0, selected ones keep
+    their bits (see ``mask_apply``).
+  * block-wise: 128 x 64 blocks, a fixed count per tile; unstructured: one
+    global magnitude cut, CSR (see ``bw_select``, ``ew_compress``).
 
 Parity pins for every function here live in ``tests/test_oracle_*.py``.
 """
