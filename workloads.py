@@ -66,6 +66,12 @@ WORKLOADS = {
                     math.sqrt(2.0 / 2304), "halfnormal", "bf16"),
     "c4": Workload("c4", "large 2:4 SpMM 8192x8192 . 8192x8192", 8192, 8192, 8192, 0.02,
                    "normal", "bf16"),
+    # one GPU's share of c4 when the product is split over 8 GPUs (no exchange step):
+    # by tokens (N) or by output rows (M)
+    "c4n8": Workload("c4n8", "8192^3 split 8 ways by tokens: 8192x8192 . 8192x1024", 8192, 8192, 1024, 0.02,
+                     "normal", "bf16"),
+    "c4m8": Workload("c4m8", "8192^3 split 8 ways by output rows: 1024x8192 . 8192x8192", 1024, 8192, 8192, 0.02,
+                     "normal", "bf16"),
     "c5": Workload("c5", "TVW 4096x4096 . 4096x4096, tile 128 rows, keep 2048 columns", 4096, 4096,
                    4096, 0.02, "normal", "bf16", tile_m=128, keep_k=2048),
     "c5v": Workload("c5v", "TVW with per-tile keep counts 4096x4096 . 4096x4096, tile 128 rows, "
