@@ -820,13 +820,14 @@ static int64_t nblocks_for(Tile t, int64_t M, int64_t N) {
   return ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
 }
 
-// The largest of 256x256, 128x128 and 64x128 that still gives at least 160
-// blocks (five eighths of the CUs), else the one with the most blocks.  The
-// big tile moves the fewest bytes per MFMA, so it wins even with a quarter of
-// the CUs idle; below that the smaller tiles, which also fit two blocks per CU,
-// win on parallelism.  128x256 (one wave per SIMD) never beat 128x128 on the
-// measured shapes and is only taken by request.  P24_TILE=<256x256|128x256|
-// 128x128|64x128> overrides (measurement aid).
+// The first of 256x256, 128x256, 128x128 and 64x128 that still gives at
+// least 160 blocks (five eighths of the CUs), else the one with the most
+// blocks.  The big tiles move the fewest bytes per MFMA, so they win even with
+// a quarter of the CUs idle; below that the smaller tiles, which also fit two
+// blocks per CU, win on parallelism.  Measured: 256x256 on the 8192^3 and
+// BERT FFN shapes, 128x256 on one GPU's share of 8192^3 split 8 ways (256
+// blocks; 7 % over 128x128), 128x128 and 64x128 on the ResNet-50 shapes.
+// P24_TILE=<256x256|128x256|128x128|64x128> overrides (measurement aid).
 static Tile choose_tile(int64_t M, int64_t N) {
   if (const char* e = getenv("P24_TILE")) {
     const std::string s(e);
@@ -835,7 +836,7 @@ static Tile choose_tile(int64_t M, int64_t N) {
     if (s == "128x128") return Tile::T128x128;
     if (s == "64x128") return Tile::T64x128;
   }
-  const Tile order[] = {Tile::T256x256, Tile::T128x128, Tile::T64x128};
+  const Tile order[] = {Tile::T256x256, Tile::T128x256, Tile::T128x128, Tile::T64x128};
   for (Tile t : order)
     if (nblocks_for(t, M, N) >= 160) return t;
   return Tile::T64x128;
