@@ -84,7 +84,7 @@ def test_integer_exact_and_identity():
     assert np.array_equal(y_host(Y), O.bf16_to_f64(O.decompress_24(v, m, 128)))
 
 
-@pytest.mark.parametrize("key", ["c1", "c2", "c3a", "c3b", "c4"])
+@pytest.mark.parametrize("key", ["c1", "c2", "c3a", "c3b", "c4", "c4n8", "c4m8"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
 def test_workloads_full_size(key, out):
     need_gpu()
