@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--workloads", default=None, help="--table: comma-separated workload keys (default all)")
     ap.add_argument("--only", choices=["spmm", "xt", "decomp", "dense", "compress", "tvw", "copy"], default=None)
     ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the clock leg (GPU clocks read with amd-smi during back-to-back spmm24 launches)")
+    ap.add_argument("--clock-sampler", default=None, help=argparse.SUPPRESS)   # internal: helper process mode
     ap.add_argument("--table", action="store_true",
                     help="instead of the headline line, time every workload (spmm24, spmm24_xt, dense) and "
                          "print one JSON line per workload")
@@ -127,6 +130,75 @@ def cpu_baseline(wl, W, Xb):
         "sample": f"{rows} of {wl.M} output rows of {wl.key}: oracle prune+compress+decompress of those "
                   f"rows and fp64 GEMM + |W||X| bound against the full X ({dt:.1f} s)",
     }
+
+
+def parse_gfx_clocks(text):
+    """Graphics clocks (MHz) of every XCD of GPU 0 from `amd-smi metric --clock --json`."""
+    d = json.loads(text)
+    gpus = d.get("gpu_data", []) if isinstance(d, dict) else d
+    for g in gpus:
+        if isinstance(g, dict) and g.get("gpu", 0) == 0 and isinstance(g.get("clock"), dict):
+            out = []
+            for k, v in sorted(g["clock"].items()):
+                if k.startswith("gfx_") and isinstance(v, dict):
+                    val = v.get("clk", {}).get("value") if isinstance(v.get("clk"), dict) else None
+                    if isinstance(val, (int, float)):
+                        out.append(float(val))
+            return out
+    return []
+
+
+def clock_sampler(path):
+    """Helper process: append one line per amd-smi reading to `path` (start and end of the
+    reading as unix times, then the MHz of each XCD) until the parent process exits.  It is
+    started before the parent touches the GPU and never uses the GPU itself."""
+    import subprocess
+    parent = os.getppid()
+    with open(path, "a") as f:
+        while os.getppid() == parent:
+            t0 = time.time()
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                mhz = parse_gfx_clocks(r.stdout) if r.returncode == 0 else []
+            except Exception:
+                mhz = []
+            if mhz:
+                f.write(f"{t0:.3f} {time.time():.3f} " + " ".join(f"{m:.0f}" for m in mhz) + "\n")
+                f.flush()
+            time.sleep(0.1)
+
+
+def start_clock_sampler():
+    """(process, sample file) of a clock sampler, or (None, None) without amd-smi."""
+    import shutil
+    import subprocess
+    import tempfile
+    if not shutil.which("amd-smi"):
+        return None, None
+    fd, path = tempfile.mkstemp(prefix="p24_clk_", suffix=".txt")
+    os.close(fd)
+    proc = subprocess.Popen([sys.executable, os.path.abspath(__file__), "--clock-sampler", path],
+                            stdout=subprocess.DEVNULL, stderr=subprocess.DEVNULL)
+    return proc, path
+
+
+def read_clock_samples(path, t_lo, t_hi):
+    """Per-reading mean XCD clock (MHz) of the readings that lie wholly inside [t_lo, t_hi]."""
+    out = []
+    try:
+        with open(path) as f:
+            for line in f:
+                parts = line.split()
+                if len(parts) < 3:
+                    continue
+                a, b = float(parts[0]), float(parts[1])
+                if a >= t_lo and b <= t_hi:
+                    mhz = [float(x) for x in parts[2:]]
+                    out.append(sum(mhz) / len(mhz))
+    except OSError:
+        pass
+    return out
 
 
 def measured_traffic():
@@ -279,6 +351,8 @@ def table(args):
 
 def main():
     args = parse()
+    if args.clock_sampler:
+        return clock_sampler(args.clock_sampler)
     if args.table:
         return table(args)
     if args.gpus != 1:
@@ -286,6 +360,10 @@ def main():
               "across GPUs the product would split by tokens (N) or by output rows (M) with no exchange step",
               file=sys.stderr)
         sys.exit(2)
+    # the clock sampler starts before this process touches the GPU
+    clk_proc, clk_path = (None, None)
+    if args.only is None and not args.no_clock:
+        clk_proc, clk_path = start_clock_sampler()
     import numpy as np
     import torch
 
@@ -355,6 +433,31 @@ def main():
             ev_cold += event_times_ms(torch, alt[i % 2], 1)
         rows["spmm24_cold_us_mean"] = sum(ev_cold) / len(ev_cold) * 1e3
         del c2, X2, Y2, alt
+    clock = None
+    if clk_proc is not None:
+        # about 4 s of back-to-back launches while the sampler reads the XCD clocks;
+        # readings from the first half second (clock ramp) are left out
+        t_a = time.time()
+        while time.time() - t_a < 4.0:
+            for _ in range(200):
+                step()
+            torch.cuda.synchronize()
+        t_b = time.time()
+        mhz = read_clock_samples(clk_path, t_a + 0.5, t_b)
+        clk_proc.terminate()
+        try:
+            clk_proc.wait(timeout=10)
+        except Exception:
+            clk_proc.kill()
+        try:
+            os.remove(clk_path)
+        except OSError:
+            pass
+        if mhz:
+            clock = {"sclk_mhz_mean": round(sum(mhz) / len(mhz), 1), "sclk_mhz_min": min(mhz),
+                     "sclk_mhz_max": max(mhz), "readings": len(mhz), "published_mhz": 2400.0,
+                     "source": "amd-smi metric --clock: mean of the XCD graphics clocks, read during "
+                               "4 s of back-to-back spmm24 launches on the headline workload"}
     if args.only == "spmm":
         print(json.dumps(rows))
         return
@@ -499,6 +602,11 @@ def main():
         "speedup_vs_dense": round(rows["speedup_vs_dense"], 3),
         "rows": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rows.items()},
     }
+    if clock is not None:
+        # the published peak assumes 2.4 GHz; the same launch against the peak at the measured clock
+        clock["frac_at_measured_clock"] = round(out["roofline"]["frac"] * clock["published_mhz"]
+                                                / clock["sclk_mhz_mean"], 4)
+    out["clock"] = clock
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, W, Xb)
     print(json.dumps(out))
