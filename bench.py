@@ -169,12 +169,22 @@ def clock_sampler(path):
             time.sleep(0.1)
 
 
+def under_profiler(env=None):
+    """True when a profiler's library is preloaded (`env` defaults to this process's
+    environment).  Such a library may initialise the GPU before main() runs, and no process
+    that has touched the GPU may start another program."""
+    env = os.environ if env is None else env
+    pre = env.get("LD_PRELOAD", "")
+    return "rocprof" in pre or "roctracer" in pre or any(k.startswith("ROCPROF") for k in env)
+
+
 def start_clock_sampler():
-    """(process, sample file) of a clock sampler, or (None, None) without amd-smi."""
+    """(process, sample file) of a clock sampler, or (None, None) without amd-smi or
+    under a profiler."""
     import shutil
     import subprocess
     import tempfile
-    if not shutil.which("amd-smi"):
+    if under_profiler() or not shutil.which("amd-smi"):
         return None, None
     fd, path = tempfile.mkstemp(prefix="p24_clk_", suffix=".txt")
     os.close(fd)

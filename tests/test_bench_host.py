@@ -39,3 +39,10 @@ def test_read_clock_samples_keeps_readings_inside_the_window(tmp_path):
                  "garbage\n")
     assert bench.read_clock_samples(str(p), 10.5, 14.0) == [1900.0, 1900.0]
     assert bench.read_clock_samples(str(tmp_path / "missing.txt"), 0, 1e9) == []
+
+
+def test_under_profiler_detects_the_profiler_environment():
+    assert bench.under_profiler({"LD_PRELOAD": "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so"})
+    assert bench.under_profiler({"ROCPROF_KERNEL_TRACE": "1"})
+    assert not bench.under_profiler({"LD_PRELOAD": "/usr/lib/libother.so", "PATH": "/usr/bin"})
+    assert not bench.under_profiler({})
