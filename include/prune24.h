@@ -29,6 +29,10 @@
  *     nothing is enqueued.  P24_ERR_HIP means a launch failed.  M == 0 or
  *     N == 0 is a valid no-op.
  *   - The library is stateless and thread-safe.
+ *   - It links the HIP runtime by soname (libamdhip64.so.7) and uses the copy
+ *     the process has already loaded.  A process holds one copy: when another
+ *     component opens its own copy by path (PyTorch does), load that component
+ *     first.
  *
  * Layouts of a compressed matrix (values are bf16, metadata uint32)
  *   P24_LAYOUT_CANONICAL

@@ -115,6 +115,13 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
                                "or python structured_sparse_gemm_prune24_amd/build.py")
+        # One HIP runtime per process: torch opens its own copy by path, so torch is
+        # loaded first and the library, which names the runtime by soname, binds to
+        # that copy instead of bringing a second one.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in _SIGNATURES.items():
             f = getattr(L, name)
