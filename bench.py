@@ -309,6 +309,7 @@ def table(args):
             rec["spmm_tvw_fused_gelu_us"] = timeit(lambda: p24.spmm_tvw(t, X, out=Y, bias=bt, act="gelu"))
             tw = p24.tw_compress(W, tile_m=wl.tile_m, keep_k=wl.keep_k)
             rec["spmm_tw_us"] = timeit(lambda: p24.spmm_tw(tw, X, out=Y))
+            rec["spmm_tw_fused_gelu_us"] = timeit(lambda: p24.spmm_tw(tw, X, out=Y, bias=bt, act="gelu"))
             # the page's comparison patterns at TVW's density (a quarter of the weights):
             # TW keeping a quarter of the columns, block-wise 128 x 64 blocks, unstructured
             d4 = wl.K // 4

@@ -359,6 +359,23 @@ P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, con
                                int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream);
 
 /*
+ * spmm_tw_fused / spmm_tw_var_fused -- spmm_tw / spmm_tw_var with the epilogue
+ *   of spmm24_fused: Y = act(W X + bias), bias fp32 [M] (one value per output
+ *   row, nullptr for none, 4 B aligned), act P24_ACT_NONE / _RELU / _GELU
+ *   (else P24_ERR_UNSUPPORTED); other arguments and rules as for the plain
+ *   calls (kernel fusion, "Accelerating Sparse DNNs Based on Tiled GEMM",
+ *   TL;DR).
+ */
+P24_API p24_status spmm_tw_fused(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,
+                                 int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
+                                 int32_t y_dtype, int64_t ldy, const float* bias, int32_t act,
+                                 void* stream);
+P24_API p24_status spmm_tw_var_fused(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                                     const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
+                                     int64_t N, void* Y, int32_t y_dtype, int64_t ldy, const float* bias,
+                                     int32_t act, void* stream);
+
+/*
  * Comparison patterns ("Accelerating Sparse DNNs Based on Tiled GEMM",
  * Abstract: TVW against block and unstructured sparsity; Figure 5 names the
  * element-wise and block-wise patterns).

@@ -82,6 +82,10 @@ _SIGNATURES = {
                                  _c_size, _c_vp]),
     "spmm_tw_var": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
                              _c_i64, _c_vp]),
+    "spmm_tw_fused": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32,
+                               _c_i64, _c_vp, _c_i32, _c_vp]),
+    "spmm_tw_var_fused": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64, _c_vp,
+                                   _c_i32, _c_i64, _c_vp, _c_i32, _c_vp]),
     "bw_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
     "bw_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp, _c_size, _c_vp]),
     "ew_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
@@ -504,9 +508,15 @@ def tw_compress(W, tile_m: int = 128, keep_k: int | None = None) -> CompressedTW
     return CompressedTW(kept, Wp, M, K, tile_m, keep_k)
 
 
-def spmm_tw(t: CompressedTW, X, out_dtype=None, out=None):
-    """Y = W X for a TW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
+def spmm_tw(t: CompressedTW, X, out_dtype=None, out=None, bias=None, act="none"):
+    """Y = act(W X + bias) for a TW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
     ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
+    if fused:
+        _check(lib().spmm_tw_fused(_ptr(t.kept), _ptr(t.Wp), t.M, t.K, t.tile_m, t.keep_k, _ptr(X), ldx, N,
+                                   _ptr(out), _out_code(out.dtype), ldy, bptr, act_code, _stream(X.device)),
+               "spmm_tw_fused")
+        return out
     _check(lib().spmm_tw(_ptr(t.kept), _ptr(t.Wp), t.M, t.K, t.tile_m, t.keep_k, _ptr(X), ldx, N, _ptr(out),
                          _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tw")
     return out
@@ -535,9 +545,15 @@ def tw_var_compress(W, total_keep: int | None = None) -> CompressedTWVar:
     return CompressedTWVar(offsets, order, kept, Wp, M, K, total_keep)
 
 
-def spmm_tw_var(t: CompressedTWVar, X, out_dtype=None, out=None):
-    """Y = W X for a per-tile-keep TW matrix; X bf16 [K, N]."""
+def spmm_tw_var(t: CompressedTWVar, X, out_dtype=None, out=None, bias=None, act="none"):
+    """Y = act(W X + bias) for a per-tile-keep TW matrix; X bf16 [K, N]."""
     ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
+    if fused:
+        _check(lib().spmm_tw_var_fused(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.Wp), t.M, t.K,
+                                       _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, bptr, act_code,
+                                       _stream(X.device)), "spmm_tw_var_fused")
+        return out
     _check(lib().spmm_tw_var(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.Wp), t.M, t.K, _ptr(X), ldx, N,
                              _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tw_var")
     return out

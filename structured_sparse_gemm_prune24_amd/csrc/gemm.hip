@@ -1042,14 +1042,23 @@ extern "C" P24_API p24_status spmm_tvw_var_fused(const int64_t* offsets, const i
 
 // TW alone: the dense MFMA on each tile's packed kept columns, X rows gathered
 // by the tile's kept list; one block row per 128-row slice, 8 waves (2 x 4).
-extern "C" P24_API p24_status spmm_tw(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,
-                                      int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
-                                      int32_t y_dtype, int64_t ldy, void* stream) {
+// The fused variants add the bias + activation epilogue.
+template <int XM>
+static p24_status launch_tw(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
+  if (!fused) return launch_cfg<128, 256, 2, 4, A_DENSE, XM, 0>(a, y_dtype, st);
+  if (act == P24_ACT_GELU) return launch_cfg<128, 256, 2, 4, A_DENSE, XM, 2>(a, y_dtype, st);
+  return launch_cfg<128, 256, 2, 4, A_DENSE, XM, 1>(a, y_dtype, st);
+}
+
+static p24_status tw_fixed(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,
+                           int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
+                           int64_t ldy, bool fused, const float* bias, int32_t act, void* stream) {
   p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
   if (s != P24_OK) return s;
   if (M < 0 || K <= 0 || tile_m <= 0 || keep_k <= 0 || keep_k > K || M > INT32_MAX || K > INT32_MAX)
     return P24_ERR_SHAPE;
   if (tile_m % 128 || keep_k % 64) return P24_ERR_UNSUPPORTED;
+  if (fused && (s = check_epilogue(bias, act)) != P24_OK) return s;
   if (M == 0 || N == 0) return P24_OK;
   if ((uint64_t)K * ldx * 2 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;   // gathered rows: all of X in a 32-bit range
   if (!kept || !Wp) return P24_ERR_NULL;
@@ -1068,16 +1077,19 @@ extern "C" P24_API p24_status spmm_tw(const int32_t* kept, const void* Wp, int64
   a.Kc = (int)keep_k;
   a.Kx = (int)K;
   a.tile_m = (int)tile_m;
-  return launch_cfg<128, 256, 2, 4, A_DENSE, X_KN_GATHER>(a, y_dtype, (hipStream_t)stream);
+  a.bias = bias;
+  a.act = act;
+  return launch_tw<X_KN_GATHER>(a, y_dtype, fused, act, (hipStream_t)stream);
 }
 
-extern "C" P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept,
-                                          const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
-                                          int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream) {
+static p24_status tw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept, const void* Wp,
+                         int64_t M, int64_t K, const void* X, int64_t ldx, int64_t N, void* Y, int32_t y_dtype,
+                         int64_t ldy, bool fused, const float* bias, int32_t act, void* stream) {
   p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
   if (s != P24_OK) return s;
   if (M < 0 || K <= 0 || M > INT32_MAX || K > INT32_MAX) return P24_ERR_SHAPE;
   if (K % 64) return P24_ERR_UNSUPPORTED;
+  if (fused && (s = check_epilogue(bias, act)) != P24_OK) return s;
   if (M == 0 || N == 0) return P24_OK;
   if ((uint64_t)K * ldx * 2 >= (1ull << 32)) return P24_ERR_UNSUPPORTED;
   if (!offsets || !order || !kept || !Wp) return P24_ERR_NULL;
@@ -1098,7 +1110,35 @@ extern "C" P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t*
   a.Kc = 0;            // per tile, from the offsets
   a.Kx = (int)K;
   a.tile_m = 128;
-  return launch_cfg<128, 256, 2, 4, A_DENSE, X_KN_GATHER_VAR>(a, y_dtype, (hipStream_t)stream);
+  a.bias = bias;
+  a.act = act;
+  return launch_tw<X_KN_GATHER_VAR>(a, y_dtype, fused, act, (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status spmm_tw(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,
+                                      int64_t keep_k, const void* X, int64_t ldx, int64_t N, void* Y,
+                                      int32_t y_dtype, int64_t ldy, void* stream) {
+  return tw_fixed(kept, Wp, M, K, tile_m, keep_k, X, ldx, N, Y, y_dtype, ldy, false, nullptr, P24_ACT_NONE, stream);
+}
+
+extern "C" P24_API p24_status spmm_tw_fused(const int32_t* kept, const void* Wp, int64_t M, int64_t K,
+                                            int64_t tile_m, int64_t keep_k, const void* X, int64_t ldx, int64_t N,
+                                            void* Y, int32_t y_dtype, int64_t ldy, const float* bias, int32_t act,
+                                            void* stream) {
+  return tw_fixed(kept, Wp, M, K, tile_m, keep_k, X, ldx, N, Y, y_dtype, ldy, true, bias, act, stream);
+}
+
+extern "C" P24_API p24_status spmm_tw_var(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                                          const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
+                                          int64_t N, void* Y, int32_t y_dtype, int64_t ldy, void* stream) {
+  return tw_var(offsets, order, kept, Wp, M, K, X, ldx, N, Y, y_dtype, ldy, false, nullptr, P24_ACT_NONE, stream);
+}
+
+extern "C" P24_API p24_status spmm_tw_var_fused(const int64_t* offsets, const int32_t* order, const int32_t* kept,
+                                                const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,
+                                                int64_t N, void* Y, int32_t y_dtype, int64_t ldy, const float* bias,
+                                                int32_t act, void* stream) {
+  return tw_var(offsets, order, kept, Wp, M, K, X, ldx, N, Y, y_dtype, ldy, true, bias, act, stream);
 }
 
 extern "C" P24_API p24_status gemm_bf16(const void* Wp, int64_t M, int64_t K, const void* X, int64_t ldx,

@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 33
+    assert len(syms) == len(set(syms)) == 35
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -159,6 +159,19 @@ def test_tvw_validation(L):
     assert v(FAKE, FAKE, FAKE, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL, -1, NUL) == p24.P24_ERR_UNSUPPORTED
     assert v(FAKE, NUL, FAKE, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_NULL
     assert v(NUL, NUL, NUL, NUL, NUL, 0, 256, NUL, 64, 64, NUL, 0, 64, NUL, 1, NUL) == p24.P24_OK
+    w = L.spmm_tw_fused       # spmm_tw's rules plus the epilogue's
+    assert w(FAKE, FAKE, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL, 3, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert w(FAKE, FAKE, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, MISALIGNED, 1, NUL) == p24.P24_ERR_ALIGN
+    assert w(FAKE, FAKE, 256, 256, 64, 128, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert w(FAKE, FAKE, 256, 256, 128, 300, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_SHAPE
+    assert w(NUL, FAKE, 256, 256, 128, 128, FAKE, 64, 64, FAKE, 0, 64, NUL, 2, NUL) == p24.P24_ERR_NULL
+    assert w(NUL, NUL, 0, 256, 128, 128, NUL, 64, 64, NUL, 0, 64, NUL, 2, NUL) == p24.P24_OK
+    u = L.spmm_tw_var_fused
+    assert u(FAKE, FAKE, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL, 7, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert u(FAKE, FAKE, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, MISALIGNED, 2, NUL) == p24.P24_ERR_ALIGN
+    assert u(FAKE, FAKE, FAKE, FAKE, 256, 96, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert u(FAKE, NUL, FAKE, FAKE, 256, 256, FAKE, 64, 64, FAKE, 0, 64, NUL, 1, NUL) == p24.P24_ERR_NULL
+    assert u(NUL, NUL, NUL, NUL, 0, 256, NUL, 64, 64, NUL, 0, 64, NUL, 1, NUL) == p24.P24_OK
 
 
 def test_tvw_var_validation(L):

@@ -1,9 +1,10 @@
-"""GPU parity for spmm24_fused: Y = act(W X + b) with the bias add and activation
-run in the sparse-MFMA kernel's epilogue.
+"""GPU parity for the fused products: Y = act(W X + b) with the bias add and
+activation run in the GEMM kernel's epilogue (spmm24 / spmm24_xt, the TVW
+products, and TW alone on the dense MFMA).
 
 Every result is checked elementwise against the oracle's fp64 act(W X + b)
 within ``oracle.prune24.fused_tolerance``; with no bias and no activation the
-fused call must reproduce spmm24 / spmm24_xt bit for bit.
+fused call must reproduce the plain product bit for bit.
 """
 import numpy as np
 import pytest
@@ -154,5 +155,44 @@ def test_tvw_fused_parity(var, act, out):
     # no bias and no activation: the fused kernel reproduces the plain product bit for bit
     Yn = (p24.spmm_tvw_var(t, X, out_dtype=dt, bias=torch.zeros_like(b)) if var
           else p24.spmm_tvw(t, X, out_dtype=dt, bias=torch.zeros_like(b)))
+    torch.cuda.synchronize()
+    assert torch.equal(Yn, Yp)
+
+
+@pytest.mark.parametrize("var", [False, True])
+@pytest.mark.parametrize("act", ["relu", "gelu", "none"])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_tw_fused_parity(var, act, out):
+    """TW alone (dense MFMA on the kept columns) with the fused epilogue, fixed and per-tile
+    keep, ragged M and N."""
+    need_gpu()
+    M, K, N = 300, 512, 1000
+    print(f"[fused] tw var={var} {act} {out}", flush=True)
+    W = workloads.random_matrix((M, K), seed=51, sigma=0.05)
+    W[128:256] *= 1.3
+    Xb = workloads.random_bf16((K, N), seed=52)
+    bias = np.random.default_rng(53).standard_normal(M).astype(np.float32)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    b = torch.from_numpy(bias).cuda()
+    X = bf16_dev(Xb)
+    if var:
+        t = p24.tw_var_compress(f32_dev(W), total_keep=3 * 256)
+        Y = p24.spmm_tw_var(t, X, out_dtype=dt, bias=b, act=act)
+        Yp = p24.spmm_tw_var(t, X, out_dtype=dt)
+        tiles = O.tw_var_compress(W, 128, O.tvw_var_counts(W, 128, 3 * 256))
+        Wd = O.tw_decompress([k for k, _ in tiles], [w for _, w in tiles], M, K, 128)
+    else:
+        t = p24.tw_compress(f32_dev(W), tile_m=128, keep_k=256)
+        Y = p24.spmm_tw(t, X, out_dtype=dt, bias=b, act=act)
+        Yp = p24.spmm_tw(t, X, out_dtype=dt)
+        kept, Wc = O.tw_compress(W, 128, 256)
+        Wd = O.tw_decompress(list(kept), [Wc[128 * i:128 * i + 128] for i in range(kept.shape[0])], M, K, 128)
+    torch.cuda.synchronize()
+    y_ref, z_ref, bnd = O.fused_ref(Wd, Xb, bias, ACTS[act], rows=None)
+    ok, worst = O.check_fused(y_host(Y), y_ref, z_ref, bnd, ACTS[act], out)
+    assert ok, f"worst err/tol {worst}"
+    # no bias and no activation: the fused kernel reproduces the plain product bit for bit
+    Yn = (p24.spmm_tw_var(t, X, out_dtype=dt, bias=torch.zeros_like(b)) if var
+          else p24.spmm_tw(t, X, out_dtype=dt, bias=torch.zeros_like(b)))
     torch.cuda.synchronize()
     assert torch.equal(Yn, Yp)
