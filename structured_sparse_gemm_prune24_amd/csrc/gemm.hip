@@ -922,13 +922,47 @@ extern "C" P24_API p24_status spmm24(const void* values, const void* meta, int32
   return dispatch<A_SPARSE, X_KN>(a, y_dtype, (hipStream_t)stream);
 }
 
-// TVW products: one block row = one 128-row slice of a TVW tile, 8 waves
-// (2 x 4, each 64 x 64); the fused variants add the bias + activation epilogue.
+// Gathered products (TVW on the sparse MFMA, TW alone on the dense MFMA): one
+// block row = one 128-row slice of a tile, 8 waves (2 x 4); the fused variants
+// add the bias + activation epilogue.
+//
+// Block width.  With one keep count for every tile the block is 128 x 512 when
+// that grid still gives at least 160 blocks (five eighths of the CUs), else
+// 128 x 256.  The wide block moves fewer X bytes per multiply-add and halves
+// the number of blocks: on the 4096^3 TVW product (keep 2048) that is one
+// round of 256 blocks instead of two rounds of 512, measured 10 % faster, in
+// spite of holding only two 73 KiB stages.  Per-tile keep counts stay at
+// 128 x 256: their heaviest-first order needs more blocks than CUs to even out
+// the tiles (one round of 128 x 512 blocks measured 24 % slower).
+// P24_GATHER_TILE=<128x256|128x512> overrides the width of the fixed-keep
+// products (measurement and test aid).
+static bool wide_gather(int64_t M, int64_t N) {
+  if (const char* e = getenv("P24_GATHER_TILE")) {
+    const std::string s(e);
+    if (s == "128x512") return true;
+    if (s == "128x256") return false;
+  }
+  return ((M + 127) / 128) * ((N + 511) / 512) >= 160;
+}
+
+template <int AM, int XM, int BN>
+static p24_status launch_gather_bn(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
+  if (!fused) return launch_cfg<128, BN, 2, 4, AM, XM, 0>(a, y_dtype, st);
+  if (act == P24_ACT_GELU) return launch_cfg<128, BN, 2, 4, AM, XM, 2>(a, y_dtype, st);
+  return launch_cfg<128, BN, 2, 4, AM, XM, 1>(a, y_dtype, st);
+}
+
+template <int AM, int XM>
+static p24_status launch_gather(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
+  if constexpr (XM == X_KN_GATHER) {
+    if (wide_gather(a.M, a.N)) return launch_gather_bn<AM, XM, 512>(a, y_dtype, fused, act, st);
+  }
+  return launch_gather_bn<AM, XM, 256>(a, y_dtype, fused, act, st);
+}
+
 template <int XM>
 static p24_status launch_tvw(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
-  if (!fused) return launch_cfg<128, 256, 2, 4, A_SPARSE, XM, 0>(a, y_dtype, st);
-  if (act == P24_ACT_GELU) return launch_cfg<128, 256, 2, 4, A_SPARSE, XM, 2>(a, y_dtype, st);
-  return launch_cfg<128, 256, 2, 4, A_SPARSE, XM, 1>(a, y_dtype, st);
+  return launch_gather<A_SPARSE, XM>(a, y_dtype, fused, act, st);
 }
 
 static p24_status check_epilogue(const float* bias, int32_t act) {
@@ -1041,13 +1075,10 @@ extern "C" P24_API p24_status spmm_tvw_var_fused(const int64_t* offsets, const i
 }
 
 // TW alone: the dense MFMA on each tile's packed kept columns, X rows gathered
-// by the tile's kept list; one block row per 128-row slice, 8 waves (2 x 4).
-// The fused variants add the bias + activation epilogue.
+// by the tile's kept list (block shapes as for TVW above).
 template <int XM>
 static p24_status launch_tw(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
-  if (!fused) return launch_cfg<128, 256, 2, 4, A_DENSE, XM, 0>(a, y_dtype, st);
-  if (act == P24_ACT_GELU) return launch_cfg<128, 256, 2, 4, A_DENSE, XM, 2>(a, y_dtype, st);
-  return launch_cfg<128, 256, 2, 4, A_DENSE, XM, 1>(a, y_dtype, st);
+  return launch_gather<A_DENSE, XM>(a, y_dtype, fused, act, st);
 }
 
 static p24_status tw_fixed(const int32_t* kept, const void* Wp, int64_t M, int64_t K, int64_t tile_m,

@@ -121,14 +121,17 @@ def test_gelu_activation_sweep():
         assert ok, f"{act}: worst err/tol {worst}"
 
 
-@pytest.mark.parametrize("var", [False, True])
+@pytest.mark.parametrize("var,tile", [(False, "128x256"), (False, "128x512"), (True, None)])
 @pytest.mark.parametrize("act", ["relu", "gelu", "none"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_tvw_fused_parity(var, act, out):
-    """The TVW products with the fused epilogue (fixed keep and per-tile keep), ragged M and N."""
+def test_tvw_fused_parity(var, tile, act, out, monkeypatch):
+    """The TVW products with the fused epilogue (fixed keep at both block widths, and
+    per-tile keep), ragged M and N."""
     need_gpu()
+    if tile:
+        monkeypatch.setenv("P24_GATHER_TILE", tile)
     M, K, N = 300, 512, 1000
-    print(f"[fused] tvw var={var} {act} {out}", flush=True)
+    print(f"[fused] tvw var={var} tile={tile} {act} {out}", flush=True)
     W = workloads.random_matrix((M, K), seed=41, sigma=0.05)
     W[:128] *= 1.2
     Xb = workloads.random_bf16((K, N), seed=42)
@@ -159,15 +162,17 @@ def test_tvw_fused_parity(var, act, out):
     assert torch.equal(Yn, Yp)
 
 
-@pytest.mark.parametrize("var", [False, True])
+@pytest.mark.parametrize("var,tile", [(False, "128x256"), (False, "128x512"), (True, None)])
 @pytest.mark.parametrize("act", ["relu", "gelu", "none"])
 @pytest.mark.parametrize("out", ["f32", "bf16"])
-def test_tw_fused_parity(var, act, out):
-    """TW alone (dense MFMA on the kept columns) with the fused epilogue, fixed and per-tile
-    keep, ragged M and N."""
+def test_tw_fused_parity(var, tile, act, out, monkeypatch):
+    """TW alone (dense MFMA on the kept columns) with the fused epilogue, fixed keep at both
+    block widths and per-tile keep, ragged M and N."""
     need_gpu()
+    if tile:
+        monkeypatch.setenv("P24_GATHER_TILE", tile)
     M, K, N = 300, 512, 1000
-    print(f"[fused] tw var={var} {act} {out}", flush=True)
+    print(f"[fused] tw var={var} tile={tile} {act} {out}", flush=True)
     W = workloads.random_matrix((M, K), seed=51, sigma=0.05)
     W[128:256] *= 1.3
     Xb = workloads.random_bf16((K, N), seed=52)

@@ -86,9 +86,15 @@ def test_c5_full():
         assert ok, worst
 
 
-@pytest.mark.parametrize("M,K,N,keep", [(256, 256, 200, 128), (384, 512, 1000, 256), (300, 256, 72, 128)])
-def test_spmm_tvw_small(M, K, N, keep):
+@pytest.mark.parametrize("M,K,N,keep", [(256, 256, 200, 128), (384, 512, 1000, 256), (300, 256, 72, 128),
+                                         (256, 256, 1096, 128)])
+@pytest.mark.parametrize("tile", ["128x256", "128x512"])
+def test_spmm_tvw_small(M, K, N, keep, tile, monkeypatch):
+    """Both block widths of the fixed-keep gathered product (the width is forced; by default
+    only grids of at least 160 wide blocks take 128 x 512), ragged N included."""
     need_gpu()
+    monkeypatch.setenv("P24_GATHER_TILE", tile)
+    print(f"[tvw] spmm M={M} K={K} N={N} keep={keep} tile={tile}", flush=True)
     W = workloads.random_matrix((M, K), seed=N + keep, sigma=0.05)
     Xb = workloads.random_bf16((K, N), seed=N)
     t = p24.tvw_compress(f32_dev(W), tile_m=128, keep_k=keep)

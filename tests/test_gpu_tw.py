@@ -58,9 +58,13 @@ def test_tw_compress(M, K, tile, keep):
     _compare_fixed(workloads.random_matrix((M, K), seed=M + K + keep, sigma=0.02), tile, keep)
 
 
-@pytest.mark.parametrize("M,K,N,keep", [(256, 256, 200, 128), (384, 512, 1000, 256), (300, 256, 72, 192)])
-def test_spmm_tw_small(M, K, N, keep):
+@pytest.mark.parametrize("M,K,N,keep", [(256, 256, 200, 128), (384, 512, 1000, 256), (300, 256, 72, 192),
+                                         (256, 256, 1096, 128)])
+@pytest.mark.parametrize("tile", ["128x256", "128x512"])
+def test_spmm_tw_small(M, K, N, keep, tile, monkeypatch):
+    """Both block widths of the fixed-keep gathered product, ragged N included."""
     need_gpu()
+    monkeypatch.setenv("P24_GATHER_TILE", tile)
     W = workloads.random_matrix((M, K), seed=N + keep, sigma=0.05)
     Xb = workloads.random_bf16((K, N), seed=N)
     t, kept, Wc = _compare_fixed(W, 128, keep)
