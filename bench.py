@@ -447,14 +447,14 @@ def main():
     clock = None
     if clk_proc is not None:
         # about 4 s of back-to-back launches while the sampler reads the XCD clocks;
-        # readings from the first half second (clock ramp) are left out
+        # readings from the first second (clock ramp) are left out
         t_a = time.time()
         while time.time() - t_a < 4.0:
             for _ in range(200):
                 step()
             torch.cuda.synchronize()
         t_b = time.time()
-        mhz = read_clock_samples(clk_path, t_a + 0.5, t_b)
+        mhz = read_clock_samples(clk_path, t_a + 1.0, t_b)
         clk_proc.terminate()
         try:
             clk_proc.wait(timeout=10)
@@ -465,10 +465,12 @@ def main():
         except OSError:
             pass
         if mhz:
-            clock = {"sclk_mhz_mean": round(sum(mhz) / len(mhz), 1), "sclk_mhz_min": min(mhz),
+            # the median: a reading taken while the clocks dip (it happens) does not move it
+            clock = {"sclk_mhz_median": round(median(mhz), 1), "sclk_mhz_min": min(mhz),
                      "sclk_mhz_max": max(mhz), "readings": len(mhz), "published_mhz": 2400.0,
-                     "source": "amd-smi metric --clock: mean of the XCD graphics clocks, read during "
-                               "4 s of back-to-back spmm24 launches on the headline workload"}
+                     "source": "amd-smi metric --clock: median over readings of the mean XCD graphics "
+                               "clock, read during 4 s of back-to-back spmm24 launches on the headline "
+                               "workload"}
     if args.only == "spmm":
         print(json.dumps(rows))
         return
@@ -616,7 +618,7 @@ def main():
     if clock is not None:
         # the published peak assumes 2.4 GHz; the same launch against the peak at the measured clock
         clock["frac_at_measured_clock"] = round(out["roofline"]["frac"] * clock["published_mhz"]
-                                                / clock["sclk_mhz_mean"], 4)
+                                                / clock["sclk_mhz_median"], 4)
     out["clock"] = clock
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, W, Xb)
