@@ -12,8 +12,8 @@ constexpr int EW_WAVES = 4;
 constexpr int EW_ROWS_PER_WAVE = 8;
 constexpr int EW_ROWS = EW_WAVES * EW_ROWS_PER_WAVE;   // W rows per block
 constexpr int EW_NB = 256;                              // columns per block: 4 per lane
-constexpr int EW_KB = 128;                              // X rows staged in LDS at a time
-constexpr int EW_ROWB = EW_NB * 2;                      // bytes per staged X row
+constexpr int EW_KB = 32;                               // X rows staged in LDS at a time
+constexpr int EW_ROWB = EW_NB * 4;                      // bytes per staged X row (fp32)
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
@@ -38,13 +38,18 @@ template <> __device__ __forceinline__ void ew_store<uint16_t>(uint16_t* p, cons
 }
 
 // One block per (32 rows of W, 256 columns of N).  The block walks K in
-// chunks of 128: the chunk X[k0 .. k0+128)[n0 .. n0+256) is staged in LDS
-// (64 KiB, rows past K and columns past N zero), then each wave takes its 8
-// rows.  For a row, 64 stored entries at a time are read one per lane; those
-// inside the chunk (columns ascending, so a prefix of the lanes) are
-// broadcast one by one, and each adds w * X[k][4 lane .. +4] from LDS to the
-// lane's fp32 accumulators, in column order.  Every X element is read from
-// L2 once per block instead of once per stored entry.
+// chunks of 32: the chunk X[k0 .. k0+32)[n0 .. n0+256) is staged in LDS as
+// fp32 (32 KiB, rows past K and columns past N zero; converted once per
+// element here instead of once per stored entry below), then each wave takes
+// its 8 rows.  The small chunk leaves room for four blocks per CU, whose
+// waves hide each other's LDS and lane-broadcast latencies (64 KiB chunks, two
+// blocks per CU, measured 17 % slower).  For a row, 64 stored entries at a time are read one per lane;
+// those inside the chunk (columns ascending, so a prefix of the lanes) are
+// broadcast one by one as one word (bf16 value in the high half, chunk row in
+// the low half: the value is that word with the low half cleared), and each
+// adds w * X[k][4 lane .. +4] from LDS to the lane's fp32 accumulators, in
+// column order.  Every X element is read from L2 once per block instead of
+// once per stored entry.
 template <typename OutT>
 __global__ __launch_bounds__(64 * EW_WAVES) void k_spmm_ew(const int64_t* __restrict__ row_ptr,
                                                            const int32_t* __restrict__ cols,
@@ -73,12 +78,28 @@ __global__ __launch_bounds__(64 * EW_WAVES) void k_spmm_ew(const int64_t* __rest
     for (int c = 0; c < 4; ++c) acc[i][c] = 0.0f;
 
   for (int64_t k0 = 0; k0 < K; k0 += EW_KB) {
+    // The first window of stored entries (64, one per lane) of each of the
+    // wave's rows, loaded for all rows before any is used: the loads overlap
+    // each other and the staging below instead of costing one latency per row.
+    int32_t cwin[EW_ROWS_PER_WAVE];
+    uint32_t wwin[EW_ROWS_PER_WAVE];
+#pragma unroll
+    for (int i = 0; i < EW_ROWS_PER_WAVE; ++i) {
+      const int64_t q = pos[i] + lane;
+      const bool valid = q < end[i];
+      cwin[i] = valid ? cols[q] : 0x7FFFFFFF;
+      wwin[i] = valid ? vals[q] : 0u;
+    }
     __syncthreads();                                      // the previous chunk is consumed
-    // stage the chunk: piece q = tid + 256 j is row q / 32, 16 B piece q % 32
-#pragma unroll 4
-    for (int j = 0; j < EW_KB * EW_ROWB / 16 / (64 * EW_WAVES); ++j) {
+    // stage the chunk: piece q = tid + 256 j is row q / 32, 8 bf16 columns
+    // 8 (q % 32) .. +8; every piece is loaded before any is written, so all
+    // loads are in flight at once
+    constexpr int PIECES = EW_KB * EW_NB / 8 / (64 * EW_WAVES);
+    u32x4 pv[PIECES];
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
       const int q = tid + 64 * EW_WAVES * j;
-      const int r = q / (EW_ROWB / 16), pc = q % (EW_ROWB / 16);
+      const int r = q / (EW_NB / 8), pc = q % (EW_NB / 8);
       const int64_t k = k0 + r, n = n0 + 8 * pc;
       u32x4 v = {0u, 0u, 0u, 0u};
       if (k < K) {
@@ -92,7 +113,17 @@ __global__ __launch_bounds__(64 * EW_WAVES) void k_spmm_ew(const int64_t* __rest
           v = u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
         }
       }
-      *reinterpret_cast<u32x4*>(xs + r * EW_ROWB + pc * 16) = v;
+      pv[j] = v;
+    }
+#pragma unroll
+    for (int j = 0; j < PIECES; ++j) {
+      const int q = tid + 64 * EW_WAVES * j;
+      const int r = q / (EW_NB / 8), pc = q % (EW_NB / 8);
+      const u32x4 v = pv[j];
+      const u32x4 lo = {v[0] << 16, v[0] & 0xFFFF0000u, v[1] << 16, v[1] & 0xFFFF0000u};
+      const u32x4 hi = {v[2] << 16, v[2] & 0xFFFF0000u, v[3] << 16, v[3] & 0xFFFF0000u};
+      *reinterpret_cast<u32x4*>(xs + r * EW_ROWB + pc * 32) = lo;
+      *reinterpret_cast<u32x4*>(xs + r * EW_ROWB + pc * 32 + 16) = hi;
     }
     __syncthreads();
     const int64_t k_hi = k0 + EW_KB;
@@ -100,44 +131,55 @@ __global__ __launch_bounds__(64 * EW_WAVES) void k_spmm_ew(const int64_t* __rest
     for (int i = 0; i < EW_ROWS_PER_WAVE; ++i) {
       int64_t p = pos[i];
       const int64_t e = end[i];
+      int32_t c_next = cwin[i];
+      uint32_t w_next = wwin[i];
       while (p < e) {
         const int64_t q = p + lane;
         const bool valid = q < e;
-        const int32_t c = valid ? cols[q] : 0x7FFFFFFF;
-        const uint32_t w = valid ? vals[q] : 0u;
+        const int32_t c = c_next;
+        const uint32_t w = w_next;
         const bool in = valid && c < k_hi;
         const int n_in = __popcll(__ballot(in));
-        // row offset of each entry inside the staged chunk, clamped into it
+        // chunk row of each entry (clamped into the chunk) in the low half, the
+        // bf16 value in the high half
         int32_t kk = c - (int32_t)k0;
         kk = kk < 0 ? 0 : (kk >= EW_KB ? EW_KB - 1 : kk);
-        const uint32_t roff = (uint32_t)kk * EW_ROWB;
+        const uint32_t packed = (w << 16) | (uint32_t)kk;
+        const uint32_t lane_off = (uint32_t)lane * 16;
+        auto fma4 = [&](uint32_t word, f32x4 xv) {
+          const float wf = __uint_as_float(word & 0xFFFF0000u);
+          acc[i][0] = fmaf(wf, xv[0], acc[i][0]);
+          acc[i][1] = fmaf(wf, xv[1], acc[i][1]);
+          acc[i][2] = fmaf(wf, xv[2], acc[i][2]);
+          acc[i][3] = fmaf(wf, xv[3], acc[i][3]);
+        };
+        auto xrow = [&](uint32_t word) {
+          return *reinterpret_cast<const f32x4*>(xs + (word & 0xFFFFu) * EW_ROWB + lane_off);
+        };
         // eight entries at a time: their LDS reads are all issued before the
         // multiply-adds, which then run in entry (column) order
-        auto fma4 = [&](float wf, u32x2 xv) {
-          acc[i][0] = fmaf(wf, bf16_to_f32(xv.x & 0xFFFFu), acc[i][0]);
-          acc[i][1] = fmaf(wf, bf16_to_f32(xv.x >> 16), acc[i][1]);
-          acc[i][2] = fmaf(wf, bf16_to_f32(xv.y & 0xFFFFu), acc[i][2]);
-          acc[i][3] = fmaf(wf, bf16_to_f32(xv.y >> 16), acc[i][3]);
-        };
         int j = 0;
         for (; j + 8 <= n_in; j += 8) {
-          u32x2 xv[8];
-          float wf[8];
+          uint32_t wd[8];
+          f32x4 xv[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)roff, j + u) + lane * 8;
-            wf[u] = bf16_to_f32((uint32_t)__builtin_amdgcn_readlane((int)w, j + u));
-            xv[u] = *reinterpret_cast<const u32x2*>(xs + a);
+            wd[u] = (uint32_t)__builtin_amdgcn_readlane((int)packed, j + u);
+            xv[u] = xrow(wd[u]);
           }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) fma4(wf[u], xv[u]);
+          for (int u = 0; u < 8; ++u) fma4(wd[u], xv[u]);
         }
         for (; j < n_in; ++j) {
-          const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)roff, j) + lane * 8;
-          fma4(bf16_to_f32((uint32_t)__builtin_amdgcn_readlane((int)w, j)), *reinterpret_cast<const u32x2*>(xs + a));
+          const uint32_t wd = (uint32_t)__builtin_amdgcn_readlane((int)packed, j);
+          fma4(wd, xrow(wd));
         }
         p += n_in;
         if (n_in < 64) break;
+        // a full window inside the chunk: the next one
+        const int64_t qn = p + lane;
+        c_next = qn < e ? cols[qn] : 0x7FFFFFFF;
+        w_next = qn < e ? vals[qn] : 0u;
       }
       pos[i] = p;
     }
