@@ -586,6 +586,8 @@ def main():
     achieved = wl.kept_flops / (launch_ms * 1e-3) / 1e12
     rows["speedup_vs_dense"] = rows["gemm_bf16_us_mean"] / rows["spmm24_us_mean"]
     rows["speedup_vs_torch_matmul"] = rows["torch_matmul_us_mean"] / rows["spmm24_us_mean"]
+    # context: hipBLASLt on its fastest layout here (both operands K-contiguous)
+    rows["speedup_vs_torch_linear_tn"] = rows["torch_linear_tn_us_mean"] / rows["spmm24_us_mean"]
     rows["dense_eq_frac_of_sparse_peak"] = (wl.dense_flops / (launch_ms * 1e-3) / 1e12) / (2 * PEAK_BF16_MFMA_TFLOPS)
     out = {
         "metric": "dense-equiv TFLOP/s of 2:4 SpMM (bf16, 1 MI355X); speedup vs dense GEMM",
