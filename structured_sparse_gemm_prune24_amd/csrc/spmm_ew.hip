@@ -8,7 +8,7 @@
 
 namespace p24 {
 
-constexpr int EW_WAVES = 4;
+constexpr int EW_WAVES = 8;
 constexpr int EW_ROWS_PER_WAVE = 8;
 constexpr int EW_ROWS = EW_WAVES * EW_ROWS_PER_WAVE;   // W rows per block
 constexpr int EW_NB = 256;                              // columns per block: 4 per lane
@@ -37,13 +37,14 @@ template <> __device__ __forceinline__ void ew_store<uint16_t>(uint16_t* p, cons
   }
 }
 
-// One block per (32 rows of W, 256 columns of N).  The block walks K in
-// chunks of 32: the chunk X[k0 .. k0+32)[n0 .. n0+256) is staged in LDS as
+// One block per (64 rows of W, 256 columns of N), 8 waves.  The block walks K
+// in chunks of 32: the chunk X[k0 .. k0+32)[n0 .. n0+256) is staged in LDS as
 // fp32 (32 KiB, rows past K and columns past N zero; converted once per
 // element here instead of once per stored entry below), then each wave takes
-// its 8 rows.  The small chunk leaves room for four blocks per CU, whose
-// waves hide each other's LDS and lane-broadcast latencies (64 KiB chunks, two
-// blocks per CU, measured 17 % slower).  For a row, 64 stored entries at a time are read one per lane;
+// its 8 rows.  The small chunk leaves room for two blocks per CU, whose 16
+// waves hide each other's LDS and lane-broadcast latencies (64 KiB chunks and
+// one block of 4 waves less per CU measured 17 % slower; 4-wave blocks of 32
+// rows, which stage each chunk for half as many rows, 7 % slower).  For a row, 64 stored entries at a time are read one per lane;
 // those inside the chunk (columns ascending, so a prefix of the lanes) are
 // broadcast one by one as one word (bf16 value in the high half, chunk row in
 // the low half: the value is that word with the low half cleared), and each
@@ -91,7 +92,7 @@ __global__ __launch_bounds__(64 * EW_WAVES) void k_spmm_ew(const int64_t* __rest
       wwin[i] = valid ? vals[q] : 0u;
     }
     __syncthreads();                                      // the previous chunk is consumed
-    // stage the chunk: piece q = tid + 256 j is row q / 32, 8 bf16 columns
+    // stage the chunk: piece q = tid + 64 EW_WAVES j is row q / 32, 8 bf16 columns
     // 8 (q % 32) .. +8; every piece is loaded before any is written, so all
     // loads are in flight at once
     constexpr int PIECES = EW_KB * EW_NB / 8 / (64 * EW_WAVES);
