@@ -44,7 +44,8 @@ template <> __device__ __forceinline__ void ew_store<uint16_t>(uint16_t* p, cons
 // its 8 rows.  The small chunk leaves room for two blocks per CU, whose 16
 // waves hide each other's LDS and lane-broadcast latencies (64 KiB chunks and
 // one block of 4 waves less per CU measured 17 % slower; 4-wave blocks of 32
-// rows, which stage each chunk for half as many rows, 7 % slower).  For a row, 64 stored entries at a time are read one per lane;
+// rows, which stage each chunk for half as many rows, 7 % slower; 16-wave
+// blocks of 128 rows, one per CU, 2 % slower).  For a row, 64 stored entries at a time are read one per lane;
 // those inside the chunk (columns ascending, so a prefix of the lanes) are
 // broadcast one by one as one word (bf16 value in the high half, chunk row in
 // the low half: the value is that word with the low half cleared), and each
