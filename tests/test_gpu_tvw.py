@@ -106,6 +106,26 @@ def test_spmm_tvw_small(M, K, N, keep, tile, monkeypatch):
     assert ok, worst
 
 
+@pytest.mark.parametrize("M,K,N,keep", [(512, 512, 600, 256), (400, 256, 264, 128)])
+@pytest.mark.parametrize("tile", ["128x256", "128x512"])
+def test_spmm_tvw_tall_tiles(M, K, N, keep, tile, monkeypatch):
+    """TVW tiles of 256 output rows: the two 128-row block rows of a tile gather by the same
+    kept list (the last tile ragged in the second case), at both block widths."""
+    need_gpu()
+    monkeypatch.setenv("P24_GATHER_TILE", tile)
+    print(f"[tvw] tall tiles M={M} K={K} N={N} keep={keep} tile={tile}", flush=True)
+    W = workloads.random_matrix((M, K), seed=M + N, sigma=0.05)
+    Xb = workloads.random_bf16((K, N), seed=N + 7)
+    t = p24.tvw_compress(f32_dev(W), tile_m=256, keep_k=keep)
+    Y = p24.spmm_tvw(t, bf16_dev(Xb), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    kept, values, meta = O.tvw_compress(W, 256, keep)
+    assert np.array_equal(t.kept.cpu().numpy(), kept)
+    y_ref, bnd = O.gemm_ref(O.tvw_decompress(kept, values, meta, M, K, 256), Xb)
+    ok, worst = O.check(y_host(Y), y_ref, bnd, "f32")
+    assert ok, worst
+
+
 def test_keep_all_equals_plain_24():
     need_gpu()
     M, K, N = 256, 256, 128

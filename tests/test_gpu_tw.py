@@ -78,6 +78,26 @@ def test_spmm_tw_small(M, K, N, keep, tile, monkeypatch):
     assert ok, worst
 
 
+@pytest.mark.parametrize("M,K,N,keep", [(512, 512, 600, 256), (400, 256, 264, 128)])
+@pytest.mark.parametrize("tile", ["128x256", "128x512"])
+def test_spmm_tw_tall_tiles(M, K, N, keep, tile, monkeypatch):
+    """TW tiles of 256 output rows (two 128-row block rows per kept list; ragged last tile in
+    the second case), at both block widths."""
+    need_gpu()
+    monkeypatch.setenv("P24_GATHER_TILE", tile)
+    W = workloads.random_matrix((M, K), seed=M + N + 1, sigma=0.05)
+    Xb = workloads.random_bf16((K, N), seed=N + 8)
+    t, kept, Wc = _compare_fixed(W, 256, keep)
+    print(f"[tw] tall tiles spmm M={M} K={K} N={N} keep={keep} tile={tile}", flush=True)
+    Y = p24.spmm_tw(t, bf16_dev(Xb), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    T = kept.shape[0]
+    Wd = O.tw_decompress(list(kept), [Wc[256 * i:256 * i + 256] for i in range(T)], M, K, 256)
+    y_ref, bnd = O.gemm_ref(Wd, Xb)
+    ok, worst = O.check(y_host(Y), y_ref, bnd, "f32")
+    assert ok, worst
+
+
 def test_tw_keep_all_equals_dense():
     """Keeping every column is the dense product of the bf16 cast, bit for bit."""
     need_gpu()
