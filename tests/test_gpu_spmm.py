@@ -13,7 +13,7 @@ import pytest
 
 import workloads
 from oracle import prune24 as O
-from gpu_util import bf16_dev, f32_dev, need_gpu, sample_rows, torch, u16_host, y_host
+from gpu_util import DEV, bf16_dev, f32_dev, need_gpu, sample_rows, torch, u16_host, y_host
 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
@@ -149,3 +149,44 @@ def test_zero_sized_noop():
     L = p24.lib()
     assert L.spmm24(None, None, 1, 0, 128, None, 64, 64, None, 0, 64, 0, None) == p24.P24_OK
     assert L.gemm_bf16(None, 64, 128, None, 0, 0, None, 0, 0, None) == p24.P24_OK
+
+
+@pytest.mark.parametrize("pad", [3, 8])
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_strided_outputs(pad, out):
+    """Y as a column slice of a wider buffer (row stride N + pad): pad = 3 leaves the rows
+    unaligned, so the epilogue stores element by element; pad = 8 keeps 16-byte row pieces.
+    The products match the oracle and no write lands in the padding."""
+    need_gpu()
+    M, K, N = 300, 256, 200
+    print(f"[spmm] strided Y pad={pad} {out}", flush=True)
+    W = workloads.random_matrix((M, K), seed=21, sigma=0.05)
+    Xb = workloads.random_bf16((K, N), seed=22)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    c = p24.compress(f32_dev(W), layout="device")
+    X = bf16_dev(Xb)
+    XT = bf16_dev(np.ascontiguousarray(Xb.T))
+    Wp = p24.pack_dense(bf16_dev(O.decompress_24(*O.compress_24(W, "f32"), K)))
+    t = p24.tvw_compress(f32_dev(W), tile_m=128, keep_k=128)
+    calls = {
+        "spmm24": lambda Y: p24.spmm24(c, X, out=Y),
+        "spmm24_xt": lambda Y: p24.spmm24_xt(c, XT, out=Y),
+        "spmm24_fused": lambda Y: p24.spmm24(c, X, out=Y, act="relu"),
+        "gemm_bf16": lambda Y: p24.gemm_bf16(Wp, M, K, X, out=Y),
+        "spmm_tvw": lambda Y: p24.spmm_tvw(t, X, out=Y),
+    }
+    values, meta = O.compress_24(W, "f32")
+    y24, b24 = O.gemm_ref(O.decompress_24(values, meta, K), Xb)
+    kept, tv, tm = O.tvw_compress(W, 128, 128)
+    ytvw, btvw = O.gemm_ref(O.tvw_decompress(kept, tv, tm, M, K, 128), Xb)
+    for name, call in calls.items():
+        full = torch.full((M, N + pad), 7.0, dtype=dt, device=DEV)
+        Y = full[:, :N]
+        call(Y)
+        torch.cuda.synchronize()
+        assert torch.all(full[:, N:] == 7.0), f"{name} wrote into the padding"
+        y_ref, bnd = (ytvw, btvw) if name == "spmm_tvw" else (y24, b24)
+        if name == "spmm24_fused":
+            y_ref = np.maximum(y_ref, 0.0)
+        ok, worst = O.check(y_host(Y), y_ref, bnd, out)
+        assert ok, f"{name}: worst err/tol {worst}"
