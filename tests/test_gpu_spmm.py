@@ -190,3 +190,34 @@ def test_strided_outputs(pad, out):
             y_ref = np.maximum(y_ref, 0.0)
         ok, worst = O.check(y_host(Y), y_ref, bnd, out)
         assert ok, f"{name}: worst err/tol {worst}"
+
+
+@pytest.mark.parametrize("out", ["f32", "bf16"])
+def test_non_finite_x_where_w_is_pruned(out):
+    """X rows that meet only pruned weights: the sparse MFMA never multiplies them (the
+    result is the product without those terms), while the expanded-tile path multiplies the
+    explicit zeros (0 * Inf = NaN), as the header states."""
+    need_gpu()
+    M, K, N, g = 256, 256, 136, 5
+    print(f"[spmm] non-finite X rows {out}", flush=True)
+    W = workloads.random_matrix((M, K), seed=41, sigma=0.05)
+    W[:, 4 * g + 0:4 * g + 2] += np.float32(10.0)       # positions 0 and 1 win in every row
+    Xb = workloads.random_bf16((K, N), seed=42)
+    Xb[4 * g + 2, :] = 0x7F80                            # +Inf
+    Xb[4 * g + 3, ::3] = 0x7FC0                          # NaN in every third column
+    values, meta = O.compress_24(W, "f32")
+    Wd = O.decompress_24(values, meta, K)
+    assert not Wd[:, 4 * g + 2:4 * g + 4].any()          # both rows pruned everywhere
+    X0 = Xb.copy()
+    X0[4 * g + 2:4 * g + 4, :] = 0                       # the terms the sparse MFMA skips
+    y_ref, bnd = O.gemm_ref(Wd, X0)
+    dt = torch.float32 if out == "f32" else torch.bfloat16
+    c = p24.compress(f32_dev(W))
+    X = bf16_dev(Xb)
+    Y = p24.spmm24(c, X, out_dtype=dt)
+    Yd = p24.spmm24(c, X, out_dtype=dt, algo="decomp_mfma")
+    torch.cuda.synchronize()
+    assert torch.isfinite(Y).all().item()
+    ok, worst = O.check(y_host(Y), y_ref, bnd, out)
+    assert ok, f"worst err/tol {worst}"
+    assert torch.isnan(Yd).all().item()
