@@ -33,6 +33,12 @@
  *     the process has already loaded.  A process holds one copy: when another
  *     component opens its own copy by path (PyTorch does), load that component
  *     first.
+ *   - The products pick their block tile from the shape.  Two environment
+ *     variables, read at each call, force a tile instead (measurement and
+ *     test aids; results stay within the same bounds):
+ *     P24_TILE=256x256|128x256|128x128|64x128 for spmm24, spmm24_xt, the
+ *     fused product and gemm_bf16; P24_GATHER_TILE=128x256|128x512 for the
+ *     fixed-keep gathered products (spmm_tvw, spmm_tw and their fused forms).
  *
  * Layouts of a compressed matrix (values are bf16, metadata uint32)
  *   P24_LAYOUT_CANONICAL
