@@ -11,7 +11,7 @@ Sources (the method's definition):
   * "Accelerating Sparse Deep Neural Networks" (Mishra et al.), Abstract: a 2:4
     pattern keeps 50% of the weights and the sparse matrix unit does twice the
     dense math rate.
-  * NVIDIA A100 sparsity blog page (nvidia-a100-benchmarks), body text and its
+  * NVIDIA A100 sparsity blog page, body text and its
     (missing) Figure 1: in every run of four consecutive weights at least two
     are zero; the survivors are stored in a compressed form with a small amount
     of position metadata.
