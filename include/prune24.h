@@ -421,8 +421,9 @@ P24_API p24_status spmm_ew(const int64_t* row_ptr, const int32_t* cols, const vo
                            int64_t ldy, void* stream);
 
 /*
- * Dense bf16 GEMM, the denominator of every speedup ("over the dense model",
- * "Accelerating Sparse DNNs Based on Tiled GEMM", Abstract).  It runs the same
+ * Dense bf16 GEMM, the denominator of every speedup (the pages measure their
+ * speedups against the dense model: "Accelerating Sparse DNNs Based on Tiled
+ * GEMM", Abstract).  It runs the same
  * tile loop as spmm24 with the dense MFMA v_mfma_f32_32x32x16_bf16.
  *   gemm_bf16_pack: W (M x K bf16, ldw >= K, ldw % 8 == 0, 16 B aligned) ->
  *     Wp in MFMA operand order: (Mp/32) x (K/16) blocks of 64 x 8 bf16, block
