@@ -101,26 +101,37 @@ def cpu_baseline(wl, W, Xb):
     """Oracle (numpy, fp64) on a bounded row sample of the headline workload."""
     import numpy as np
     from oracle import prune24 as O
+    blas = None
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        blas = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                                 if i.get("user_api") == "blas"})) or None
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        pass
     def run(rows):
         t0 = time.perf_counter()
         values, meta = O.compress_24(W[:rows], "f32")
         Wd = O.decompress_24(values, meta, wl.K)
+        t1 = time.perf_counter()
         y, bnd = O.gemm_ref(Wd, Xb)
-        dt = time.perf_counter() - t0
+        t2 = time.perf_counter()
         assert np.isfinite(y).all() and np.isfinite(bnd).all()
-        return dt
+        return t1 - t0, t2 - t1
     # size the sample to about 10-30 s of host work: the whole workload when the
     # estimate from a small probe stays under 30 s, else a proportional slice
     probe = 256
-    dt = run(probe)
-    est_full = dt * wl.M / probe
+    est_full = sum(run(probe)) * wl.M / probe
     rows = wl.M if est_full <= 30.0 else max(probe, int(wl.M * 15.0 / est_full) // probe * probe)
-    dt = run(rows)
+    t_compress, t_gemm = run(rows)
+    dt = t_compress + t_gemm
     flops = 2.0 * rows * wl.N * wl.K
     return {
         "value": round(flops / dt / 1e12, 6),
@@ -129,6 +140,10 @@ def cpu_baseline(wl, W, Xb):
         "kind": "oracle",
         "sample": f"{rows} of {wl.M} output rows of {wl.key}: oracle prune+compress+decompress of those "
                   f"rows and fp64 GEMM + |W||X| bound against the full X ({dt:.1f} s)",
+        "prune_compress_s": round(t_compress, 3),
+        "gemm_and_bound_s": round(t_gemm, 3),
+        "cpu_model": cpu_model,
+        "blas": blas,
     }
 
 
