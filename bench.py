@@ -226,13 +226,13 @@ def read_clock_samples(path, t_lo, t_hi):
     return out
 
 
-def measured_traffic():
-    """HBM bytes per spmm24 launch from the committed rocprofv3 counter summary, or None
-    when the kernel source changed since those counters were taken."""
+def measured_traffic(path=None, src=None):
+    """HBM bytes per spmm24 launch from the committed rocprofv3 counter summary (`path`), or
+    None when the kernel source (`src`) changed since those counters were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", "spmm24_8192cube_hbm_traffic.md")
-    src = os.path.join(ROOT, "structured_sparse_gemm_prune24_amd", "csrc", "gemm.hip")
+    path = path or os.path.join(ROOT, "profiles", "spmm24_8192cube_hbm_traffic.md")
+    src = src or os.path.join(ROOT, "structured_sparse_gemm_prune24_amd", "csrc", "gemm.hip")
     try:
         text = open(path).read()
         digest = hashlib.sha256(open(src, "rb").read()).hexdigest()

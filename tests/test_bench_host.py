@@ -1,4 +1,5 @@
-"""Host logic of bench.py: the clock reading parser and the sample window filter."""
+"""Host logic of bench.py: the clock reading parser, the sample window filter, the traffic
+figure's source-hash gate, the one-GPU rule and the CPU baseline leg."""
 import json
 import os
 import sys
@@ -46,3 +47,41 @@ def test_under_profiler_detects_the_profiler_environment():
     assert bench.under_profiler({"ROCPROF_KERNEL_TRACE": "1"})
     assert not bench.under_profiler({"LD_PRELOAD": "/usr/lib/libother.so", "PATH": "/usr/bin"})
     assert not bench.under_profiler({})
+
+
+def test_measured_traffic_is_gated_by_the_kernel_source_hash(tmp_path):
+    """The traffic figure is reported only while the kernel source is the one profiled."""
+    import hashlib
+    src = tmp_path / "gemm.hip"
+    src.write_text("// kernel source\n")
+    digest = hashlib.sha256(src.read_bytes()).hexdigest()
+    prof = tmp_path / "traffic.md"
+    prof.write_text(f"traffic_bytes_per_launch: 123456\nkernel_source_sha256_prefix: {digest[:16]}\n")
+    assert bench.measured_traffic(str(prof), str(src)) == 123456
+    src.write_text("// kernel source, changed\n")
+    assert bench.measured_traffic(str(prof), str(src)) is None
+    assert bench.measured_traffic(str(tmp_path / "missing.md"), str(src)) is None
+    prof.write_text("no machine-readable lines\n")
+    assert bench.measured_traffic(str(prof), str(src)) is None
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU; --gpus above 1 exits with status 2 and says so."""
+    import subprocess
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=60, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU only" in r.stderr
+    assert r.stdout == ""
+
+
+def test_cpu_baseline_on_the_small_workload():
+    """The CPU leg runs the oracle on the whole small workload and reports its figures."""
+    import workloads
+    wl = workloads.WORKLOADS["c1"]
+    cb = bench.cpu_baseline(wl, workloads.weights(wl), workloads.activations(wl))
+    assert cb["kind"] == "oracle" and cb["unit"] == "TFLOP/s (dense-equivalent)"
+    assert cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["sample"].startswith(f"{wl.M} of {wl.M} output rows of c1")
+    assert cb["prune_compress_s"] >= 0 and cb["gemm_and_bound_s"] >= 0
+    assert set(cb) >= {"cpu_model", "blas"}
