@@ -296,12 +296,12 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
   const int64_t r1 = (t + 1) * tile_m < M ? (t + 1) * tile_m : M;
   double acc = 0.0;
   int64_t m = t * tile_m;
-  for (; m + 8 <= r1; m += 8) {          // 8 loads in flight, then the adds in row order
-    float v[8];
+  for (; m + 16 <= r1; m += 16) {        // 16 loads in flight, then the adds in row order
+    float v[16];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = W[(m + u) * ldw + k];
+    for (int u = 0; u < 16; ++u) v[u] = W[(m + u) * ldw + k];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) acc = acc + fabs((double)v[u]);
+    for (int u = 0; u < 16; ++u) acc = acc + fabs((double)v[u]);
   }
   for (; m < r1; ++m) acc = acc + fabs((double)W[m * ldw + k]);
   scores[id] = acc;
@@ -328,7 +328,7 @@ __device__ __forceinline__ int64_t block_exclusive_scan(U v, int64_t* total, U* 
   static_assert(sizeof(U) == 4 || sizeof(U) == 8, "32- or 64-bit counts");
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t o = __shfl_up(incl, d);
+    const U o = __shfl_up(incl, d);      // full width: 64-bit partial sums stay whole
     if (lane >= d) incl += o;
   }
   if (lane == 63) wave_sums[wave] = incl;

@@ -58,6 +58,16 @@ def test_select_many_chunks():
     _compare_compress(W, 128, 2500, "canonical")
 
 
+@pytest.mark.parametrize("K", [8192, 8320])
+def test_select_wide_tiles(K):
+    """Wide tiles (8192 and 8320 columns: 8 and 9 scan chunks, the second ragged) with
+    a tie straddling the cut."""
+    need_gpu()
+    W = workloads.random_matrix((130, K), seed=79, sigma=0.02)
+    W[:, 3000:3400] = 0.25
+    _compare_compress(W, 128, K // 2 + 64, "canonical")
+
+
 def test_select_threshold_tie():
     """A tie straddling the cut: only the lowest-index tied columns make it."""
     need_gpu()
