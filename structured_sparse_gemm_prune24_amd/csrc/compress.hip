@@ -164,21 +164,18 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, 
   // group and then take the padding result (zero values, positions (0, 1)).
   const int64_t g_rd = gv ? g : G - 1;
   u32x4* vout = reinterpret_cast<u32x4*>(dvals + (rbl * S + 8 * c) * 64 * 8);
-  // Gathered columns: when the block's 32 rows lie in one tile (per-tile keep
-  // counts, or a tile height that is a multiple of 32) the lane's four kept
-  // columns are read once, so each row's loads depend on nothing else.
-  // Padding rows read the last row, whose tile is the block's first row's.
+  // Gathered columns: tile heights are multiples of 32 (the host checks), so
+  // the block's 32 rows lie in one tile and the lane's four kept columns are
+  // read once; each row's loads then depend on nothing else.  Padding rows
+  // read the last row, which lies in the tile of the block's first row.
   int64_t kcol[4] = {0, 0, 0, 0};
-  const bool one_tile = GATHER && (GM == G_VAR || tile_m % 32 == 0);
   if constexpr (GATHER) {
-    if (one_tile) {
-      const int64_t m_first = rb * 32 < M ? rb * 32 : M - 1;
-      const int32_t* kr = GM == G_FIXED ? kept + (m_first / tile_m) * K : kept_tile;
+    const int64_t m_first = rb * 32 < M ? rb * 32 : M - 1;
+    const int32_t* kr = GM == G_FIXED ? kept + (m_first / tile_m) * K : kept_tile;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t k = kr[4 * g_rd + i];
-        kcol[i] = k < 0 ? 0 : (k >= kmax ? kmax - 1 : k);
-      }
+    for (int i = 0; i < 4; ++i) {
+      const int64_t k = kr[4 * g_rd + i];
+      kcol[i] = k < 0 ? 0 : (k >= kmax ? kmax - 1 : k);
     }
   }
   for (int r0 = 0; r0 < 32; r0 += 8) {
@@ -188,14 +185,13 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, 
       const int64_t m = rb * 32 + r;
       const bool live = m < M && gv;
       const int64_t m_rd = m < M ? m : M - 1;
-      const int32_t* kept_row = GM == G_FIXED ? kept + (m_rd / tile_m) * K : kept_tile;
       uint32_t b[4];
-      if (one_tile) {
+      if constexpr (GATHER) {
         const T* row = W + m_rd * ldw;
 #pragma unroll
         for (int i = 0; i < 4; ++i) b[i] = raw_bits<T>(row[kcol[i]]);
       } else {
-        fetch_group<T, GATHER>(W, ldw, m_rd, g_rd, kept_row, kmax, b);
+        fetch_group<T, false>(W, ldw, m_rd, g_rd, nullptr, kmax, b);
       }
       uint16_t v0, v1;
       uint32_t code = compress_group<T>(b, v0, v1);
