@@ -366,7 +366,8 @@ __device__ __forceinline__ int64_t block_exclusive_scan(U v, int64_t* total, U* 
 // The need-th largest key (need >= 1, at most the histogram total) has the
 // digit d at which the keys of bins >= d first reach `need`; the lane that
 // owns d returns true with d and that key's rank among the keys of bin d.
-__device__ __forceinline__ bool find_cut(const uint32_t (&hb)[4], int64_t need, int l, int* digit, int64_t* rest) {
+__device__ __forceinline__ bool find_cut(const uint32_t (&hb)[4], int64_t need, int l, int* digit, int64_t* rest,
+                                         uint32_t* bin = nullptr) {
   const uint32_t own = hb[0] + hb[1] + hb[2] + hb[3];
   uint32_t incl = own;                 // inclusive suffix sum over lanes l .. 63
 #pragma unroll
@@ -379,12 +380,15 @@ __device__ __forceinline__ bool find_cut(const uint32_t (&hb)[4], int64_t need, 
   // the cut lies in this lane's bins: walk them from the highest
   int64_t a = above;
   int d = 4 * l + 3;
+  uint32_t cnt = hb[3];
   for (int i = 3; i > 0 && a + hb[i] < need; --i) {
     a += hb[i];
     --d;
+    cnt = hb[i - 1];
   }
   *digit = d;
   *rest = need - a;
+  if (bin) *bin = cnt;
   return true;
 }
 
@@ -395,6 +399,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
   __shared__ uint32_t wave_sums[SEL_WAVES];
   __shared__ uint64_t sh_prefix;
   __shared__ int64_t sh_need;
+  __shared__ uint32_t sh_whole;
   const int64_t t = blockIdx.x;
   const uint64_t* key = reinterpret_cast<const uint64_t*>(scores + t * K);
   const int tid = threadIdx.x;
@@ -419,14 +424,24 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
       const uint32_t hb[4] = {hist[4 * tid], hist[4 * tid + 1], hist[4 * tid + 2], hist[4 * tid + 3]};
       int d;
       int64_t rest;
-      if (find_cut(hb, need, tid, &d, &rest)) {
+      uint32_t bin;
+      if (find_cut(hb, need, tid, &d, &rest, &bin)) {
         sh_prefix = prefix | ((uint64_t)d << shift);
         sh_need = rest;
+        sh_whole = rest == (int64_t)bin ? 1u : 0u;
       }
     }
     __syncthreads();
     prefix = sh_prefix;
     need = sh_need;
+    // Every key of the cut's bin is kept: the kept set is then every key >= the
+    // bin's lowest value (prefix, lower bits zero), which the scan below takes
+    // as the keys above prefix plus all keys equal to it.  No later digit can
+    // change that set, so the remaining passes are skipped.
+    if (sh_whole) {
+      need = K;
+      break;
+    }
   }
   // prefix is the threshold key; `need` columns equal to it are kept, lowest first
   int64_t eq_base = 0, out_base = 0;
@@ -439,7 +454,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
     const int64_t eq_rank = eq_base + block_exclusive_scan<uint32_t>(eq ? 1u : 0u, &eq_total, wave_sums);
     const bool keep = gt || (eq && eq_rank < need);
     const int64_t pos = out_base + block_exclusive_scan<uint32_t>(keep ? 1u : 0u, &keep_total, wave_sums);
-    if (keep) kept_out[pos] = (int32_t)k;
+    if (keep && pos < keep_k) kept_out[pos] = (int32_t)k;   // exactly keep_k keys are kept; the bound is a guard
     eq_base += eq_total;
     out_base += keep_total;
   }

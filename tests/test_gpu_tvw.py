@@ -68,6 +68,17 @@ def test_select_wide_tiles(K):
     _compare_compress(W, 128, K // 2 + 64, "canonical")
 
 
+def test_select_cut_bin_all_tied_and_kept():
+    """keep_k equals the number of columns at or above a block of 300 tied columns,
+    so the bin holding the cut is kept whole (the selection stops early there)."""
+    need_gpu()
+    W = workloads.random_matrix((128, 1024), seed=80, sigma=0.02)
+    W[:, 600:700] = 1.0                  # 100 columns above everything
+    W[:, 100:400] = 0.25                 # 300 tied columns, above every random one
+    t, kept, _, _ = _compare_compress(W, 128, 400, "canonical")
+    assert np.array_equal(kept[0], np.r_[100:400, 600:700])
+
+
 def test_select_threshold_tie():
     """A tie straddling the cut: only the lowest-index tied columns make it."""
     need_gpu()
