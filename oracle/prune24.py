@@ -34,7 +34,9 @@ Readings where the pages are silent:
   * TVW: tile t = output rows [t*tile_m, (t+1)*tile_m); column score = fp64
     sum of |W| over the tile's rows in ascending row order; keep the keep_k
     columns with the largest score (ties -> lower k), listed ascending; then
-    2:4 along the compacted axis.
+    2:4 along the compacted axis.  A computed score that is NaN ranks above
+    +Inf, and NaN scores tie with each other (``score_key``): IEEE 754 leaves
+    the payload of an arithmetic NaN open, so no order may depend on it.
   * GEMM tolerance: |y - y_ref| <= 1e-3 * (|W|.|X|)_ij on the fp32 result; a
     bf16 result also gets the half-ulp of its final rounding,
     2^-8 * (|y_ref| + 1e-3 * (|W|.|X|)).
@@ -323,18 +325,36 @@ def tvw_scores(W: np.ndarray, tile_m: int) -> np.ndarray:
     return out
 
 
+SCORE_NAN_KEY = 0x7FF8000000000000
+
+
+def score_key(sc: np.ndarray) -> np.ndarray:
+    """Ranking key of computed fp64 scores (column, block and per-tile scores).
+
+    A score is a sum of magnitudes, so it is +0, positive, +Inf or NaN, and
+    for all but NaN its bit pattern read as an unsigned integer orders like
+    its value.  The payload of a NaN that arithmetic produces is not fixed by
+    IEEE 754, so every NaN score gets the one key 0x7FF8000000000000: above
+    +Inf (0x7FF0000000000000), and NaN scores tie with each other, the tie
+    going to the lower index like every other tie.
+    """
+    sc = np.asarray(sc, dtype=np.float64)
+    key = sc.view(np.uint64).copy()
+    key[np.isnan(sc)] = SCORE_NAN_KEY
+    return key
+
+
 def tvw_select(W: np.ndarray, tile_m: int, keep_k: int) -> np.ndarray:
     """Kept column indices per tile, int32 [T, keep_k], ascending.
 
-    Order: score descending, then column ascending (stable sort).  Scores are
-    non-negative, so comparing their fp64 bit patterns as unsigned integers is
-    the value order; it also gives NaN (sign cleared) a place above +Inf.
+    Order: score key descending (``score_key``: the value order, every NaN
+    above +Inf), then column ascending (stable sort).
     """
     M, K = np.asarray(W).shape
     if not (0 < keep_k <= K) or keep_k % 4:
         raise ValueError("keep_k must be in (0, K] and a multiple of 4")
     sc = tvw_scores(W, tile_m)
-    key = sc.view(np.uint64)
+    key = score_key(sc)
     order = np.argsort(np.iinfo(np.uint64).max - key, axis=1, kind="stable")
     kept = np.sort(order[:, :keep_k], axis=1)
     return kept.astype(np.int32)
@@ -389,7 +409,7 @@ def tvw_var_counts(W: np.ndarray, tile_m: int, total_keep: int) -> np.ndarray:
     T, K = sc.shape
     if K % VAR_STEP or not (0 < total_keep <= T * K):
         raise ValueError("K must be a multiple of 64 and 0 < total_keep <= T*K")
-    key = sc.view(np.uint64).reshape(-1)
+    key = score_key(sc).reshape(-1)
     ranked = np.argsort(np.iinfo(np.uint64).max - key, kind="stable")
     raw = np.bincount(ranked[:total_keep] // K, minlength=T)
     counts = VAR_STEP * ((raw + VAR_STEP // 2) // VAR_STEP)
@@ -400,7 +420,7 @@ def tvw_var_compress(W: np.ndarray, tile_m: int, counts):
     """Per tile: (kept int32 [c_t] ascending, values u16 [rows_t, c_t/2], meta u32 [rows_t, c_t/32])."""
     W = np.asarray(W, dtype=np.float32)
     M, K = W.shape
-    key = tvw_scores(W, tile_m).view(np.uint64)
+    key = score_key(tvw_scores(W, tile_m))
     out = []
     for t, c in enumerate(np.asarray(counts)):
         order = np.argsort(np.iinfo(np.uint64).max - key[t], kind="stable")
@@ -534,7 +554,7 @@ def bw_select(W: np.ndarray, keep_blocks: int) -> np.ndarray:
     bs = bw_block_scores(W)
     if not (0 < keep_blocks <= bs.shape[1]):
         raise ValueError("keep_blocks must be in (0, K/64]")
-    order = np.argsort(np.iinfo(np.uint64).max - bs.view(np.uint64), axis=1, kind="stable")
+    order = np.argsort(np.iinfo(np.uint64).max - score_key(bs), axis=1, kind="stable")
     blocks = np.sort(order[:, :keep_blocks], axis=1)
     cols = (blocks[:, :, None] * BW_COLS + np.arange(BW_COLS)[None, None, :]).reshape(bs.shape[0], -1)
     return cols.astype(np.int32)

@@ -305,7 +305,15 @@ __global__ __launch_bounds__(256) void k_pack_dense(const uint16_t* __restrict__
 // TVW column scores: one thread per (tile, column); fp64 sum of |W| over the
 // tile's rows, one row at a time in ascending order (fixed order -> the same
 // correctly rounded sums as a sequential host loop).
+// A NaN sum is stored as the one quiet NaN 0x7FF8000000000000: IEEE 754 does
+// not fix the payload an addition passes on, and the selections rank scores by
+// their bit patterns, so every NaN score must carry the same bits (above
+// +Inf; NaN columns then tie and go to the lower index).
 // --------------------------------------------------------------------------
+__device__ __forceinline__ double canonical_score(double s) {
+  return s != s ? __longlong_as_double(0x7FF8000000000000ll) : s;
+}
+
 __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W, int64_t ldw, int64_t M,
                                                     int64_t K, int64_t tile_m, double* __restrict__ scores) {
   const int64_t T_ = (M + tile_m - 1) / tile_m;
@@ -323,13 +331,14 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
     for (int u = 0; u < 16; ++u) acc = acc + fabs((double)v[u]);
   }
   for (; m < r1; ++m) acc = acc + fabs((double)W[m * ldw + k]);
-  scores[id] = acc;
+  scores[id] = canonical_score(acc);
 }
 
 // --------------------------------------------------------------------------
 // TVW selection: one block per tile.  The kept set is the keep_k largest
-// scores, ties to the lower column.  Scores are non-negative fp64 sums, so
-// their bit patterns order like the values.  An MSB-first radix select (8
+// scores, ties to the lower column.  Scores are non-negative fp64 sums with
+// one NaN pattern, so their bit patterns order like the values (NaN above
+// +Inf).  An MSB-first radix select (8
 // passes of 8 bits, a 256-bin histogram over the keys that still match the
 // prefix found so far) finds the keep_k-th largest key v and how many of the
 // keys equal to v are kept; a block-wide scan in column order then writes
@@ -680,7 +689,7 @@ __global__ __launch_bounds__(256) void k_bw_block_scores(const double* __restric
   const double* sc = scores + t * K + 64 * j;
   double acc = 0.0;
   for (int c = 0; c < 64; ++c) acc = acc + sc[c];
-  bscores[id] = acc;
+  bscores[id] = canonical_score(acc);
 }
 
 __global__ __launch_bounds__(256) void k_bw_expand(const int32_t* __restrict__ kept_blocks, int64_t T,
