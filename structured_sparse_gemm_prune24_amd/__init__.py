@@ -179,6 +179,46 @@ def _rowmajor(t, name):
     return t.stride(0)
 
 
+def _same_device(t, dev, name):
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, the operation runs on {dev}")
+
+
+def _x_bf16(X, name, device=None):
+    """X must be a bf16 device tensor, 2-D, unit stride along its last dimension; returns its row stride."""
+    torch = _torch()
+    _require_cuda(X, name)
+    if X.dtype != torch.bfloat16:
+        raise ValueError(f"{name} must be bfloat16")
+    if device is not None:
+        _same_device(X, device, name)
+    return _rowmajor(X, name)
+
+
+def _operands_on(device, *named):
+    """Every (tensor, name) of a compressed operand must live on the device the product runs on."""
+    for t, name in named:
+        if t is not None:
+            _require_cuda(t, name)
+            _same_device(t, device, name)
+
+
+def _out_tensor(out, M, N, out_dtype, device):
+    """The output: a new (M, N) tensor, or the caller's, checked before any launch: a device
+    tensor on `device`, shape exactly (M, N), fp32 or bf16, unit column stride."""
+    torch = _torch()
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype or torch.bfloat16, device=device)
+    else:
+        _require_cuda(out, "out")
+        _same_device(out, device, "out")
+        if tuple(out.shape) != (M, N):
+            raise ValueError(f"out is {tuple(out.shape)}, the product is {(M, N)}")
+    ldy = _rowmajor(out, "out")
+    _out_code(out.dtype)
+    return out, ldy
+
+
 def _out_code(out_dtype):
     torch = _torch()
     if out_dtype == torch.float32:
@@ -348,20 +388,14 @@ def spmm24(c: Compressed24, X, out_dtype=None, out=None, algo="auto", bias=None,
     "decomp_mfma" (operand expanded to a dense LDS tile, dense MFMA).
     bias (fp32 [M], one value per output row) and act ("none", "relu", "gelu")
     run fused in the sparse-MFMA kernel's epilogue."""
-    torch = _torch()
     if algo not in _ALGOS:
         raise ValueError(f"algo must be one of {sorted(_ALGOS)}")
-    out_dtype = out_dtype or torch.bfloat16
-    _require_cuda(X, "X")
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bfloat16")
-    ldx = _rowmajor(X, "X")
+    ldx = _x_bf16(X, "X")
     if X.shape[0] != c.K:
         raise ValueError(f"X has {X.shape[0]} rows, W has K = {c.K}")
     N = X.shape[1]
-    if out is None:
-        out = torch.empty((c.M, N), dtype=out_dtype, device=X.device)
-    ldy = _rowmajor(out, "out")
+    _operands_on(X.device, (c.values, "values"), (c.meta, "meta"))
+    out, ldy = _out_tensor(out, c.M, N, out_dtype, X.device)
     bptr, act_code, fused = _fused_args(bias, act, c.M, X.device)
     if fused:
         if algo == "decomp_mfma":
@@ -400,18 +434,12 @@ def tvw_compress(W, tile_m: int = 128, keep_k: int | None = None, layout="device
 
 def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None, bias=None, act="none"):
     """Y = act(W X + bias) for a TVW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
-    torch = _torch()
-    out_dtype = out_dtype or torch.bfloat16
-    _require_cuda(X, "X")
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bfloat16")
-    ldx = _rowmajor(X, "X")
+    ldx = _x_bf16(X, "X")
     if X.shape[0] != t.K:
         raise ValueError(f"X has {X.shape[0]} rows, W has K = {t.K}")
     N = X.shape[1]
-    if out is None:
-        out = torch.empty((t.M, N), dtype=out_dtype, device=X.device)
-    ldy = _rowmajor(out, "out")
+    _operands_on(X.device, (t.kept, "kept"), (t.values, "values"), (t.meta, "meta"))
+    out, ldy = _out_tensor(out, t.M, N, out_dtype, X.device)
     bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
     if fused:
         _check(lib().spmm_tvw_fused(_ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.layout, t.M, t.K, t.tile_m,
@@ -451,18 +479,13 @@ def tvw_var_compress(W, total_keep: int | None = None) -> CompressedTVWVar:
 
 def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None, bias=None, act="none"):
     """Y = act(W X + bias) for a per-tile-keep TVW matrix; X bf16 [K, N]."""
-    torch = _torch()
-    out_dtype = out_dtype or torch.bfloat16
-    _require_cuda(X, "X")
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bfloat16")
-    ldx = _rowmajor(X, "X")
+    ldx = _x_bf16(X, "X")
     if X.shape[0] != t.K:
         raise ValueError(f"X has {X.shape[0]} rows, W has K = {t.K}")
     N = X.shape[1]
-    if out is None:
-        out = torch.empty((t.M, N), dtype=out_dtype, device=X.device)
-    ldy = _rowmajor(out, "out")
+    _operands_on(X.device, (t.offsets, "offsets"), (t.order, "order"), (t.kept, "kept"), (t.values, "values"),
+                 (t.meta, "meta"))
+    out, ldy = _out_tensor(out, t.M, N, out_dtype, X.device)
     bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
     if fused:
         _check(lib().spmm_tvw_var_fused(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.values), _ptr(t.meta),
@@ -475,17 +498,14 @@ def spmm_tvw_var(t: CompressedTVWVar, X, out_dtype=None, out=None, bias=None, ac
     return out
 
 
-def _x_out(X, K, M, out_dtype, out):
-    torch = _torch()
-    _require_cuda(X, "X")
-    if X.dtype != torch.bfloat16:
-        raise ValueError("X must be bfloat16")
-    ldx = _rowmajor(X, "X")
+def _x_out(X, K, M, out_dtype, out, *operands):
+    """X checks, the compressed operand's tensors on X's device, and the output."""
+    ldx = _x_bf16(X, "X")
     if X.shape[0] != K:
         raise ValueError(f"X has {X.shape[0]} rows, W has K = {K}")
-    if out is None:
-        out = torch.empty((M, X.shape[1]), dtype=out_dtype or torch.bfloat16, device=X.device)
-    return ldx, X.shape[1], out, _rowmajor(out, "out")
+    _operands_on(X.device, *operands)
+    out, ldy = _out_tensor(out, M, X.shape[1], out_dtype, X.device)
+    return ldx, X.shape[1], out, ldy
 
 
 def tw_compress(W, tile_m: int = 128, keep_k: int | None = None) -> CompressedTW:
@@ -510,7 +530,7 @@ def tw_compress(W, tile_m: int = 128, keep_k: int | None = None) -> CompressedTW
 
 def spmm_tw(t: CompressedTW, X, out_dtype=None, out=None, bias=None, act="none"):
     """Y = act(W X + bias) for a TW-compressed W; X bf16 [K, N] (rows gathered per tile)."""
-    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out, (t.kept, "kept"), (t.Wp, "Wp"))
     bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
     if fused:
         _check(lib().spmm_tw_fused(_ptr(t.kept), _ptr(t.Wp), t.M, t.K, t.tile_m, t.keep_k, _ptr(X), ldx, N,
@@ -547,7 +567,8 @@ def tw_var_compress(W, total_keep: int | None = None) -> CompressedTWVar:
 
 def spmm_tw_var(t: CompressedTWVar, X, out_dtype=None, out=None, bias=None, act="none"):
     """Y = act(W X + bias) for a per-tile-keep TW matrix; X bf16 [K, N]."""
-    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out, (t.offsets, "offsets"), (t.order, "order"),
+                              (t.kept, "kept"), (t.Wp, "Wp"))
     bptr, act_code, fused = _fused_args(bias, act, t.M, X.device)
     if fused:
         _check(lib().spmm_tw_var_fused(_ptr(t.offsets), _ptr(t.order), _ptr(t.kept), _ptr(t.Wp), t.M, t.K,
@@ -601,7 +622,8 @@ def ew_compress(W, keep_total: int) -> CompressedEW:
 
 def spmm_ew(t: CompressedEW, X, out_dtype=None, out=None):
     """Y = W X for an unstructured (CSR) W; X bf16 [K, N]."""
-    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out)
+    ldx, N, out, ldy = _x_out(X, t.K, t.M, out_dtype, out, (t.row_ptr, "row_ptr"), (t.cols, "cols"),
+                              (t.vals, "vals"))
     _check(lib().spmm_ew(_ptr(t.row_ptr), _ptr(t.cols), _ptr(t.vals), t.M, t.K, _ptr(X), ldx, N, _ptr(out),
                          _out_code(out.dtype), ldy, _stream(X.device)), "spmm_ew")
     return out
@@ -623,16 +645,28 @@ def pack_dense(W):
     return Wp
 
 
+def _packed_w(Wp, M: int, K: int, device):
+    """Wp: a bf16 device tensor on `device` holding at least gemm_bf16_packed_bytes(M, K)."""
+    torch = _torch()
+    _require_cuda(Wp, "Wp")
+    _same_device(Wp, device, "Wp")
+    if Wp.dtype != torch.bfloat16:
+        raise ValueError("Wp must be bfloat16 (the output of pack_dense)")
+    need = lib().gemm_bf16_packed_bytes(M, K)
+    if need == 0 and M * K:
+        raise P24Error(P24_ERR_UNSUPPORTED, "gemm_bf16")
+    if Wp.numel() * 2 < need:
+        raise ValueError(f"Wp holds {Wp.numel() * 2} bytes, a packed {M} x {K} matrix needs {need}")
+
+
 def gemm_bf16(Wp, M: int, K: int, X, out_dtype=None, out=None):
     """Dense baseline Y = W X from packed W (see pack_dense)."""
-    torch = _torch()
-    out_dtype = out_dtype or torch.bfloat16
-    _require_cuda(X, "X")
-    ldx = _rowmajor(X, "X")
+    ldx = _x_bf16(X, "X")
+    if X.shape[0] != K:
+        raise ValueError(f"X has {X.shape[0]} rows, W has K = {K}")
     N = X.shape[1]
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=X.device)
-    ldy = _rowmajor(out, "out")
+    _packed_w(Wp, M, K, X.device)
+    out, ldy = _out_tensor(out, M, N, out_dtype, X.device)
     _check(lib().gemm_bf16(_ptr(Wp), M, K, _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy,
                            _stream(X.device)), "gemm_bf16")
     return out
@@ -641,13 +675,15 @@ def gemm_bf16(Wp, M: int, K: int, X, out_dtype=None, out=None):
 def transpose(src, out=None):
     """bf16 src [R, C] -> out [C, R] (bit copy on the GPU)."""
     torch = _torch()
-    _require_cuda(src, "src")
-    if src.dtype != torch.bfloat16:
-        raise ValueError("src must be bfloat16")
-    lds = _rowmajor(src, "src")
+    lds = _x_bf16(src, "src")
     R, Cc = src.shape
     if out is None:
         out = torch.empty((Cc, R), dtype=src.dtype, device=src.device)
+    else:
+        _require_cuda(out, "out")
+        _same_device(out, src.device, "out")
+        if out.dtype != torch.bfloat16 or tuple(out.shape) != (Cc, R):
+            raise ValueError(f"out must be bfloat16 of shape {(Cc, R)}")
     ldd = _rowmajor(out, "out")
     _check(lib().transpose_bf16(_ptr(src), R, Cc, lds, _ptr(out), ldd, _stream(src.device)), "transpose_bf16")
     return out
@@ -655,18 +691,12 @@ def transpose(src, out=None):
 
 def spmm24_xt(c: Compressed24, XT, out_dtype=None, out=None, bias=None, act="none"):
     """Y = act(W X + bias) for compressed W with X supplied transposed: XT bf16 [N, K]."""
-    torch = _torch()
-    out_dtype = out_dtype or torch.bfloat16
-    _require_cuda(XT, "XT")
-    if XT.dtype != torch.bfloat16:
-        raise ValueError("XT must be bfloat16")
-    ldxt = _rowmajor(XT, "XT")
+    ldxt = _x_bf16(XT, "XT")
     if XT.shape[1] != c.K:
         raise ValueError(f"XT has {XT.shape[1]} columns, W has K = {c.K}")
     N = XT.shape[0]
-    if out is None:
-        out = torch.empty((c.M, N), dtype=out_dtype, device=XT.device)
-    ldy = _rowmajor(out, "out")
+    _operands_on(XT.device, (c.values, "values"), (c.meta, "meta"))
+    out, ldy = _out_tensor(out, c.M, N, out_dtype, XT.device)
     bptr, act_code, fused = _fused_args(bias, act, c.M, XT.device)
     if fused:
         _check(lib().spmm24_fused(_ptr(c.values), _ptr(c.meta), c.layout, c.M, c.K, _ptr(XT), ldxt, P24_X_NK, N,
@@ -680,14 +710,12 @@ def spmm24_xt(c: Compressed24, XT, out_dtype=None, out=None, bias=None, act="non
 
 def gemm_bf16_xt(Wp, M: int, K: int, XT, out_dtype=None, out=None):
     """Dense baseline with X supplied transposed: XT bf16 [N, K]."""
-    torch = _torch()
-    out_dtype = out_dtype or torch.bfloat16
-    _require_cuda(XT, "XT")
-    ldxt = _rowmajor(XT, "XT")
+    ldxt = _x_bf16(XT, "XT")
+    if XT.shape[1] != K:
+        raise ValueError(f"XT has {XT.shape[1]} columns, W has K = {K}")
     N = XT.shape[0]
-    if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=XT.device)
-    ldy = _rowmajor(out, "out")
+    _packed_w(Wp, M, K, XT.device)
+    out, ldy = _out_tensor(out, M, N, out_dtype, XT.device)
     _check(lib().gemm_bf16_xt(_ptr(Wp), M, K, _ptr(XT), ldxt, N, _ptr(out), _out_code(out.dtype), ldy,
                               _stream(XT.device)), "gemm_bf16_xt")
     return out

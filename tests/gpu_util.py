@@ -1,6 +1,11 @@
 """Helpers shared by the GPU parity tests (host-side plumbing only)."""
+from collections import OrderedDict
+
 import numpy as np
 import pytest
+
+import workloads
+from oracle import prune24 as O
 
 torch = pytest.importorskip("torch")
 
@@ -42,8 +47,37 @@ def y_host(t, rows=None) -> np.ndarray:
     return t.float().cpu().numpy().astype(np.float64)
 
 
-def sample_rows(M: int, n: int, seed: int) -> np.ndarray:
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(M, size=min(n, M), replace=False).tolist())
-    rows.update({0, M - 1})
-    return np.array(sorted(rows))
+_REFS: "OrderedDict[tuple, tuple]" = OrderedDict()
+_REFS_KEPT = 2
+
+
+def cached_ref(tag: tuple, make):
+    """(y_ref, bound) from `make()` (an oracle call), computed once per session under
+    `tag`: several tests multiply the same full-size weight, and an fp64 reference of
+    every row of the 8192^3 product takes seconds on the host.  The two most
+    recently used references are kept (about 1 GiB each at that size)."""
+    if tag in _REFS:
+        _REFS.move_to_end(tag)
+        return _REFS[tag]
+    while len(_REFS) >= _REFS_KEPT:
+        _REFS.popitem(last=False)
+    _REFS[tag] = make()
+    return _REFS[tag]
+
+
+def pruned_workload_ref(key: str):
+    """Oracle (y_ref, bound) over every output row of the named workload: its weight
+    magnitude-pruned 2:4 and rounded to bf16, times its activations."""
+    def make():
+        wl = workloads.WORKLOADS[key]
+        W = workloads.weights(wl)
+        values, meta = O.compress_24(W, "f32")
+        return O.gemm_ref(O.decompress_24(values, meta, wl.K), workloads.activations(wl))
+    return cached_ref(("pruned", key), make)
+
+
+def check_full(Y, y_ref, bound, out: str):
+    """Every output element of Y against the oracle's bound; returns the worst err/tol."""
+    ok, worst = O.check(y_host(Y), y_ref, bound, out)
+    assert ok, f"worst err/tol {worst}"
+    return worst

@@ -12,16 +12,16 @@ import pytest
 
 import workloads
 from oracle import prune24 as O
-from gpu_util import bf16_dev, f32_dev, need_gpu, sample_rows, torch, y_host
+from gpu_util import bf16_dev, check_full, f32_dev, need_gpu, pruned_workload_ref, torch, y_host
 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
 
 
-def _check(Y, W, Xb, out, rows=None):
+def _check(Y, W, Xb, out):
     v, m = O.compress_24(W, "f32")
-    y_ref, bnd = O.gemm_ref(O.decompress_24(v, m, W.shape[1]), Xb, rows=rows)
-    ok, worst = O.check(y_host(Y, rows), y_ref, bnd, out)
+    y_ref, bnd = O.gemm_ref(O.decompress_24(v, m, W.shape[1]), Xb)
+    ok, worst = O.check(y_host(Y), y_ref, bnd, out)
     assert ok, f"worst err/tol {worst}"
 
 
@@ -98,9 +98,7 @@ def test_decomp_workloads(key):
     c = p24.compress(f32_dev(W))
     Y = p24.spmm24(c, bf16_dev(Xb), out_dtype=torch.bfloat16, algo="decomp_mfma")
     torch.cuda.synchronize()
-    rows = sample_rows(wl.M, 40, seed=6)
-    _check(Y, W, Xb, "bf16", rows)
-    assert torch.isfinite(Y).all().item()
+    check_full(Y, *pruned_workload_ref(key), "bf16")
 
 
 def test_decomp_deterministic():

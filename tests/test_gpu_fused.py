@@ -11,7 +11,7 @@ import pytest
 
 import workloads
 from oracle import prune24 as O
-from gpu_util import bf16_dev, f32_dev, need_gpu, sample_rows, torch, y_host
+from gpu_util import bf16_dev, f32_dev, need_gpu, torch, y_host
 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
@@ -31,10 +31,10 @@ def _run(W, Xb, bias, act, out, order):
     return c, Y
 
 
-def _check(Y, W, Xb, bias, act, out, rows=None):
+def _check(Y, W, Xb, bias, act, out):
     v, m = O.compress_24(W, "f32")
-    y_ref, z_ref, bnd = O.fused_ref(O.decompress_24(v, m, W.shape[1]), Xb, bias, ACTS[act], rows=rows)
-    ok, worst = O.check_fused(y_host(Y, rows), y_ref, z_ref, bnd, ACTS[act], out)
+    y_ref, z_ref, bnd = O.fused_ref(O.decompress_24(v, m, W.shape[1]), Xb, bias, ACTS[act])
+    ok, worst = O.check_fused(y_host(Y), y_ref, z_ref, bnd, ACTS[act], out)
     assert ok, f"worst err/tol {worst}"
 
 
@@ -99,8 +99,7 @@ def test_fused_workloads(key, act):
     Xb = workloads.activations(wl)
     bias = (0.1 * np.random.default_rng(7).standard_normal(wl.M)).astype(np.float32)
     _, Y = _run(W, Xb, bias, act, "bf16", "kn")
-    rows = sample_rows(wl.M, 40, seed=8)
-    _check(Y, W, Xb, bias, act, "bf16", rows)
+    _check(Y, W, Xb, bias, act, "bf16")
     if act == "relu":
         assert (Y >= 0).all().item()
 

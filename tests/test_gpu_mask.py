@@ -7,7 +7,7 @@ import pytest
 
 import workloads
 from oracle import prune24 as O
-from gpu_util import bf16_dev, f32_dev, need_gpu, sample_rows, torch, u16_host, u32_host
+from gpu_util import bf16_dev, check_full, f32_dev, need_gpu, pruned_workload_ref, torch, u16_host, u32_host
 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
@@ -110,32 +110,25 @@ def test_fine_tune_loop():
 
 
 def test_refresh_and_mask_at_bench_size():
-    """The 8192 x 8192 fp32 weight the benchmark re-prunes: sampled rows of the in-place result, of a
-    foreign mask and of the product with the re-compressed weight against the oracle."""
+    """The 8192 x 8192 fp32 weight the benchmark re-prunes: every row of the in-place result,
+    of a foreign mask and of the product with the re-compressed weight against the oracle."""
     need_gpu()
     wl = workloads.WORKLOADS["c4"]
     W = workloads.weights(wl)
-    rows = sample_rows(wl.M, 24, seed=9)
     print("[mask] refresh 8192^2", flush=True)
     Wd = f32_dev(W)
     c = p24.refresh(Wd)
     torch.cuda.synchronize()
-    got = Wd[torch.as_tensor(rows, device=Wd.device)].cpu().numpy()
-    assert np.array_equal(got.view(np.uint32), O.prune_24(W[rows]).view(np.uint32))
+    assert np.array_equal(Wd.cpu().numpy().view(np.uint32), O.prune_24(W).view(np.uint32))
     print("[mask] mask_apply 8192^2", flush=True)
-    V = f32_dev(workloads.random_matrix((wl.M, wl.K), seed=11, sigma=0.02))
-    Vh = V[torch.as_tensor(rows, device=V.device)].cpu().numpy()
+    Vh = workloads.random_matrix((wl.M, wl.K), seed=11, sigma=0.02)
+    V = f32_dev(Vh)
     p24.mask_apply(V, c)
     torch.cuda.synchronize()
-    _, meta = O.compress_24(W[rows])
-    got = V[torch.as_tensor(rows, device=V.device)].cpu().numpy()
-    assert np.array_equal(got.view(np.uint32), O.mask_apply(Vh, meta).view(np.uint32))
+    _, meta = O.compress_24(W)
+    assert np.array_equal(V.cpu().numpy().view(np.uint32), O.mask_apply(Vh, meta).view(np.uint32))
     print("[mask] spmm24 on the re-pruned weight", flush=True)
     Xb = workloads.activations(wl)
     Y = p24.spmm24(c, bf16_dev(Xb), out_dtype=torch.float32)
     torch.cuda.synchronize()
-    values, meta = O.compress_24(W[rows])
-    y_ref, bnd = O.gemm_ref(O.decompress_24(values, meta, wl.K), Xb)
-    y = Y[torch.as_tensor(rows, device=Y.device)].cpu().numpy().astype(np.float64)
-    ok, worst = O.check(y, y_ref, bnd, "f32")
-    assert ok, worst
+    check_full(Y, *pruned_workload_ref("c4"), "f32")

@@ -4,7 +4,7 @@ Tolerance: |y - y_ref| <= 1e-3 * (|W|.|X|)_ij on fp32 output; a bf16 output
 also gets the half-ulp of its final rounding (see oracle.prune24.tolerance).
 Exact pins: integer data (every partial sum exact in fp32) and X = I.
 Full-size workloads run in the launch configuration the benchmark uses and
-are checked on sampled rows the oracle computes one by one.
+are checked on every output element.
 """
 import os
 
@@ -13,7 +13,8 @@ import pytest
 
 import workloads
 from oracle import prune24 as O
-from gpu_util import DEV, bf16_dev, f32_dev, need_gpu, sample_rows, torch, u16_host, y_host
+from gpu_util import (DEV, bf16_dev, cached_ref, check_full, f32_dev, need_gpu, pruned_workload_ref, torch,
+                      u16_host, y_host)
 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
@@ -30,11 +31,11 @@ def _run_sparse(W, Xb, out_dtype, x_pad=0):
     return c, Y
 
 
-def _check(Y, W, Xb, out, rows=None):
+def _check(Y, W, Xb, out):
     values, meta = O.compress_24(W, "f32")
     K = W.shape[1]
-    y_ref, bnd = O.gemm_ref(O.decompress_24(values, meta, K), Xb, rows=rows)
-    ok, worst = O.check(y_host(Y, rows), y_ref, bnd, out)
+    y_ref, bnd = O.gemm_ref(O.decompress_24(values, meta, K), Xb)
+    ok, worst = O.check(y_host(Y), y_ref, bnd, out)
     assert ok, f"worst err/tol {worst}"
     return worst
 
@@ -93,9 +94,7 @@ def test_workloads_full_size(key, out):
     W = workloads.weights(wl)
     Xb = workloads.activations(wl)
     _, Y = _run_sparse(W, Xb, torch.float32 if out == "f32" else torch.bfloat16)
-    rows = None if wl.M * wl.N <= 1 << 22 else sample_rows(wl.M, 48, seed=5)
-    _check(Y, W, Xb, out, rows)
-    assert torch.isfinite(Y).all().item()
+    check_full(Y, *pruned_workload_ref(key), out)
 
 
 def test_deterministic():
@@ -138,10 +137,7 @@ def test_dense_workloads(key):
     Wb = workloads.truncate_to_bf16_bits(workloads.weights(wl))
     Xb = workloads.activations(wl)
     Y = _run_dense(Wb, Xb, torch.bfloat16)
-    rows = sample_rows(wl.M, 32, seed=9)
-    y_ref, bnd = O.gemm_ref(Wb, Xb, rows=rows)
-    ok, worst = O.check(y_host(Y, rows), y_ref, bnd, "bf16")
-    assert ok, worst
+    check_full(Y, *cached_ref(("dense", key), lambda: O.gemm_ref(Wb, Xb)), "bf16")
 
 
 def test_zero_sized_noop():

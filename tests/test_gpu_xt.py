@@ -9,7 +9,7 @@ import pytest
 
 import workloads
 from oracle import prune24 as O
-from gpu_util import bf16_dev, f32_dev, need_gpu, sample_rows, torch, u16_host, y_host
+from gpu_util import bf16_dev, check_full, f32_dev, need_gpu, pruned_workload_ref, torch, u16_host, y_host
 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
@@ -85,11 +85,7 @@ def test_spmm24_xt_workloads(key):
     Yk = p24.spmm24(c, Xt, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert torch.equal(Y.view(torch.int16), Yk.view(torch.int16))
-    rows = sample_rows(wl.M, 40, seed=4)
-    v, m = O.compress_24(W, "f32")
-    y_ref, bnd = O.gemm_ref(O.decompress_24(v, m, wl.K), Xb, rows=rows)
-    ok, worst = O.check(y_host(Y, rows), y_ref, bnd, "bf16")
-    assert ok, worst
+    check_full(Y, *pruned_workload_ref(key), "bf16")
 
 
 @pytest.mark.parametrize("M,K,N", [(96, 128, 72), (300, 256, 200), (1024, 512, 640)])
