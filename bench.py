@@ -16,7 +16,13 @@ Beside the headline, the same run times (HIP events on the launch stream):
     rows scaled 1 +- 0.1): tvw_var_compress + spmm_tvw_var,
 and the CPU oracle on a bounded sample of the headline workload.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Before the warmup, --preheat-s seconds (default 2) of back-to-back headline
+launches bring the chip to the clock it holds under this load; the line reports
+them as "preheat", and the per-launch times of the timed region as
+rows.spmm24_launch_us.  A helper process reads the XCD clocks during the
+pre-heat and the timed region ("clock").
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--preheat-s S] [--no-cpu-baseline]
        [--only spmm|dense|compress|tvw|copy]  (profiling aid: run one kernel only)
 Prints ONE JSON line.
 """
@@ -47,7 +53,11 @@ def parse():
     ap.add_argument("--only", choices=["spmm", "xt", "decomp", "dense", "compress", "tvw", "copy"], default=None)
     ap.add_argument("--workload", default="c4", help="headline workload key (default c4)")
     ap.add_argument("--no-clock", action="store_true",
-                    help="skip the clock leg (GPU clocks read with amd-smi during back-to-back spmm24 launches)")
+                    help="do not read the GPU clocks (a helper process reads them during the pre-heat and the "
+                         "timed region)")
+    ap.add_argument("--preheat-s", type=float, default=2.0,
+                    help="seconds of back-to-back headline launches before the warmup, reported in the line as "
+                         "'preheat' (0: none)")
     ap.add_argument("--clock-sampler", default=None, help=argparse.SUPPRESS)   # internal: helper process mode
     ap.add_argument("--table", action="store_true",
                     help="instead of the headline line, time every workload (spmm24, spmm24_xt, dense) and "
@@ -163,25 +173,59 @@ def parse_gfx_clocks(text):
     return []
 
 
+def gfx_clocks_from_metrics(metrics):
+    """XCD graphics clocks (MHz) from an amdsmi gpu-metrics dict: `current_gfxclks`, leaving
+    out entries that are not numbers or read as 0 / 0xFFFF (XCDs the table does not fill)."""
+    vals = metrics.get("current_gfxclks") if isinstance(metrics, dict) else None
+    if not isinstance(vals, (list, tuple)):
+        return []
+    return [float(v) for v in vals if isinstance(v, (int, float)) and 0 < v < 0xFFFF]
+
+
+def _amdsmi_reader():
+    """A function returning GPU 0's XCD clocks through the amdsmi library (fast: a few
+    readings per millisecond of GPU work), or None when the library cannot read them."""
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        handle = amdsmi.amdsmi_get_processor_handles()[0]
+        read = lambda: gfx_clocks_from_metrics(amdsmi.amdsmi_get_gpu_metrics_info(handle))
+        return read if read() else None
+    except Exception:
+        return None
+
+
 def clock_sampler(path):
-    """Helper process: append one line per amd-smi reading to `path` (start and end of the
-    reading as unix times, then the MHz of each XCD) until the parent process exits.  It is
-    started before the parent touches the GPU and never uses the GPU itself."""
+    """Helper process: append one line per clock reading to `path` (start and end of the
+    reading as unix times, then the MHz of each XCD) until the parent process exits.  It
+    reads through the amdsmi library every ~2 ms when it can, else through the amd-smi
+    command every ~0.1 s.  It is started before the parent touches the GPU and never uses
+    the GPU itself."""
     import subprocess
     parent = os.getppid()
+    fast = _amdsmi_reader()
+
+    def slow():
+        try:
+            r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
+                               text=True, timeout=10)
+            return parse_gfx_clocks(r.stdout) if r.returncode == 0 else []
+        except Exception:
+            return []
+    read, pause = (fast, 0.002) if fast else (slow, 0.1)
     with open(path, "a") as f:
+        f.write(f"# source {'amdsmi gpu metrics' if fast else 'amd-smi metric --clock'}\n")
+        f.flush()
         while os.getppid() == parent:
             t0 = time.time()
             try:
-                r = subprocess.run(["amd-smi", "metric", "--clock", "--json"], capture_output=True,
-                                   text=True, timeout=10)
-                mhz = parse_gfx_clocks(r.stdout) if r.returncode == 0 else []
+                mhz = read()
             except Exception:
                 mhz = []
             if mhz:
-                f.write(f"{t0:.3f} {time.time():.3f} " + " ".join(f"{m:.0f}" for m in mhz) + "\n")
+                f.write(f"{t0:.4f} {time.time():.4f} " + " ".join(f"{m:.0f}" for m in mhz) + "\n")
                 f.flush()
-            time.sleep(0.1)
+            time.sleep(pause)
 
 
 def under_profiler(env=None):
@@ -208,19 +252,39 @@ def start_clock_sampler():
     return proc, path
 
 
-def read_clock_samples(path, t_lo, t_hi):
-    """Per-reading mean XCD clock (MHz) of the readings that lie wholly inside [t_lo, t_hi]."""
+def clock_source(path):
+    """The reading method the sampler wrote on its first line, or None."""
+    try:
+        with open(path) as f:
+            first = f.readline()
+    except OSError:
+        return None
+    return first[len("# source "):].strip() if first.startswith("# source ") else None
+
+
+def refresh_ms_est(timed):
+    """Mean time (ms) between changes of the reading, from (time, MHz) pairs: how often the
+    table behind the readings refreshes.  None with fewer than two changes."""
+    changes = [t for (t, m), (_, prev) in zip(timed[1:], timed[:-1]) if m != prev]
+    if len(changes) < 2:
+        return None
+    return round((changes[-1] - changes[0]) * 1e3 / (len(changes) - 1), 1)
+
+
+def read_clock_samples(path, t_lo, t_hi, with_time=False):
+    """Per-reading mean XCD clock (MHz) of the readings that lie wholly inside [t_lo, t_hi]
+    (with_time: (start time, MHz) pairs)."""
     out = []
     try:
         with open(path) as f:
             for line in f:
                 parts = line.split()
-                if len(parts) < 3:
+                if len(parts) < 3 or parts[0].startswith("#"):
                     continue
                 a, b = float(parts[0]), float(parts[1])
                 if a >= t_lo and b <= t_hi:
                     mhz = [float(x) for x in parts[2:]]
-                    out.append(sum(mhz) / len(mhz))
+                    out.append((a, sum(mhz) / len(mhz)) if with_time else sum(mhz) / len(mhz))
     except OSError:
         pass
     return out
@@ -243,6 +307,37 @@ def measured_traffic(path=None, src=None):
     if not (b and h) or not digest.startswith(h.group(1)):
         return None
     return int(b.group(1))
+
+
+TRAFFIC_PROFILE = "profiles/spmm24_8192cube_hbm_traffic.md"
+
+
+def traffic_source(traffic):
+    """Where roofline.traffic comes from (it is not measured in the bench run itself)."""
+    if traffic is None:
+        return ("null: no committed counter summary for this workload, or the kernel source changed "
+                "since the counters were taken")
+    return (f"{TRAFFIC_PROFILE}: rocprofv3 --pmc FETCH_SIZE and WRITE_SIZE of the same kernel, scaled by a "
+            f"1 GiB copy; reported only while the sha256 of csrc/gemm.hip matches the one recorded there")
+
+
+def spmm24_kernel(M, N, env=None):
+    """The k_gemm instantiation spmm24 launches for an M x N output, by the library's tile rule:
+    the first of 256x256, 128x256, 128x128, 64x128 that gives at least 160 blocks (else
+    64x128), or the tile P24_TILE forces."""
+    env = os.environ if env is None else env
+    waves = {"256x256": (2, 4), "128x256": (2, 4), "128x128": (2, 4), "64x128": (2, 2)}
+    tile = env.get("P24_TILE") if env.get("P24_TILE") in waves else None
+    if tile is None:
+        tile = "64x128"
+        for t in ("256x256", "128x256", "128x128", "64x128"):
+            bm, bn = (int(v) for v in t.split("x"))
+            if -(-M // bm) * -(-N // bn) >= 160:
+                tile = t
+                break
+    bm, bn = tile.split("x")
+    wm, wn = waves[tile]
+    return f"k_gemm<{bm},{bn},{wm},{wn},sparse,X_KN> (spmm24)"
 
 
 COLD_BYTES = 512 << 20
@@ -434,19 +529,47 @@ def main():
     def step():
         p24.spmm24(c, Xt, out=Y)
 
+    preheat = None
+    clock_pre, clock_timed, clock_pre_t = [], [], []
     if args.only in (None, "spmm"):
+        # Declared pre-heat: back-to-back headline launches for --preheat-s seconds, so that
+        # the timed region starts at the clock and power state the chip holds under this
+        # load, not in the ramp out of idle.  Its launches are not timed; the line reports it.
+        if args.preheat_s > 0:
+            n_pre, t_a = 0, time.time()
+            while time.time() - t_a < args.preheat_s:
+                for _ in range(50):
+                    step()
+                n_pre += 50
+                torch.cuda.synchronize()
+            t_b = time.time()
+            preheat = {"seconds": round(t_b - t_a, 2), "launches": n_pre,
+                       "what": "back-to-back spmm24 launches on the headline workload before the warmup, not "
+                               "timed"}
+            if clk_path:
+                t_lo = t_a + min(1.0, 0.5 * (t_b - t_a))
+                clock_pre = read_clock_samples(clk_path, t_lo, t_b)
+                clock_pre_t = read_clock_samples(clk_path, t_lo, t_b, with_time=True)
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        t_w0 = time.time()
         t0 = time.perf_counter()
         ev = event_times_ms(torch, step, args.steps)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        t_w1 = time.time()
+        if clk_path:
+            time.sleep(0.05)            # let the sampler write its last reading of the region
+            clock_timed = read_clock_samples(clk_path, t_w0, t_w1)
         ms_per_step = wall * 1e3 / args.steps
         launch_ms = sum(ev) / len(ev)
         rows["spmm24_us_mean"] = launch_ms * 1e3
         rows["spmm24_us_median"] = median(ev) * 1e3
         rows["spmm24_us_min"] = min(ev) * 1e3
+        rows["spmm24_us_max"] = max(ev) * 1e3
+        # every launch of the timed region, in order (a transient shows as a trend)
+        rows["spmm24_launch_us"] = [round(e * 1e3, 1) for e in ev]
     if args.only is None:
         # context: the same launches alternating between two full input/output sets
         # (688 MB, beyond the 256 MB MALL), so each launch finds its inputs only in HBM
@@ -461,15 +584,7 @@ def main():
         del c2, X2, Y2, alt
     clock = None
     if clk_proc is not None:
-        # about 4 s of back-to-back launches while the sampler reads the XCD clocks;
-        # readings from the first second (clock ramp) are left out
-        t_a = time.time()
-        while time.time() - t_a < 4.0:
-            for _ in range(200):
-                step()
-            torch.cuda.synchronize()
-        t_b = time.time()
-        mhz = read_clock_samples(clk_path, t_a + 1.0, t_b)
+        src = clock_source(clk_path)
         clk_proc.terminate()
         try:
             clk_proc.wait(timeout=10)
@@ -479,13 +594,20 @@ def main():
             os.remove(clk_path)
         except OSError:
             pass
+        # The figure is the median over the pre-heat's readings after its first second (the
+        # same kernel, back to back, just before the timed region), so that a reading taken
+        # while the clocks dip (it happens) does not move it.  The timed region's own readings
+        # are listed beside it: the metrics table behind them refreshes every few tens of
+        # milliseconds or more (refresh_ms_est), longer than a region of 20 launches, so
+        # they can still show the state before the region.
+        mhz = clock_pre or clock_timed
         if mhz:
-            # the median: a reading taken while the clocks dip (it happens) does not move it
             clock = {"sclk_mhz_median": round(median(mhz), 1), "sclk_mhz_min": min(mhz),
                      "sclk_mhz_max": max(mhz), "readings": len(mhz), "published_mhz": 2400.0,
-                     "source": "amd-smi metric --clock: median over readings of the mean XCD graphics "
-                               "clock, read during 4 s of back-to-back spmm24 launches on the headline "
-                               "workload"}
+                     "window": "pre-heat after its first second" if clock_pre else "timed region",
+                     "timed_region_sclk_mhz": [round(m, 1) for m in clock_timed],
+                     "refresh_ms_est": refresh_ms_est(clock_pre_t),
+                     "source": f"{src}: mean of the XCD graphics clocks per reading, median over readings"}
     if args.only == "spmm":
         print(json.dumps(rows))
         return
@@ -580,6 +702,16 @@ def main():
         rows["spmm_tvw_c5_dense_eq_tflops"] = wt.dense_flops / (rows["spmm_tvw_c5_us_mean"] * 1e-6) / 1e12
         ev5c = event_times_ms(torch, lambda: p24.tvw_compress(W5, tile_m=wt.tile_m, keep_k=wt.keep_k), 3)
         rows["tvw_compress_c5_us_mean"] = sum(ev5c) / len(ev5c) * 1e3
+        # this project's dense bf16 GEMM of the unpruned c5 weight: the TVW speedup's denominator
+        Wp5 = p24.pack_dense(to_bf16(workloads.truncate_to_bf16_bits(workloads.weights(wt))))
+        Yd5 = torch.empty_like(Y5)
+        d5step = lambda: p24.gemm_bf16(Wp5, wt.M, wt.K, X5, out=Yd5)
+        for _ in range(args.warmup):
+            d5step()
+        ev5d = event_times_ms(torch, d5step, max(args.steps, 5))
+        rows["gemm_bf16_c5_us_mean"] = sum(ev5d) / len(ev5d) * 1e3
+        rows["speedup_tvw_vs_dense_c5"] = rows["gemm_bf16_c5_us_mean"] / rows["spmm_tvw_c5_us_mean"]
+        del Wp5, Yd5
         # per-tile keep counts (same total of kept columns, tiles of different importance)
         wv = workloads.WORKLOADS["c5v"]
         W5v = torch.from_numpy(workloads.weights(wv)).to(dev)
@@ -599,11 +731,13 @@ def main():
 
     value = wl.dense_flops / (ms_per_step * 1e-3) / 1e12
     achieved = wl.kept_flops / (launch_ms * 1e-3) / 1e12
+    traffic = measured_traffic() if wl.key == "c4" else None
     rows["speedup_vs_dense"] = rows["gemm_bf16_us_mean"] / rows["spmm24_us_mean"]
     rows["speedup_vs_torch_matmul"] = rows["torch_matmul_us_mean"] / rows["spmm24_us_mean"]
     # context: hipBLASLt on its fastest layout here (both operands K-contiguous)
     rows["speedup_vs_torch_linear_tn"] = rows["torch_linear_tn_us_mean"] / rows["spmm24_us_mean"]
     rows["dense_eq_frac_of_sparse_peak"] = (wl.dense_flops / (launch_ms * 1e-3) / 1e12) / (2 * PEAK_BF16_MFMA_TFLOPS)
+    rows["speedup_vs_dense_median"] = rows["gemm_bf16_us_mean"] / rows["spmm24_us_median"]
     out = {
         "metric": "dense-equiv TFLOP/s of 2:4 SpMM (bf16, 1 MI355X); speedup vs dense GEMM",
         "value": round(value, 2),
@@ -625,11 +759,15 @@ def main():
             "peak": PEAK_BF16_MFMA_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_BF16_MFMA_TFLOPS, 4),
-            "traffic": measured_traffic() if wl.key == "c4" else None,
-            "kernel": "k_gemm<256,256,2,4,sparse,X_KN> (spmm24)",
+            "traffic": traffic,
+            "traffic_source": traffic_source(traffic),
+            "kernel": spmm24_kernel(wl.M, wl.N),
             "algorithmic_flops_per_launch": wl.kept_flops,
+            "launch_us_mean": round(launch_ms * 1e3, 2),
         },
+        "preheat": preheat,
         "speedup_vs_dense": round(rows["speedup_vs_dense"], 3),
+        "speedup_tvw_vs_dense_c5": round(rows["speedup_tvw_vs_dense_c5"], 3),
         "rows": {k: (round(v, 3) if isinstance(v, float) else v) for k, v in rows.items()},
     }
     if clock is not None:

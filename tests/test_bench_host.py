@@ -85,3 +85,44 @@ def test_cpu_baseline_on_the_small_workload():
     assert cb["sample"].startswith(f"{wl.M} of {wl.M} output rows of c1")
     assert cb["prune_compress_s"] >= 0 and cb["gemm_and_bound_s"] >= 0
     assert set(cb) >= {"cpu_model", "blas"}
+
+
+def test_spmm24_kernel_label_follows_the_tile_rule():
+    """The roofline's kernel name is the instantiation the library's tile rule picks."""
+    import workloads
+    want = {"c1": "64x128", "c2": "256x256", "c3a": "128x128", "c3b": "64x128", "c4": "256x256",
+            "c4n8": "128x256", "c4m8": "128x256"}
+    for key, tile in want.items():
+        wl = workloads.WORKLOADS[key]
+        bm, bn = tile.split("x")
+        assert bench.spmm24_kernel(wl.M, wl.N, env={}).startswith(f"k_gemm<{bm},{bn},"), key
+    assert bench.spmm24_kernel(8192, 8192, env={}) == "k_gemm<256,256,2,4,sparse,X_KN> (spmm24)"
+    assert bench.spmm24_kernel(8192, 8192, env={"P24_TILE": "128x128"}).startswith("k_gemm<128,128,2,4,")
+    assert bench.spmm24_kernel(8192, 8192, env={"P24_TILE": "bogus"}).startswith("k_gemm<256,256,")
+
+
+def test_traffic_source_says_where_the_figure_comes_from():
+    assert bench.traffic_source(None).startswith("null")
+    assert bench.traffic_source(123).startswith(bench.TRAFFIC_PROFILE)
+
+
+def test_gfx_clocks_from_metrics_and_sampler_header(tmp_path):
+    m = {"current_gfxclks": [1850, 1860, 65535, 0, "N/A", 1870, 1880, 1890], "other": 1}
+    assert bench.gfx_clocks_from_metrics(m) == [1850.0, 1860.0, 1870.0, 1880.0, 1890.0]
+    assert bench.gfx_clocks_from_metrics({"current_gfxclks": "N/A"}) == []
+    assert bench.gfx_clocks_from_metrics(None) == []
+    p = tmp_path / "clk.txt"
+    p.write_text("# source amdsmi gpu metrics\n1.0 1.1 1800 1900\n")
+    assert bench.clock_source(str(p)) == "amdsmi gpu metrics"
+    assert bench.read_clock_samples(str(p), 0.0, 2.0) == [1850.0]
+    assert bench.clock_source(str(tmp_path / "none.txt")) is None
+
+
+def test_refresh_estimate_counts_changes_of_the_reading(tmp_path):
+    p = tmp_path / "clk.txt"
+    p.write_text("# source amdsmi gpu metrics\n" +
+                 "".join(f"{0.005 * i:.4f} {0.005 * i + 0.001:.4f} {1800 + 10 * (i // 10)}\n" for i in range(100)))
+    timed = bench.read_clock_samples(str(p), 0.0, 1.0, with_time=True)
+    assert len(timed) == 100 and timed[0] == (0.0, 1800.0)
+    assert bench.refresh_ms_est(timed) == 50.0          # the value changes every 10 readings of 5 ms
+    assert bench.refresh_ms_est(timed[:5]) is None
