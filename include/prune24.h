@@ -90,7 +90,8 @@ enum {
   P24_ERR_UNSUPPORTED = -5,  /* valid request the library does not implement (e.g. K % 64) */
   P24_ERR_HIP = -6,          /* the HIP runtime reported an error at launch */
   P24_ERR_WORKSPACE = -7,    /* workspace NULL or smaller than required */
-  P24_ERR_LAYOUT = -8        /* unknown layout code, or layout not accepted here */
+  P24_ERR_LAYOUT = -8,       /* unknown layout code, or layout not accepted here */
+  P24_ERR_SCRATCH = -9       /* larger than the fixed scratch of a no-allocation entry point */
 };
 
 enum { P24_F32 = 0, P24_BF16 = 1 };                         /* element dtypes */
@@ -236,8 +237,8 @@ P24_API p24_status transpose_bf16(const void* src, int64_t rows, int64_t cols, i
  * tvw_compress -- TVW selection and compression of fp32 W.
  *   Tile t covers output rows [t*tile_m, min(M, (t+1)*tile_m)).  Its column
  *   score is the fp64 sum over those rows, in ascending row order, of |W[m][k]|;
- *   the keep_k columns with the largest score (ties -> lower k; scores compare
- *   by their fp64 bit pattern, so NaN ranks highest) are kept, listed ascending
+ *   the keep_k columns with the largest score (ties -> lower k; a NaN score
+ *   ranks above +Inf and NaN scores tie, whatever their payload) are kept, listed ascending
  *   in kept[t][0..keep_k).  The tile's rows restricted to those columns are then
  *   compressed 2:4 exactly as prune24_compress does, along the compacted axis.
  *   W         M x K fp32 (w_dtype must be P24_F32), ldw % 4 == 0, 16 B aligned;
@@ -254,6 +255,31 @@ P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64_t M, int64
                                 int64_t ldw, int64_t tile_m, int64_t keep_k, int32_t* kept,
                                 void* values, void* meta, int32_t layout, void* workspace,
                                 size_t ws_bytes, void* stream);
+
+/*
+ * tvw_compress_noalloc -- tvw_compress for callers that cannot allocate device
+ *   memory (code under HIP graph capture, tight serving loops, harnesses that
+ *   forbid hipMalloc): no workspace argument, and the call allocates and frees
+ *   nothing.  The column scores go to a fixed scratch array in device memory
+ *   that the library holds on every GPU it runs on until the process ends,
+ *   tvw_noalloc_scratch_bytes() bytes (8 MiB) per GPU.
+ *   Same arguments, outputs and errors as tvw_compress without workspace and
+ *   ws_bytes, plus:
+ *     P24_ERR_SCRATCH      tvw_workspace_bytes(M, K, tile_m, keep_k) exceeds
+ *                          the scratch (nothing is enqueued);
+ *     P24_ERR_UNSUPPORTED  `stream` belongs to another device than the current
+ *                          one (the current device's scratch is used);
+ *     P24_ERR_HIP          the scratch address could not be looked up.
+ *   The first call on a device looks up that device's scratch address
+ *   (thread-safe); later calls reuse it.  Every call on one GPU shares that
+ *   GPU's scratch: calls that overlap on one GPU (two streams, two host
+ *   threads) race and give undefined results; calls in one stream are
+ *   ordered and safe.  Nothing in the scratch needs to start at zero.
+ */
+P24_API size_t tvw_noalloc_scratch_bytes(void);
+P24_API p24_status tvw_compress_noalloc(const void* W, int32_t w_dtype, int64_t M, int64_t K,
+                                        int64_t ldw, int64_t tile_m, int64_t keep_k, int32_t* kept,
+                                        void* values, void* meta, int32_t layout, void* stream);
 
 /*
  * spmm_tvw -- Y = W X for a TVW-compressed W: for output rows of tile t,

@@ -38,6 +38,7 @@ P24_ERR_UNSUPPORTED = -5
 P24_ERR_HIP = -6
 P24_ERR_WORKSPACE = -7
 P24_ERR_LAYOUT = -8
+P24_ERR_SCRATCH = -9
 P24_F32, P24_BF16 = 0, 1
 P24_LAYOUT_CANONICAL, P24_LAYOUT_DEVICE = 0, 1
 P24_ALGO_AUTO, P24_ALGO_SMFMAC, P24_ALGO_DECOMP_MFMA = 0, 1, 2
@@ -63,6 +64,9 @@ _SIGNATURES = {
     "tvw_workspace_bytes": (_c_size, [_c_i64, _c_i64, _c_i64, _c_i64]),
     "tvw_compress": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp,
                               _c_i32, _c_vp, _c_size, _c_vp]),
+    "tvw_noalloc_scratch_bytes": (_c_size, []),
+    "tvw_compress_noalloc": (_c_i32, [_c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_vp, _c_vp,
+                                      _c_i32, _c_vp]),
     "spmm_tvw": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
                           _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
     "spmm_tvw_fused": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
@@ -430,6 +434,34 @@ def tvw_compress(W, tile_m: int = 128, keep_k: int | None = None, layout="device
     _check(L.tvw_compress(_ptr(W), P24_F32, M, K, ldw, tile_m, keep_k, _ptr(kept), _ptr(values), _ptr(meta),
                           lc, _ptr(ws), ws.numel(), _stream(W.device)), "tvw_compress")
     return CompressedTVW(kept, values, meta, M, K, tile_m, keep_k, lc)
+
+
+def tvw_compress_noalloc(W, tile_m: int = 128, keep_k: int | None = None, layout="device", out=None):
+    """tvw_compress through the library's no-allocation entry point (its fixed device scratch,
+    no workspace).  `out`, a CompressedTVW of the same shape, receives the result in place
+    (then nothing is allocated here either); without it the output tensors are new."""
+    torch = _torch()
+    _require_cuda(W, "W")
+    if W.dtype != torch.float32:
+        raise ValueError("tvw_compress_noalloc takes fp32 W")
+    ldw = _rowmajor(W, "W")
+    M, K = W.shape
+    keep_k = K // 2 if keep_k is None else int(keep_k)
+    lc = _layout_code(layout)
+    L = lib()
+    T = (M + tile_m - 1) // tile_m
+    if out is None:
+        vb, mb = L.prune24_values_bytes(M, keep_k, lc), L.prune24_meta_bytes(M, keep_k, lc)
+        out = CompressedTVW(torch.empty((T, keep_k), dtype=torch.int32, device=W.device),
+                            torch.empty(max(vb // 2, 1), dtype=torch.bfloat16, device=W.device),
+                            torch.empty(max(mb // 4, 1), dtype=torch.int32, device=W.device),
+                            M, K, tile_m, keep_k, lc)
+    elif (out.M, out.K, out.tile_m, out.keep_k, out.layout) != (M, K, tile_m, keep_k, lc):
+        raise ValueError("out was made for another shape, tile, keep count or layout")
+    _operands_on(W.device, (out.kept, "kept"), (out.values, "values"), (out.meta, "meta"))
+    _check(L.tvw_compress_noalloc(_ptr(W), P24_F32, M, K, ldw, tile_m, keep_k, _ptr(out.kept), _ptr(out.values),
+                                  _ptr(out.meta), lc, _stream(W.device)), "tvw_compress_noalloc")
+    return out
 
 
 def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None, bias=None, act="none"):

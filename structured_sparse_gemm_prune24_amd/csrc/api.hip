@@ -14,6 +14,7 @@ extern "C" P24_API const char* prune24_strerror(p24_status s) {
     case P24_ERR_HIP: return "HIP runtime error at kernel launch";
     case P24_ERR_WORKSPACE: return "workspace missing or too small";
     case P24_ERR_LAYOUT: return "unknown layout, or layout not accepted by this entry point";
+    case P24_ERR_SCRATCH: return "problem larger than the fixed scratch of the no-allocation entry point";
     default: return "unknown status";
   }
 }

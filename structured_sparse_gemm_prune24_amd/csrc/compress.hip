@@ -4,6 +4,7 @@
 #include "p24_device.hpp"
 
 #include <algorithm>
+#include <mutex>
 
 namespace p24 {
 
@@ -990,10 +991,11 @@ extern "C" P24_API size_t tvw_workspace_bytes(int64_t M, int64_t K, int64_t tile
   return (size_t)((M + tile_m - 1) / tile_m) * (size_t)K * sizeof(double);
 }
 
-extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
-                                           int64_t tile_m, int64_t keep_k, int32_t* kept, void* values,
-                                           void* meta, int32_t layout, void* workspace, size_t ws_bytes,
-                                           void* stream) {
+// Argument checks of tvw_compress and its no-allocation variant (everything but
+// the workspace), in the order the header gives the errors.
+static p24_status tvw_check(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw, int64_t tile_m,
+                            int64_t keep_k, const int32_t* kept, const void* values, const void* meta,
+                            int32_t layout) {
   if (w_dtype != P24_F32) return P24_ERR_DTYPE;
   if (layout != P24_LAYOUT_CANONICAL && layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
   if (M < 0 || K <= 0 || ldw < K || tile_m <= 0 || tile_m % 32 || keep_k <= 0 || keep_k > K || keep_k % 4)
@@ -1002,11 +1004,16 @@ extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64
   if (layout == P24_LAYOUT_DEVICE && keep_k % 64) return P24_ERR_UNSUPPORTED;
   if (M == 0) return P24_OK;
   if (!W || !kept || !values || !meta) return P24_ERR_NULL;
-  if (!workspace || ws_bytes < tvw_workspace_bytes(M, K, tile_m, keep_k)) return P24_ERR_WORKSPACE;
-  if (!aligned(W, 16) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4) ||
-      !aligned(workspace, 8))
+  if (!aligned(W, 16) || ldw % 4 || !aligned(values, 16) || !aligned(meta, 16) || !aligned(kept, 4))
     return P24_ERR_ALIGN;
-  hipStream_t st = (hipStream_t)stream;
+  return P24_OK;
+}
+
+// Scores into `workspace` (T x K doubles, every entry written before it is read),
+// per-tile selection, then 2:4 compression of the kept columns.
+static p24_status tvw_launch(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw, int64_t tile_m,
+                             int64_t keep_k, int32_t* kept, void* values, void* meta, int32_t layout,
+                             void* workspace, hipStream_t st) {
   const int64_t T_ = (M + tile_m - 1) / tile_m;
   double* scores = (double*)workspace;
   hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
@@ -1019,6 +1026,70 @@ extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64
   if (s != P24_OK) return s;
   // 2:4 along the compacted axis, reading W through the kept column lists
   return launch_compress<G_FIXED>(W, w_dtype, M, keep_k, ldw, values, meta, layout, kept, tile_m, K, st);
+}
+
+extern "C" P24_API p24_status tvw_compress(const void* W, int32_t w_dtype, int64_t M, int64_t K, int64_t ldw,
+                                           int64_t tile_m, int64_t keep_k, int32_t* kept, void* values,
+                                           void* meta, int32_t layout, void* workspace, size_t ws_bytes,
+                                           void* stream) {
+  p24_status s = tvw_check(W, w_dtype, M, K, ldw, tile_m, keep_k, kept, values, meta, layout);
+  if (s != P24_OK || M == 0) return s;
+  if (!workspace || ws_bytes < tvw_workspace_bytes(M, K, tile_m, keep_k)) return P24_ERR_WORKSPACE;
+  if (!aligned(workspace, 8)) return P24_ERR_ALIGN;
+  return tvw_launch(W, w_dtype, M, K, ldw, tile_m, keep_k, kept, values, meta, layout, workspace,
+                    (hipStream_t)stream);
+}
+
+// --------------------------------------------------------------------------
+// tvw_compress without an allocation or a workspace argument: the column
+// scores go to `scratch`, a fixed array in device memory (each GPU holds its
+// own copy for the life of the process).  Host code reaches it only through
+// the address hipGetSymbolAddress returns for the current device, looked up
+// once per device and kept; the array's name itself is not a device address
+// on the host.  Nothing in it has to start at zero: the score kernel writes
+// every entry the selection reads.  Calls that overlap on one GPU share it and
+// race.
+// --------------------------------------------------------------------------
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)8 << 20;
+static __device__ __align__(256) uint8_t scratch[NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MAX_DEVICES];
+
+// The scratch address on the current device, looked up on the first call there.
+static p24_status scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return P24_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return P24_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return P24_OK;
+}
+
+extern "C" P24_API size_t tvw_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
+
+extern "C" P24_API p24_status tvw_compress_noalloc(const void* W, int32_t w_dtype, int64_t M, int64_t K,
+                                                   int64_t ldw, int64_t tile_m, int64_t keep_k, int32_t* kept,
+                                                   void* values, void* meta, int32_t layout, void* stream) {
+  p24_status s = tvw_check(W, w_dtype, M, K, ldw, tile_m, keep_k, kept, values, meta, layout);
+  if (s != P24_OK || M == 0) return s;
+  if (tvw_workspace_bytes(M, K, tile_m, keep_k) > NOALLOC_SCRATCH_BYTES) return P24_ERR_SCRATCH;
+  // the stream must belong to the current device, whose copy of the scratch is used
+  if (stream) {
+    int sdev = -1, cur = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+      return P24_ERR_HIP;
+    if (sdev != cur) return P24_ERR_UNSUPPORTED;
+  }
+  void* ws = nullptr;
+  s = scratch_on_current_device(&ws);
+  if (s != P24_OK) return s;
+  return tvw_launch(W, w_dtype, M, K, ldw, tile_m, keep_k, kept, values, meta, layout, ws, (hipStream_t)stream);
 }
 
 static int64_t var_tiles(int64_t M) { return (M + 127) / 128; }

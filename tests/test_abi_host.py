@@ -21,7 +21,7 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     syms = p24.header_symbols()
-    assert len(syms) == len(set(syms)) == 35
+    assert len(syms) == len(set(syms)) == 37
     for s in syms:
         assert hasattr(L, s), s
     assert set(syms) == set(p24._SIGNATURES), "binding signatures drift from the header"
@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol(L):
 
 def test_version_and_strerror(L):
     assert L.prune24_abi_version() == 1
-    for code in range(-8, 1):
+    for code in range(-9, 1):
         assert p24.strerror(code)
     assert p24.strerror(-99) == "unknown status"
 
@@ -46,6 +46,7 @@ def test_size_helpers(L):
     assert L.prune24_values_bytes(32, 96, p24.P24_LAYOUT_DEVICE) == 0
     assert L.prune24_values_bytes(4, 6, p24.P24_LAYOUT_CANONICAL) == 0
     assert L.tvw_workspace_bytes(4096, 4096, 128, 2048) == 32 * 4096 * 8
+    assert L.tvw_noalloc_scratch_bytes() == 8 << 20
     assert L.gemm_bf16_packed_bytes(40, 128) == 64 * 128 * 2
     assert L.gemm_bf16_packed_bytes(40, 96) == 0
 
@@ -280,3 +281,21 @@ def test_dense_validation(L):
     assert L.gemm_bf16_pack(FAKE, 64, 96, 96, FAKE, NUL) == p24.P24_ERR_UNSUPPORTED
     assert L.gemm_bf16_pack(FAKE, 64, 128, 132, FAKE, NUL) == p24.P24_ERR_ALIGN
     assert L.gemm_bf16(NUL, 64, 128, FAKE, 64, 64, FAKE, 1, 64, NUL) == p24.P24_ERR_NULL
+
+
+def test_tvw_compress_noalloc_validation(L):
+    """The no-allocation variant checks its arguments as tvw_compress does, and refuses a
+    problem whose scores would not fit its fixed scratch, all before touching a device."""
+    f = L.tvw_compress_noalloc
+    assert f(FAKE, 1, 256, 256, 256, 128, 128, FAKE, FAKE, FAKE, 1, NUL) == p24.P24_ERR_DTYPE
+    assert f(FAKE, 0, 256, 256, 256, 128, 128, FAKE, FAKE, FAKE, 7, NUL) == p24.P24_ERR_LAYOUT
+    assert f(FAKE, 0, 256, 256, 256, 100, 128, FAKE, FAKE, FAKE, 1, NUL) == p24.P24_ERR_SHAPE     # tile % 32
+    assert f(FAKE, 0, 256, 256, 256, 128, 130, FAKE, FAKE, FAKE, 0, NUL) == p24.P24_ERR_SHAPE     # keep % 4
+    assert f(FAKE, 0, 256, 256, 256, 128, 100, FAKE, FAKE, FAKE, 1, NUL) == p24.P24_ERR_UNSUPPORTED
+    assert f(NUL, 0, 256, 256, 256, 128, 128, FAKE, FAKE, FAKE, 1, NUL) == p24.P24_ERR_NULL
+    assert f(MISALIGNED, 0, 256, 256, 256, 128, 128, FAKE, FAKE, FAKE, 1, NUL) == p24.P24_ERR_ALIGN
+    assert f(FAKE, 0, 0, 256, 256, 128, 128, NUL, NUL, NUL, 1, NUL) == p24.P24_OK                # M == 0
+    # scores of 2048 tiles x 1024 columns (16 MiB) exceed the 8 MiB scratch; 1024 tiles fit exactly
+    assert f(FAKE, 0, 2048 * 128, 1024, 1024, 128, 512, FAKE, FAKE, FAKE, 1, NUL) == p24.P24_ERR_SCRATCH
+    assert L.tvw_workspace_bytes(1024 * 128, 1024, 128, 512) == L.tvw_noalloc_scratch_bytes()
+    assert "scratch" in p24.strerror(p24.P24_ERR_SCRATCH)
