@@ -25,7 +25,9 @@ import re
 from dataclasses import dataclass
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libprune24.so")
+# P24_LIBRARY may name another build of the same library (the host-sanitized copy
+# that build.py --sanitize writes, for CPU test runs)
+LIB_PATH = os.environ.get("P24_LIBRARY") or os.path.join(PKG_DIR, "libprune24.so")
 HEADER_PATH = os.path.join(os.path.dirname(PKG_DIR), "include", "prune24.h")
 
 # status codes / enums (mirror include/prune24.h)
