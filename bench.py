@@ -712,6 +712,26 @@ def main():
         rows["gemm_bf16_c5_us_mean"] = sum(ev5d) / len(ev5d) * 1e3
         rows["speedup_tvw_vs_dense_c5"] = rows["gemm_bf16_c5_us_mean"] / rows["spmm_tvw_c5_us_mean"]
         del Wp5, Yd5
+        # two-layer chain: a 4096 x 4096 2:4 layer with bias + GELU feeding the TVW layer;
+        # fused (the epilogue writes H in the layout the gather reads) against the unfused
+        # pair (plain product, then a separate bias + GELU pass in torch, then the TVW product)
+        c51 = p24.compress(torch.from_numpy(workloads.random_matrix((wt.K, wt.K), seed=5, sigma=0.02)).to(dev))
+        b51 = torch.randn(wt.K, device=dev, dtype=torch.float32) * 0.1
+        H5 = torch.empty((wt.K, wt.N), dtype=torch.bfloat16, device=dev)
+        chain = lambda: p24.spmm24_tvw_chain(c51, t5, X5, bias1=b51, act1="gelu", out=Y5, hidden=H5)
+
+        def unfused():
+            p24.spmm24(c51, X5, out=H5)
+            H5.copy_(torch.nn.functional.gelu(H5.float() + b51[:, None]).to(torch.bfloat16))
+            p24.spmm_tvw(t5, H5, out=Y5)
+        for f in (chain, unfused):
+            for _ in range(max(args.warmup // 2, 2)):
+                f()
+        evc = event_times_ms(torch, chain, max(args.steps // 2, 5))
+        evu = event_times_ms(torch, unfused, max(args.steps // 2, 5))
+        rows["chain_c5_us_mean"] = sum(evc) / len(evc) * 1e3
+        rows["chain_unfused_c5_us_mean"] = sum(evu) / len(evu) * 1e3
+        del c51, b51, H5
         # per-tile keep counts (same total of kept columns, tiles of different importance)
         wv = workloads.WORKLOADS["c5v"]
         W5v = torch.from_numpy(workloads.weights(wv)).to(dev)

@@ -309,6 +309,30 @@ P24_API p24_status spmm_tvw_fused(const int32_t* kept, const void* values, const
                                   void* stream);
 
 /*
+ * spmm24_tvw_chain -- two layers, the second TVW ("Accelerating Sparse DNNs Based on
+ *   Tiled GEMM", TL;DR: kernel fusion):
+ *     H  = bf16(act1(W1 X + bias1))          W1: M1 x K1, 2:4 (P24_LAYOUT_DEVICE)
+ *     Y2 = act2(W2 H + bias2)                W2: M2 x M1, TVW (kept2, tile_m2, keep_k2)
+ *   Layer 1's epilogue applies bias1 and act1, rounds to bf16 and writes H
+ *   row-major (M1 features x N tokens, leading dim ldh): the layout whose whole
+ *   rows layer 2 gathers by kept2, so no pass runs between the two products.
+ *   H is a caller-owned device buffer of M1 x N bf16 (ldh >= N, ldh % 8 == 0,
+ *   16 B aligned), distinct from X and Y2; on return it holds layer 1's output.
+ *   X (K1 x N bf16), bias1 / act1 as for spmm24_fused; kept2, values2, meta2,
+ *   tile_m2, keep_k2 as for spmm_tvw with K = M1; Y2, y2_dtype, ldy2, bias2 /
+ *   act2 as for spmm_tvw_fused (bias2 NULL and act2 P24_ACT_NONE: no epilogue).
+ *   Both products are validated before either is enqueued (any error of
+ *   spmm24_fused or spmm_tvw_fused; P24_ERR_SHAPE for M1 == 0;
+ *   P24_ERR_UNSUPPORTED if H is X or Y2).  M2 == 0 or N == 0: no-op.
+ */
+P24_API p24_status spmm24_tvw_chain(const void* values1, const void* meta1, int64_t M1, int64_t K1,
+                                    const float* bias1, int32_t act1, const int32_t* kept2,
+                                    const void* values2, const void* meta2, int64_t M2,
+                                    int64_t tile_m2, int64_t keep_k2, const void* X, int64_t ldx,
+                                    int64_t N, void* H, int64_t ldh, void* Y2, int32_t y2_dtype,
+                                    int64_t ldy2, const float* bias2, int32_t act2, void* stream);
+
+/*
  * TVW with a keep count per tile ("Accelerating Sparse DNNs Based on Tiled
  * GEMM", Abstract: regular structure inside a tile, irregular pruning across
  * the matrix; TL;DR: load balancing through batching).  Tiles are 128 rows:

@@ -701,3 +701,49 @@ def check(y: np.ndarray, y_ref: np.ndarray, bound: np.ndarray, out_dtype: str):
         ratio = np.where(tol > 0, err / tol, np.where(err > 0, np.inf, 0.0))
     worst = float(ratio.max()) if ratio.size else 0.0
     return bool(finite and worst <= 1.0), worst
+
+
+# ----------------------------------------------------------------------------
+# Two-layer chain ("Accelerating Sparse DNNs Based on Tiled GEMM", TL;DR:
+# kernel fusion).  Reading: layer 1 (2:4) computes h = act1(W1 X + b1) and
+# stores it as bf16 H, features x tokens; layer 2 (TVW) computes
+# y2 = act2(W2 H + b2).  The reference uses the exact h; the tolerance carries
+# layer 1's elementwise bound on |H - h| (its fused bound with the bf16
+# rounding of H) through |W2| into layer 2, whose own GEMM bound is taken on
+# |W2| (|h| + that bound).
+# ----------------------------------------------------------------------------
+def chain_ref(W1d: np.ndarray, X: np.ndarray, bias1, act1: int, W2d: np.ndarray, bias2, act2: int):
+    """(y2_ref, z2_ref, bound2, carried): y2 = act2(W2 h + b2) with h = act1(W1 X + b1)
+    exact in fp64; bound2 = |W2| (|h| + tol_h); carried = |W2| tol_h, where tol_h is
+    layer 1's bf16-output tolerance."""
+    h, z1, bnd1 = fused_ref(W1d, X, bias1, act1)
+    tol_h = fused_tolerance(h, z1, bnd1, act1, "bf16")
+    W2f = bf16_to_f64(W2d)
+    M2 = W2f.shape[0]
+    b2 = np.zeros(M2) if bias2 is None else np.asarray(bias2, dtype=np.float32).astype(np.float64)
+    z2 = W2f @ h + b2[:, None]
+    aW2 = np.abs(W2f)
+    return act_ref(z2, act2), z2, aW2 @ (np.abs(h) + tol_h), aW2 @ tol_h
+
+
+def chain_tolerance(y2_ref, z2_ref, bound2, carried, act2: int, out_dtype: str) -> np.ndarray:
+    """Bound on |y2 - y2_ref|: layer 2's fused bound on bound2 plus the carried
+    difference of H, both through act2's Lipschitz constant, then the output rounding."""
+    lip = {ACT_NONE: 1.0, ACT_RELU: 1.0, ACT_GELU: GELU_LIPSCHITZ}[act2]
+    tol = fused_tolerance(y2_ref, z2_ref, bound2, act2, "f32") + lip * carried
+    if out_dtype == "f32":
+        return tol
+    if out_dtype == "bf16":
+        return tol + BF16_HALF_ULP * (np.abs(y2_ref) + tol)
+    raise ValueError(out_dtype)
+
+
+def check_chain(y2, y2_ref, z2_ref, bound2, carried, act2: int, out_dtype: str):
+    """(ok, worst err/tol ratio) for the chain's output.  Non-finite outputs fail."""
+    y2 = np.asarray(y2, dtype=np.float64)
+    tol = chain_tolerance(y2_ref, z2_ref, bound2, carried, act2, out_dtype)
+    err = np.abs(y2 - y2_ref)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = np.where(tol > 0, err / tol, np.where(err > 0, np.inf, 0.0))
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return bool(np.isfinite(y2).all() and worst <= 1.0), worst

@@ -73,6 +73,9 @@ _SIGNATURES = {
                           _c_i64, _c_vp, _c_i32, _c_i64, _c_vp]),
     "spmm_tvw_fused": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_i32, _c_i64, _c_i64, _c_i64, _c_i64, _c_vp, _c_i64,
                                 _c_i64, _c_vp, _c_i32, _c_i64, _c_vp, _c_i32, _c_vp]),
+    "spmm24_tvw_chain": (_c_i32, [_c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i32, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64,
+                                  _c_i64, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_vp, _c_i32, _c_i64, _c_vp, _c_i32,
+                                  _c_vp]),
     "spmm_tvw_var_fused": (_c_i32, [_c_vp, _c_vp, _c_vp, _c_vp, _c_vp, _c_i64, _c_i64, _c_vp, _c_i64, _c_i64,
                                     _c_vp, _c_i32, _c_i64, _c_vp, _c_i32, _c_vp]),
     "tvw_var_workspace_bytes": (_c_size, [_c_i64, _c_i64]),
@@ -483,6 +486,41 @@ def spmm_tvw(t: CompressedTVW, X, out_dtype=None, out=None, bias=None, act="none
     _check(lib().spmm_tvw(_ptr(t.kept), _ptr(t.values), _ptr(t.meta), t.layout, t.M, t.K, t.tile_m, t.keep_k,
                           _ptr(X), ldx, N, _ptr(out), _out_code(out.dtype), ldy, _stream(X.device)), "spmm_tvw")
     return out
+
+
+def spmm24_tvw_chain(c1: Compressed24, t2: CompressedTVW, X, bias1=None, act1="gelu", bias2=None, act2="none",
+                     out_dtype=None, out=None, hidden=None):
+    """Two layers: H = bf16(act1(W1 X + bias1)) with W1 2:4-compressed, then
+    Y2 = act2(W2 H + bias2) with W2 TVW-compressed over K = W1's rows.  Layer 1's
+    epilogue writes H in the row-major layout layer 2's gather reads.  Returns (Y2, H);
+    `hidden` may supply H's buffer (bf16 [M1, N])."""
+    torch = _torch()
+    ldx = _x_bf16(X, "X")
+    if X.shape[0] != c1.K:
+        raise ValueError(f"X has {X.shape[0]} rows, W1 has K = {c1.K}")
+    if t2.K != c1.M:
+        raise ValueError(f"layer 2 takes K = {t2.K} inputs, layer 1 gives {c1.M}")
+    if c1.layout != P24_LAYOUT_DEVICE or t2.layout != P24_LAYOUT_DEVICE:
+        raise ValueError("both layers must be in the device layout")
+    N = X.shape[1]
+    _operands_on(X.device, (c1.values, "values1"), (c1.meta, "meta1"), (t2.kept, "kept2"), (t2.values, "values2"),
+                 (t2.meta, "meta2"))
+    if hidden is None:
+        hidden = torch.empty((c1.M, N), dtype=torch.bfloat16, device=X.device)
+    else:
+        _require_cuda(hidden, "hidden")
+        _same_device(hidden, X.device, "hidden")
+        if hidden.dtype != torch.bfloat16 or tuple(hidden.shape) != (c1.M, N):
+            raise ValueError(f"hidden must be bfloat16 of shape {(c1.M, N)}")
+    ldh = _rowmajor(hidden, "hidden")
+    out, ldy = _out_tensor(out, t2.M, N, out_dtype, X.device)
+    b1, a1, _ = _fused_args(bias1, act1, c1.M, X.device)
+    b2, a2, _ = _fused_args(bias2, act2, t2.M, X.device)
+    _check(lib().spmm24_tvw_chain(_ptr(c1.values), _ptr(c1.meta), c1.M, c1.K, b1, a1, _ptr(t2.kept), _ptr(t2.values),
+                                  _ptr(t2.meta), t2.M, t2.tile_m, t2.keep_k, _ptr(X), ldx, N, _ptr(hidden), ldh,
+                                  _ptr(out), _out_code(out.dtype), ldy, b2, a2, _stream(X.device)),
+           "spmm24_tvw_chain")
+    return out, hidden
 
 
 def tvw_var_compress(W, total_keep: int | None = None) -> CompressedTVWVar:

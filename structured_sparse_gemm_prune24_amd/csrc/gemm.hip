@@ -971,10 +971,11 @@ static p24_status check_epilogue(const float* bias, int32_t act) {
   return P24_OK;
 }
 
+// dry_run: validate only (nothing is launched); the status is the one the call would return.
 static p24_status tvw_fixed(const int32_t* kept, const void* values, const void* meta, int32_t layout, int64_t M,
                             int64_t K, int64_t tile_m, int64_t keep_k, const void* X, int64_t ldx, int64_t N,
                             void* Y, int32_t y_dtype, int64_t ldy, bool fused, const float* bias, int32_t act,
-                            void* stream) {
+                            void* stream, bool dry_run = false) {
   if (layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
   p24_status s = check_xy(X, ldx, N, Y, y_dtype, ldy);
   if (s != P24_OK) return s;
@@ -1003,6 +1004,7 @@ static p24_status tvw_fixed(const int32_t* kept, const void* values, const void*
   a.tile_m = (int)tile_m;
   a.bias = bias;
   a.act = act;
+  if (dry_run) return P24_OK;
   return launch_tvw<X_KN_GATHER>(a, y_dtype, fused, act, (hipStream_t)stream);
 }
 
@@ -1242,10 +1244,10 @@ extern "C" P24_API p24_status spmm24_xt(const void* values, const void* meta, in
 
 // Fused epilogue: Y = act(W X + b), b one fp32 per output row.  X as K x N
 // (P24_X_KN, rules of spmm24) or as N x K (P24_X_NK, rules of spmm24_xt).
-extern "C" P24_API p24_status spmm24_fused(const void* values, const void* meta, int32_t layout, int64_t M,
-                                           int64_t K, const void* X, int64_t ldx, int32_t x_order, int64_t N,
-                                           void* Y, int32_t y_dtype, int64_t ldy, const float* bias, int32_t act,
-                                           void* stream) {
+// dry_run: validate only (nothing is launched); the status is the one the call would return.
+static p24_status fused24(const void* values, const void* meta, int32_t layout, int64_t M, int64_t K, const void* X,
+                          int64_t ldx, int32_t x_order, int64_t N, void* Y, int32_t y_dtype, int64_t ldy,
+                          const float* bias, int32_t act, void* stream, bool dry_run) {
   if (layout != P24_LAYOUT_DEVICE) return P24_ERR_LAYOUT;
   if (x_order != P24_X_KN && x_order != P24_X_NK) return P24_ERR_UNSUPPORTED;
   if (act != P24_ACT_NONE && act != P24_ACT_RELU && act != P24_ACT_GELU) return P24_ERR_UNSUPPORTED;
@@ -1273,12 +1275,48 @@ extern "C" P24_API p24_status spmm24_fused(const void* values, const void* meta,
   a.tile_m = 1;
   a.bias = bias;
   a.act = act;
+  if (dry_run) return P24_OK;
   if (act == P24_ACT_GELU) {
     if (x_order == P24_X_NK) return dispatch<A_SPARSE, X_NK, 2>(a, y_dtype, (hipStream_t)stream);
     return dispatch<A_SPARSE, X_KN, 2>(a, y_dtype, (hipStream_t)stream);
   }
   if (x_order == P24_X_NK) return dispatch<A_SPARSE, X_NK, 1>(a, y_dtype, (hipStream_t)stream);
   return dispatch<A_SPARSE, X_KN, 1>(a, y_dtype, (hipStream_t)stream);
+}
+
+extern "C" P24_API p24_status spmm24_fused(const void* values, const void* meta, int32_t layout, int64_t M,
+                                           int64_t K, const void* X, int64_t ldx, int32_t x_order, int64_t N,
+                                           void* Y, int32_t y_dtype, int64_t ldy, const float* bias, int32_t act,
+                                           void* stream) {
+  return fused24(values, meta, layout, M, K, X, ldx, x_order, N, Y, y_dtype, ldy, bias, act, stream, false);
+}
+
+// Two-layer chain Y2 = act2(W2 act1(W1 X + b1) + b2), layer 1 plain 2:4, layer 2
+// TVW.  Layer 1's epilogue applies its bias and activation, rounds to bf16 and
+// writes H = act1(W1 X + b1) row-major (features x tokens): the layout whose
+// whole rows layer 2's TVW gather loads, so H is written once and read once per
+// gathering tile, with no pass in between (no separate bias, activation, cast
+// or re-layout).  Both calls are validated before either is enqueued.
+extern "C" P24_API p24_status spmm24_tvw_chain(const void* values1, const void* meta1, int64_t M1, int64_t K1,
+                                               const float* bias1, int32_t act1, const int32_t* kept2,
+                                               const void* values2, const void* meta2, int64_t M2, int64_t tile_m2,
+                                               int64_t keep_k2, const void* X, int64_t ldx, int64_t N, void* H,
+                                               int64_t ldh, void* Y2, int32_t y2_dtype, int64_t ldy2,
+                                               const float* bias2, int32_t act2, void* stream) {
+  p24_status s = fused24(values1, meta1, P24_LAYOUT_DEVICE, M1, K1, X, ldx, P24_X_KN, N, H, P24_BF16, ldh, bias1,
+                         act1, stream, true);
+  if (s != P24_OK) return s;
+  const bool fused2 = bias2 != nullptr || act2 != P24_ACT_NONE;
+  s = tvw_fixed(kept2, values2, meta2, P24_LAYOUT_DEVICE, M2, M1, tile_m2, keep_k2, H, ldh, N, Y2, y2_dtype, ldy2,
+                fused2, bias2, act2, stream, true);
+  if (s != P24_OK) return s;
+  if (M1 == 0 || M2 == 0 || N == 0) return P24_OK;
+  if (H == X || H == Y2) return P24_ERR_UNSUPPORTED;     // the intermediate must be its own buffer
+  s = fused24(values1, meta1, P24_LAYOUT_DEVICE, M1, K1, X, ldx, P24_X_KN, N, H, P24_BF16, ldh, bias1, act1, stream,
+              false);
+  if (s != P24_OK) return s;
+  return tvw_fixed(kept2, values2, meta2, P24_LAYOUT_DEVICE, M2, M1, tile_m2, keep_k2, H, ldh, N, Y2, y2_dtype, ldy2,
+                   fused2, bias2, act2, stream, false);
 }
 
 extern "C" P24_API p24_status gemm_bf16_xt(const void* Wp, int64_t M, int64_t K, const void* XT, int64_t ldxt,
