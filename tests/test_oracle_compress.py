@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 
 from oracle import prune24 as O
+from mfma_models import smfmac32_model
 from workloads import random_matrix, small_int_matrix
 
 LEGAL_NIBBLES = {0x4, 0x8, 0xC, 0x9, 0xD, 0xE}
@@ -75,32 +76,7 @@ def test_device_layout_bijection(M, K):
         assert (full_m[M:] == 0x44444444).all()
 
 
-# ---- lane-level model of v_smfmac_f32_32x32x32_bf16 (measured lane map) ----
-def _smfmac32_model(a_lanes, b_lanes, idx_lanes, abid, acc):
-    """a_lanes [64,8] f64, b_lanes [64,16] f64, idx_lanes [64] u32, acc [64,16] f64 (D lane layout)."""
-    A = np.zeros((32, 32))
-    for L in range(64):
-        r, h = L % 32, L // 32
-        bits = (int(idx_lanes[L]) >> (16 * abid)) & 0xFFFF
-        for i in range(8):
-            q, j = i // 2, i % 2
-            p = (bits >> (4 * q + 2 * j)) & 3
-            A[r, 16 * h + 4 * q + p] += a_lanes[L, i]
-    B = np.zeros((32, 32))
-    for lb in range(64):
-        n, h = lb % 32, lb // 32
-        for e in range(16):
-            k = 8 * h + e if e < 8 else 16 + 8 * h + (e - 8)
-            B[k, n] = b_lanes[lb, e]
-    D = A @ B
-    out = acc.copy()
-    for lo in range(64):
-        n = lo % 32
-        for i in range(16):
-            out[lo, i] += D[8 * (i // 4) + 4 * (lo // 32) + i % 4, n]
-    return out
-
-
+# ---- lane-level model of v_smfmac_f32_32x32x32_bf16: tests/mfma_models.py ----
 def test_device_layout_through_instruction_model():
     M, K, N = 64, 128, 32
     W = small_int_matrix((M, K), seed=21)
@@ -122,7 +98,7 @@ def test_device_layout_through_instruction_model():
                 for e in range(16):
                     k = 8 * h + e if e < 8 else 16 + 8 * h + (e - 8)
                     b[lb, e] = Xf[32 * s + k, n]
-            acc = _smfmac32_model(dv[rb, s], b, dm[rb, s // 2], s % 2, acc)
+            acc = smfmac32_model(dv[rb, s], b, dm[rb, s // 2], s % 2, acc)
         for lo in range(64):
             for i in range(16):
                 Y[32 * rb + 8 * (i // 4) + 4 * (lo // 32) + i % 4, lo % 32] = acc[lo, i]

@@ -10,6 +10,7 @@ import numpy as np
 import pytest
 
 import workloads
+from mfma_models import mfma32x32x16_model
 from oracle import prune24 as O
 
 
@@ -48,22 +49,6 @@ def test_tw_var_matches_tvw_columns_and_scatter():
     assert kept.size == dv.size // 128 == counts.sum()
 
 
-def _mfma32x32x16_model(a, b, acc):
-    """Dense MFMA 32x32x16 bf16 lane semantics: A lane L = row L % 32, k 8 (L // 32) .. +8;
-    B lane L = column L % 32, same k; D lane lo, element i = row 8 (i // 4) + 4 (lo // 32) + i % 4, column lo % 32."""
-    A = np.zeros((32, 16))
-    B = np.zeros((16, 32))
-    for L in range(64):
-        A[L % 32, 8 * (L // 32): 8 * (L // 32) + 8] = a[L]
-        B[8 * (L // 32): 8 * (L // 32) + 8, L % 32] = b[L]
-    D = A @ B
-    out = acc.copy()
-    for lo in range(64):
-        for i in range(16):
-            out[lo, i] += D[8 * (i // 4) + 4 * (lo // 32) + i % 4, lo % 32]
-    return out
-
-
 def test_dense_layout_through_instruction_model():
     M, K, N = 40, 64, 32
     Wb = workloads.truncate_to_bf16_bits(workloads.small_int_matrix((M, K), seed=14))
@@ -75,7 +60,7 @@ def test_dense_layout_through_instruction_model():
         acc = np.zeros((64, 16))
         for s in range(K // 16):
             b = np.array([Xf[16 * s + 8 * (L // 32): 16 * s + 8 * (L // 32) + 8, L % 32] for L in range(64)])
-            acc = _mfma32x32x16_model(dv[rb, s], b, acc)
+            acc = mfma32x32x16_model(dv[rb, s], b, acc)
         for lo in range(64):
             for i in range(16):
                 Y[32 * rb + 8 * (i // 4) + 4 * (lo // 32) + i % 4, lo % 32] = acc[lo, i]
