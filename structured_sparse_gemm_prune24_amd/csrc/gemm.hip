@@ -159,11 +159,6 @@ __device__ __forceinline__ void wait_lds(T (&r)[N]) {
   for (int i = 0; i < N; ++i) asm volatile("" : "+v"(r[i]));
 }
 
-template <typename OutT> __device__ __forceinline__ void store_out(OutT* p, float v);
-template <> __device__ __forceinline__ void store_out<float>(float* p, float v) { *p = v; }
-template <> __device__ __forceinline__ void store_out<uint16_t>(uint16_t* p, float v) {
-  *p = f32_to_bf16_rne(__float_as_uint(v));
-}
 
 struct GemmArgs {
   const uint16_t* A;       // sparse: device-layout values; dense: packed W
@@ -720,16 +715,31 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   for (int i = 0; i < TM; ++i) {
     asm volatile("" ::: "memory");
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < TN; ++j) {
+      if constexpr (!FUSED && ES == 2) {
+        // bf16 output: elements e and e + 1 are rows r and r + 1 of the lane's
+        // column; one packed conversion (v_cvt_pk_bf16_f32, round to nearest
+        // even) makes both, then each half goes to its row.
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int r = 8 * (e >> 2) + 4 * h + (e & 3);
-        StageT v;
-        if constexpr (FUSED) v = acc[i][j][e] + bz[i][e];
-        else if constexpr (ES == 2) v = f32_to_bf16_rne(__float_as_uint(acc[i][j][e]));
-        else v = acc[i][j][e];
-        *reinterpret_cast<StageT*>(region + r * PITCH + (32 * j + (lane & 31)) * SES) = v;
+        for (int e = 0; e < 16; e += 2) {
+          const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+          const uint32_t w = __builtin_bit_cast(
+              uint32_t, __builtin_convertvector((f32x2){acc[i][j][e], acc[i][j][e + 1]}, bf16x2));
+          uint8_t* p = region + r * PITCH + (32 * j + (lane & 31)) * 2;
+          *reinterpret_cast<uint16_t*>(p) = (uint16_t)w;
+          *reinterpret_cast<uint16_t*>(p + PITCH) = (uint16_t)(w >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int r = 8 * (e >> 2) + 4 * h + (e & 3);
+          StageT v;
+          if constexpr (FUSED) v = acc[i][j][e] + bz[i][e];
+          else v = acc[i][j][e];
+          *reinterpret_cast<StageT*>(region + r * PITCH + (32 * j + (lane & 31)) * SES) = v;
+        }
       }
+    }
     asm volatile("" ::: "memory");
     if constexpr (FUSED) {
       // VO outputs per 16 B store, read as VO staged fp32 values (32 B for a
@@ -754,12 +764,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         }
         if (row >= M) continue;
         OutT o[VO];
+        float f[VO];
 #pragma unroll
         for (int u = 0; u < VO; ++u) {
           const float z = zf[u];
-          const float f = EPI == 2 ? apply_act(z, P24_ACT_GELU) : (args.act == P24_ACT_RELU ? (z > 0.0f ? z : 0.0f) : z);
-          if constexpr (ES == 2) o[u] = f32_to_bf16_rne(__float_as_uint(f));
-          else o[u] = f;
+          f[u] = EPI == 2 ? apply_act(z, P24_ACT_GELU) : (args.act == P24_ACT_RELU ? (z > 0.0f ? z : 0.0f) : z);
+        }
+#pragma unroll
+        for (int u = 0; u < VO; u += 2) {
+          if constexpr (ES == 2) {
+            // packed conversion, round to nearest even (v_cvt_pk_bf16_f32)
+            const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){f[u], f[u + 1]}, bf16x2));
+            o[u] = (uint16_t)w;
+            o[u + 1] = (uint16_t)(w >> 16);
+          } else {
+            o[u] = f[u];
+            o[u + 1] = f[u + 1];
+          }
         }
         OutT* dst = Y + (int64_t)row * args.ldy + col;
         if (vec_ok && col + VO <= N) {
