@@ -58,7 +58,7 @@ enum XMode { X_KN = 0, X_KN_GATHER = 1, X_NK = 2, X_KN_GATHER_VAR = 3 };
 // pruned slots) that the dense MFMA loop then reads.
 enum AMode { A_DENSE = 0, A_SPARSE = 1, A_DECOMP = 2 };
 
-template <int BM, int BN, int WGM, int WGN, int AM>
+template <int BM, int BN, int WGM, int WGN, int AM, bool GATHER_X = false>
 struct TileCfg {
   static constexpr bool SPARSE = AM != A_DENSE;    // compressed operand staged in LDS
   static constexpr int NWAVES = WGM * WGN;
@@ -82,18 +82,32 @@ struct TileCfg {
   // A_DECOMP: one dense A tile (BM x BK bf16 in dense fragment order) after the stages
   static constexpr int D_BYTES = AM == A_DECOMP ? RB * 4 * 1024 : 0;
   static constexpr int NSTAGE = 3 * STAGE + D_BYTES <= LDS_LIMIT ? 3 : 2;
-  // direct-to-LDS loads per wave per K step (each moves 1 KiB, or 256 B for metadata)
-  static constexpr int X_DMA = X_BYTES / 1024 / NWAVES;
-  static constexpr int A_DMA = A_BYTES / 1024 / NWAVES;
+  // Waves that issue the stage loads.  With 8 waves, two per SIMD, only the
+  // first four load (one per SIMD, waves taking SIMDs in turn): after each
+  // stage barrier the other wave of the SIMD goes straight to its multiplies
+  // while its partner issues the loads.  Measured (graph replay, A/B against
+  // all eight waves loading): 8192^3 sparse 523 -> 505 us, X given N x K
+  // 518 -> 492 us, dense 835 -> 792 us; BERT FFN 18.6 -> 18.1 us.  The
+  // gathered products keep all eight: their loaders also fetch the kept row
+  // indices, and the 4096^3 TVW product measured 60 -> 63 us with four.  It
+  // needs the four loaders' counts to fit the 6-bit load counter with
+  // NSTAGE - 1 steps in flight.
+  static constexpr int LW_HALF = NWAVES / 2;
+  static constexpr bool HALF_LOAD =
+      !GATHER_X && NWAVES == 8 && (X_BYTES / 1024 / LW_HALF + A_BYTES / 1024 / LW_HALF + 1) * 3 < 64;
+  static constexpr int LW = HALF_LOAD ? LW_HALF : NWAVES;
+  // direct-to-LDS loads per loading wave per K step (each moves 1 KiB, or 256 B for metadata)
+  static constexpr int X_DMA = X_BYTES / 1024 / LW;
+  static constexpr int A_DMA = A_BYTES / 1024 / LW;
   // waves 0 .. MG-1 issue one metadata load per step on top of their share
   // of X and A, so the per-wave load counts differ by one
   static constexpr int DMA_O = X_DMA + A_DMA;
   static constexpr int DMA_M = DMA_O + 1;
   static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "wave tiles must be multiples of 32");
-  static_assert(X_BYTES % (1024 * NWAVES) == 0 && A_BYTES % (1024 * NWAVES) == 0, "even load split");
+  static_assert(X_BYTES % (1024 * LW) == 0 && A_BYTES % (1024 * LW) == 0, "even load split");
   static_assert(AM != A_DECOMP || RB % NWAVES == 0, "the expansion splits row blocks evenly among waves");
   static_assert(RB >= 4 ? RB % 4 == 0 : RB == 2, "row blocks come in whole metadata groups or one half");
-  static_assert(MG <= NWAVES, "one metadata load per wave at most");
+  static_assert(MG <= LW, "one metadata load per loading wave at most");
   static_assert(CPR >= 16, "the chunk swizzle needs at least 16 chunks per row");
   static_assert(2 * STAGE + D_BYTES <= LDS_LIMIT, "two stages must fit in LDS");
   static_assert(3 * DMA_M < 64, "vmcnt range");
@@ -216,7 +230,7 @@ __device__ __forceinline__ void dma4_to_lds(__amdgpu_buffer_rsrc_t r, void* lds_
 
 template <int BM, int BN, int WGM, int WGN, int AM, int XM, typename OutT, int EPI>
 __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
-  using C = TileCfg<BM, BN, WGM, WGN, AM>;
+  using C = TileCfg<BM, BN, WGM, WGN, AM, XM == X_KN_GATHER || XM == X_KN_GATHER_VAR>;
   constexpr bool SPARSE = C::SPARSE, SMFMAC = AM == A_SPARSE, DECOMP = AM == A_DECOMP;
   constexpr bool VAR = XM == X_KN_GATHER_VAR;
   constexpr bool GATHER = XM == X_KN_GATHER || VAR;
@@ -289,10 +303,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   constexpr int X_LOADS_PER_ROW = C::CPR / 64 > 0 ? C::CPR / 64 : 1;     // loads per row when CPR > 64
   static_assert(X_LOADS_PER_ROW == 1, "BN <= 512");
   const int p0 = wave * 64 + lane;                   // chunk of load j = 0
-  const int x_r0 = p0 / C::CPR;                      // its tile row; load j adds j * NWAVES * X_ROWS_PER_LOAD rows
+  const int x_r0 = p0 / C::CPR;                      // its tile row; load j adds j * LW * X_ROWS_PER_LOAD rows
   int x_col = n0 + 8 * ((p0 % C::CPR) ^ chunk_swizzle(x_r0));
   x_col = x_col <= n_hi ? x_col : n_hi;
-  constexpr int X_ROW_STEP = C::NWAVES * X_ROWS_PER_LOAD;   // multiple of 4: the swizzle of row x_r0 holds for all j
+  constexpr int X_ROW_STEP = C::LW * X_ROWS_PER_LOAD;   // multiple of 4: the swizzle of row x_r0 holds for all j
   static_assert(X_ROW_STEP % 4 == 0, "X row step must keep the swizzle phase");
   uint32_t x_voff = GATHER ? (uint32_t)x_col * 2 : (uint32_t)(x_r0 * ldx + x_col) * 2;
   // X^T (N x K): the stage holds BN rows (n) of 64 k = 8 chunks of 16 B.  LDS
@@ -307,8 +321,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     const int n_loc = 8 * q + ((lane >> 3) ^ (q & 1));      // row' = 8q + lane/8, n = row' ^ (q & 1)
     const int c = (lane & 7) ^ (n_loc & 7);
     x_voff = (uint32_t)(n_loc * ldx + 8 * c) * 2;
-    xt_jstride = (uint32_t)(8 * C::NWAVES * ldx * 2);       // q advances by NWAVES (even: parity kept)
-    static_assert(C::NWAVES % 2 == 0, "X^T loads keep the row-pair parity per wave");
+    xt_jstride = (uint32_t)(8 * C::LW * ldx * 2);           // q advances by LW (even: parity kept)
+    static_assert(C::LW % 2 == 0, "X^T loads keep the row-pair parity per wave");
   }
   // A values: load j fills the (row block, step) block q = j*NWAVES + wave of
   // the stage.  Metadata: wave w < MG loads group w (four row blocks, 1 KiB per
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // past the resource end and come back as zeros.
   const uint32_t a_voff = (uint32_t)lane * 16;
   auto a_block_off = [&](int j) -> uint32_t {
-    const int q = j * C::NWAVES + wave;
+    const int q = j * C::LW + wave;
     return (uint32_t)(((q / ASTEPS) * S + q % ASTEPS) * 1024);
   };
   const bool meta_wave = wave < C::MG;
@@ -342,37 +356,43 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // TVW: the gathered X rows of step g are read one step before their loads
   // are issued (and are issued before them), so waiting for the indices never
   // waits for a tile in flight.
+  // Only the loading waves read kept entries: their rows x_r0 + j * X_ROW_STEP
+  // cover exactly the step's BK entries, while the rows the other waves would
+  // compute run past the step (and, on a tile's last step, past its list).
+  static_assert(!GATHER || C::X_DMA * X_ROW_STEP == BK, "a loading wave's kept rows stay inside the step");
   int k_cur[GATHER ? C::X_DMA : 1], k_nxt[GATHER ? C::X_DMA : 1];
   auto load_kept = [&](int g, int (&kk)[GATHER ? C::X_DMA : 1]) {
+    if (C::LW < C::NWAVES && wave >= C::LW) return;
     if constexpr (GATHER) {
 #pragma unroll
       for (int j = 0; j < C::X_DMA; ++j) kk[j] = kept_tile[(int64_t)g * BK + x_r0 + j * X_ROW_STEP];
     }
   };
 
-  // all direct-to-LDS loads of K step g into stage st
+  // all direct-to-LDS loads of K step g into stage st (loading waves only)
   auto issue_step = [&](int g, int st) {
+    if (C::LW < C::NWAVES && wave >= C::LW) return;
     uint8_t* stage = lds + st * C::STAGE;
     if constexpr (GATHER) {
 #pragma unroll
       for (int j = 0; j < C::X_DMA; ++j) {
         int k = k_cur[j];
         k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
-        dma16_to_lds(xg_rsrc, stage + (j * C::NWAVES + wave) * 1024, (uint32_t)(k * ldx * 2) + x_voff, 0);
+        dma16_to_lds(xg_rsrc, stage + (j * C::LW + wave) * 1024, (uint32_t)(k * ldx * 2) + x_voff, 0);
       }
     } else if constexpr (XT) {
 #pragma unroll
       for (int j = 0; j < C::X_DMA; ++j)
-        dma16_to_lds(xt_rsrc, stage + (j * C::NWAVES + wave) * 1024, x_voff, (uint32_t)g * BK * 2 + j * xt_jstride);
+        dma16_to_lds(xt_rsrc, stage + (j * C::LW + wave) * 1024, x_voff, (uint32_t)g * BK * 2 + j * xt_jstride);
     } else {
       const __amdgpu_buffer_rsrc_t xr = make_rsrc(args.X + (int64_t)g * BK * ldx, (uint32_t)(BK * ldx * 2));
 #pragma unroll
       for (int j = 0; j < C::X_DMA; ++j)
-        dma16_to_lds(xr, stage + (j * C::NWAVES + wave) * 1024, x_voff, (uint32_t)(j * X_ROW_STEP * ldx * 2));
+        dma16_to_lds(xr, stage + (j * C::LW + wave) * 1024, x_voff, (uint32_t)(j * X_ROW_STEP * ldx * 2));
     }
 #pragma unroll
     for (int j = 0; j < C::A_DMA; ++j)
-      dma16_to_lds(a_rsrc, stage + C::X_BYTES + (j * C::NWAVES + wave) * 1024, a_voff,
+      dma16_to_lds(a_rsrc, stage + C::X_BYTES + (j * C::LW + wave) * 1024, a_voff,
                    (uint32_t)g * ASTEPS * 1024 + a_block_off(j));
     if constexpr (SPARSE) {
       if (meta_wave)
