@@ -483,7 +483,7 @@ def main():
         sys.exit(2)
     # the clock sampler starts before this process touches the GPU
     clk_proc, clk_path = (None, None)
-    if args.only is None and not args.no_clock:
+    if args.only in (None, "spmm") and not args.no_clock:
         clk_proc, clk_path = start_clock_sampler()
     import numpy as np
     import torch
@@ -609,6 +609,7 @@ def main():
                      "refresh_ms_est": refresh_ms_est(clock_pre_t),
                      "source": f"{src}: mean of the XCD graphics clocks per reading, median over readings"}
     if args.only == "spmm":
+        rows["clock"] = clock
         print(json.dumps(rows))
         return
 

@@ -369,36 +369,44 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     }
   };
 
-  // all direct-to-LDS loads of K step g into stage st (loading waves only)
-  auto issue_step = [&](int g, int st) {
-    if (C::LW < C::NWAVES && wave >= C::LW) return;
+  // Load q of a loading wave's list for K step g into stage st: X loads
+  // first (q < X_DMA), then A (q < X_DMA + A_DMA), then the metadata load of
+  // the waves that take one.  The caller keeps the non-loading waves out.
+  constexpr int NQ = C::X_DMA + C::A_DMA + (SPARSE ? 1 : 0);
+  const bool loader = !(C::LW < C::NWAVES && wave >= C::LW);
+  auto issue_one = [&](auto QC, int g, int st) {
+    constexpr int q = decltype(QC)::value;
     uint8_t* stage = lds + st * C::STAGE;
-    if constexpr (GATHER) {
-#pragma unroll
-      for (int j = 0; j < C::X_DMA; ++j) {
+    if constexpr (q < C::X_DMA) {
+      constexpr int j = q;
+      if constexpr (GATHER) {
         int k = k_cur[j];
         k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
         dma16_to_lds(xg_rsrc, stage + (j * C::LW + wave) * 1024, (uint32_t)(k * ldx * 2) + x_voff, 0);
-      }
-    } else if constexpr (XT) {
-#pragma unroll
-      for (int j = 0; j < C::X_DMA; ++j)
+      } else if constexpr (XT) {
         dma16_to_lds(xt_rsrc, stage + (j * C::LW + wave) * 1024, x_voff, (uint32_t)g * BK * 2 + j * xt_jstride);
-    } else {
-      const __amdgpu_buffer_rsrc_t xr = make_rsrc(args.X + (int64_t)g * BK * ldx, (uint32_t)(BK * ldx * 2));
-#pragma unroll
-      for (int j = 0; j < C::X_DMA; ++j)
+      } else {
+        const __amdgpu_buffer_rsrc_t xr = make_rsrc(args.X + (int64_t)g * BK * ldx, (uint32_t)(BK * ldx * 2));
         dma16_to_lds(xr, stage + (j * C::LW + wave) * 1024, x_voff, (uint32_t)(j * X_ROW_STEP * ldx * 2));
-    }
-#pragma unroll
-    for (int j = 0; j < C::A_DMA; ++j)
+      }
+    } else if constexpr (q < C::X_DMA + C::A_DMA) {
+      constexpr int j = q - C::X_DMA;
       dma16_to_lds(a_rsrc, stage + C::X_BYTES + (j * C::LW + wave) * 1024, a_voff,
                    (uint32_t)g * ASTEPS * 1024 + a_block_off(j));
-    if constexpr (SPARSE) {
+    } else if constexpr (SPARSE) {
       if (meta_wave)
         dma16_to_lds(m_rsrc, stage + C::X_BYTES + C::A_BYTES + wave * 1024, a_voff,
                      (uint32_t)g * 1024 + (uint32_t)wave * T_ * 1024);
     }
+  };
+  // loads [Q0, Q1) of K step g into stage st
+  auto issue_range = [&](auto Q0, auto Q1, int g, int st) {
+    if (!loader) return;
+    static_for<decltype(Q0)::value, decltype(Q1)::value>([&](auto Q) { issue_one(Q, g, st); });
+  };
+  // all direct-to-LDS loads of K step g into stage st (loading waves only)
+  auto issue_step = [&](int g, int st) {
+    issue_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NQ>{}, g, st);
   };
 
   // ---- LDS read addresses, one set per stage ----
@@ -524,6 +532,30 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
                                                               __builtin_bit_cast(bf16x16, bf[j]), acc[i][j],
                                                               (int)meta[i], 0, decltype(SS)::value);
   };
+  // The same multiplies with loads Q0 .. Q1-1 of step g (into stage st)
+  // issued one after each MFMA, the rest after the last: spread out this way
+  // a loading wave's vector-memory issue waits sit in the shadow of its
+  // MFMAs instead of holding them back in one burst.
+  // LD (compile time) says whether this wave loads: a branch on it here,
+  // between fragment reads and their wait, would let the compiler copy the
+  // read registers at the join before they have arrived.
+  auto mma_sparse_loads = [&](auto LD, auto SS, const i16x8 (&a)[TM], const i16x16 (&bf)[TN],
+                              const uint32_t (&meta)[TM], auto Q0, auto Q1, int g, int st) {
+    constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
+    if constexpr (!decltype(LD)::value) {
+      mma_sparse(SS, a, bf, meta);
+      return;
+    }
+    static_for<0, TM * TN>([&](auto KC) {
+      constexpr int k = decltype(KC)::value, i = k / TN, j = k % TN;
+      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                            __builtin_bit_cast(bf16x16, bf[j]), acc[i][j],
+                                                            (int)meta[i], 0, decltype(SS)::value);
+      if constexpr (q0 + k < q1) issue_one(std::integral_constant<int, q0 + k>{}, g, st);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    static_for<q0 + TM * TN < q1 ? q0 + TM * TN : q1, q1>([&](auto Q) { issue_one(Q, g, st); });
+  };
 
   // One K step on stage ST (dense MFMA on packed W or on the expanded tile).
   auto compute = [&](auto ST) {
@@ -584,13 +616,36 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     // The loop is unrolled by NSTAGE so every stage address is a constant.
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
+    // With three stages the loads of step it+NSTAGE are split: the first P0
+    // go out with the multiplies after the barrier of step it, the rest with
+    // the first-half multiplies of step it+1, ahead of its barrier (so the
+    // count waited for there is unchanged).  The prologue issues that first
+    // part only for its last step.  With two stages every load of a step goes
+    // out after the barrier, as the stage is needed one half-step later.  The
+    // gathered products keep all loads after the barrier too: their X loads
+    // take the kept indices that are replaced at the end of the step.
+    constexpr bool SPLIT = !GATHER && NSTAGE >= 3;
+    constexpr int P0 = SPLIT ? (C::X_DMA + C::A_DMA) / 4 : NQ;
+    // Scheduling fences that keep each half's fragment reads ahead of the
+    // multiplies that overlap them (and those multiplies on their side of the
+    // stage barrier).  Without them the scheduler sinks the reads below most
+    // of the multiplies to save registers, so their latency shows at the
+    // wait.  They need all four fragment sets live at once, which fits the
+    // 256 registers without spilling only in the plain bf16-output variant of
+    // the widest tile; measured there 1-1.5 % faster.
+    constexpr bool PIN = !(BM == 256 && BN == 256) || (XM == X_KN && EPI == 0 && sizeof(OutT) == 2);
+    using QP0 = std::integral_constant<int, P0>;
+    using QNQ = std::integral_constant<int, NQ>;
 #pragma unroll
     for (int g = 0; g < NSTAGE; ++g) {
       load_kept(min(g, nk - 1), k_cur);
-      issue_step(min(g, nk - 1), g);
+      if (SPLIT && g == NSTAGE - 1) issue_range(I0{}, QP0{}, min(g, nk - 1), g);
+      else issue_step(min(g, nk - 1), g);
     }
     load_kept(min(NSTAGE, nk - 1), k_cur);
-    wait_vmcnt_by_wave<(NSTAGE - 1) * C::DMA_M, (NSTAGE - 1) * C::DMA_O>(meta_wave);
+    constexpr int PRO_M = SPLIT ? (NSTAGE - 2) * C::DMA_M + P0 : (NSTAGE - 1) * C::DMA_M;
+    constexpr int PRO_O = SPLIT ? (NSTAGE - 2) * C::DMA_O + P0 : (NSTAGE - 1) * C::DMA_O;
+    wait_vmcnt_by_wave<PRO_M, PRO_O>(meta_wave);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // The fragment reads are asynchronous (results land at the lgkmcnt wait)
@@ -607,24 +662,37 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     wait_lds(meta[0]);
     wait_lds(a0);
     wait_lds(b0);
-    auto body = [&](auto ST, int it) {
+    auto body = [&](auto ST, auto LD, int it) {
       constexpr int st = decltype(ST)::value;
       constexpr int nx = (st + 1) % NSTAGE;
       rd_a(ST, I1{}, a1);
       rd_b(ST, I1{}, b1);
-      mma_sparse(I0{}, a0, b0, meta[st]);
+      if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SPLIT)
+        mma_sparse_loads(LD, I0{}, a0, b0, meta[st], QP0{}, QNQ{}, min(it + NSTAGE - 1, nk - 1),
+                         (st + NSTAGE - 1) % NSTAGE);
+      else
+        mma_sparse(I0{}, a0, b0, meta[st]);
+      if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       wait_lds(a1);
       wait_lds(b1);
       wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(meta_wave);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
+      if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       load_kept(min(it + NSTAGE + 1, nk - 1), k_nxt);
-      issue_step(min(it + NSTAGE, nk - 1), st);
-      asm volatile("" ::: "memory");
+      if constexpr (!SPLIT) {
+        if constexpr (decltype(LD)::value) issue_step(min(it + NSTAGE, nk - 1), st);
+        asm volatile("" ::: "memory");
+      }
       rd_meta(std::integral_constant<int, nx>{}, meta[nx]);
       rd_a(std::integral_constant<int, nx>{}, I0{}, a0);
       rd_b(std::integral_constant<int, nx>{}, I0{}, b0);
-      mma_sparse(I1{}, a1, b1, meta[st]);
+      if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
+      if constexpr (SPLIT)
+        mma_sparse_loads(LD, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st);
+      else
+        mma_sparse(I1{}, a1, b1, meta[st]);
       __builtin_amdgcn_sched_barrier(0);
       wait_lds(meta[nx]);
       wait_lds(a0);
@@ -634,11 +702,17 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
       }
     };
-    for (int it = 0; it < nk; it += NSTAGE) {
-      static_for<0, NSTAGE>([&](auto ST) {
-        if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
-      });
-    }
+    // loading and non-loading waves run separate copies of the loop (the
+    // branch is taken here, with no fragment read in flight)
+    auto main_loop = [&](auto LD) {
+      for (int it = 0; it < nk; it += NSTAGE) {
+        static_for<0, NSTAGE>([&](auto ST) {
+          if (it + decltype(ST)::value < nk) body(ST, LD, it + decltype(ST)::value);
+        });
+      }
+    };
+    if (loader) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
   } else {
     // Step g is loaded into stage g % NSTAGE by the loads issued NSTAGE-1 steps
     // earlier.  At the top of step it the loads of steps it+1 .. it+NSTAGE-2 may

@@ -77,9 +77,20 @@ def pending_lds_uses(asm: str) -> Dict[str, List[str]]:
     return out
 
 
+def spilling_kernels(asm: str) -> List[str]:
+    """Kernels that touch scratch memory (register spills).  The loop's hand-counted
+    vmcnt waits stay correct with extra memory operations in flight (they only get
+    stricter), but a spill inside the loop costs a memory round trip per step."""
+    return [name for name, body in _KERNEL.findall(asm) if re.search(r"^\s*scratch_", body, re.M)]
+
+
 def check_file(path: str) -> None:
     with open(path) as f:
-        found = pending_lds_uses(f.read())
+        asm = f.read()
+    found = pending_lds_uses(asm)
     if found:
         lines = [f"{k}: {len(v)} (first: {v[0]})" for k, v in found.items()]
         raise RuntimeError(f"{path}: instructions use LDS read results before their wait:\n" + "\n".join(lines))
+    spills = spilling_kernels(asm)
+    if spills:
+        raise RuntimeError(f"{path}: GEMM kernels spill registers to scratch:\n" + "\n".join(spills))

@@ -1,5 +1,6 @@
 """The build-time ISA check: it must flag a register read before the LDS wait that
-covers it, accept the waited form, and find nothing in the built kernels."""
+covers it, accept the waited form, flag register spills, and find nothing in the
+built kernels."""
 import os
 
 import pytest
@@ -49,9 +50,16 @@ def test_partial_wait_completes_older_reads():
     assert I.pending_lds_uses(asm) == {}
 
 
+def test_flags_spills():
+    assert I.spilling_kernels(_k("\tscratch_store_dword off, v0, off offset:384\n")) == [HEAD.split()[0][:-1]]
+    assert I.spilling_kernels(_k("\tv_mov_b32_e32 v1, v2\n\tglobal_store_dword v[2:3], v1, off\n")) == []
+
+
 def test_built_kernels_are_clean():
     path = B.device_asm(os.path.join(B.CSRC, "gemm.hip"))
     if not os.path.exists(path):
         pytest.skip("library not built with assembly kept (run __graft_entry__.build())")
     with open(path) as f:
-        assert I.pending_lds_uses(f.read()) == {}
+        asm = f.read()
+    assert I.pending_lds_uses(asm) == {}
+    assert I.spilling_kernels(asm) == []
