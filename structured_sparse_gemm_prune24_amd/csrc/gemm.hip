@@ -623,8 +623,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     // part only for its last step.  With two stages every load of a step goes
     // out after the barrier, as the stage is needed one half-step later.  The
     // gathered products keep all loads after the barrier too: their X loads
-    // take the kept indices that are replaced at the end of the step.
-    constexpr bool SPLIT = !GATHER && NSTAGE >= 3;
+    // take the kept indices that are replaced at the end of the step.  So do
+    // the 4-wave tiles, where every wave loads a batch of five or six: there
+    // is no burst to spread, and the ResNet-50 3x3 shape (64 x 128 tiles)
+    // measured 3 % slower split.
+    constexpr bool SPLIT = !GATHER && NSTAGE >= 3 && C::HALF_LOAD;
     constexpr int P0 = SPLIT ? (C::X_DMA + C::A_DMA) / 4 : NQ;
     // Scheduling fences that keep each half's fragment reads ahead of the
     // multiplies that overlap them (and those multiplies on their side of the
