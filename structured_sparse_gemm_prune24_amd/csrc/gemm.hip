@@ -42,6 +42,7 @@ namespace p24 {
 
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int BK = 64;                 // logical K per main-loop iteration
@@ -69,7 +70,7 @@ struct TileCfg {
   static constexpr int TN = WTN / 32;              // ... (cols)
   static constexpr int RB = BM / 32;               // 32-row blocks per block
   static constexpr int ASTEPS = SPARSE ? 2 : 4;    // 1 KiB A blocks per row block per K step
-  // stage layout: [X tile | A blocks | metadata blocks]
+  // stage layout: [X tile | A blocks | metadata blocks | kept indices]
   static constexpr int ROWB = BN * 2;              // bytes per LDS row of an X tile
   static constexpr int CPR = BN / 8;               // 16 B chunks per X row
   static constexpr int X_BYTES = BK * ROWB;
@@ -78,7 +79,9 @@ struct TileCfg {
   // loads its whole group and reads its half)
   static constexpr int MG = SPARSE ? (RB >= 4 ? RB / 4 : 1) : 0;
   static constexpr int M_BYTES = MG * 1024;
-  static constexpr int STAGE = X_BYTES + A_BYTES + M_BYTES;
+  // gathered X on the sparse MFMA: the kept row indices of a later step (64 x 4 B)
+  static constexpr int K_BYTES = GATHER_X && AM == A_SPARSE ? 256 : 0;
+  static constexpr int STAGE = X_BYTES + A_BYTES + M_BYTES + K_BYTES;
   // A_DECOMP: one dense A tile (BM x BK bf16 in dense fragment order) after the stages
   static constexpr int D_BYTES = AM == A_DECOMP ? RB * 4 * 1024 : 0;
   static constexpr int NSTAGE = 3 * STAGE + D_BYTES <= LDS_LIMIT ? 3 : 2;
@@ -335,6 +338,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     return (uint32_t)(((q / ASTEPS) * S + q % ASTEPS) * 1024);
   };
   const bool meta_wave = wave < C::MG;
+  // waves with one load per step beyond their share of X and A: the metadata
+  // loaders and, for a gather on the sparse MFMA, the wave that brings the
+  // kept indices (defined below)
+  bool extra_wave = meta_wave;
   const int rb_end = nrb < rb0 + C::RB ? nrb : rb0 + C::RB;
   const __amdgpu_buffer_rsrc_t a_rsrc =
       make_rsrc(A + (int64_t)rb0 * S * 512, (uint32_t)((rb_end - rb0) * S * 1024));
@@ -368,6 +375,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       for (int j = 0; j < C::X_DMA; ++j) kk[j] = kept_tile[(int64_t)g * BK + x_r0 + j * X_ROW_STEP];
     }
   };
+  // On the sparse MFMA the indices travel through LDS instead: the loads of
+  // step g also bring the 64 indices of step g + NSTAGE into the stage's last
+  // 256 B (one 4-byte load per lane, by wave MG), ordered so that a lane's
+  // X_DMA entries are consecutive: position x_r0 * X_DMA + j holds entry
+  // x_r0 + j * X_ROW_STEP.  A wave reads them from the stage with that
+  // stage's fragments, so the loads of step g + NSTAGE, issued one step
+  // later, find their rows in registers and never wait on a global load.
+  constexpr bool KG = C::K_BYTES > 0;
+  static_assert(!KG || (C::X_DMA % 4 == 0 && C::MG < C::LW), "kept indices: whole 16-byte reads, a free loading wave");
+  constexpr int KV = KG ? C::X_DMA / 4 : 1;
+  constexpr int K_OFF = C::X_BYTES + C::A_BYTES + C::M_BYTES;
+  const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kept_tile, (uint32_t)(KG ? Kc * 4 : 0));
+  const uint32_t k_voff = (uint32_t)((lane / C::X_DMA) + (lane % C::X_DMA) * X_ROW_STEP) * 4;
+  const bool kept_wave = KG && wave == C::MG;
+  extra_wave = extra_wave || kept_wave;
+  i32x4 kv_cur[KV], kv_nxt[KV];
 
   // Load q of a loading wave's list for K step g into stage st: X loads
   // first (q < X_DMA), then A (q < X_DMA + A_DMA), then the metadata load of
@@ -380,7 +403,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     if constexpr (q < C::X_DMA) {
       constexpr int j = q;
       if constexpr (GATHER) {
-        int k = k_cur[j];
+        int k;
+        if constexpr (KG) k = kv_cur[j / 4][j % 4];
+        else k = k_cur[j];
         k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
         dma16_to_lds(xg_rsrc, stage + (j * C::LW + wave) * 1024, (uint32_t)(k * ldx * 2) + x_voff, 0);
       } else if constexpr (XT) {
@@ -397,6 +422,8 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       if (meta_wave)
         dma16_to_lds(m_rsrc, stage + C::X_BYTES + C::A_BYTES + wave * 1024, a_voff,
                      (uint32_t)g * 1024 + (uint32_t)wave * T_ * 1024);
+      else if (kept_wave)
+        dma4_to_lds(k_rsrc, stage + K_OFF, k_voff, (uint32_t)min(g + NSTAGE, nk - 1) * BK * 4);
     }
   };
   // loads [Q0, Q1) of K step g into stage st
@@ -491,6 +518,16 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     constexpr int st = decltype(ST)::value;
     static_for<0, TM>([&](auto I) { meta[decltype(I)::value] = lds_read_b32<decltype(I)::value * 256>(m_off[st]); });
   };
+  // this lane's kept indices from stage ST (those of the step NSTAGE after the stage's own)
+  auto rd_kept = [&](auto ST, i32x4 (&kv)[KV]) {
+    if constexpr (KG) {
+      constexpr int st = decltype(ST)::value;
+      const uint32_t ad = lds_base + st * C::STAGE + K_OFF + (uint32_t)x_r0 * C::X_DMA * 4;
+      static_for<0, KV>([&](auto V) {
+        kv[decltype(V)::value] = __builtin_bit_cast(i32x4, lds_read_b128<decltype(V)::value * 16>(ad));
+      });
+    }
+  };
   auto rd_a = [&](auto ST, auto SS, i16x8 (&a)[TM]) {
     constexpr int st = decltype(ST)::value;
     static_for<0, TM>([&](auto I) {
@@ -558,7 +595,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   };
 
   // One K step on stage ST (dense MFMA on packed W or on the expanded tile).
-  auto compute = [&](auto ST) {
+  // A loading wave (LD) issues its loads for step g into stage stl spread over
+  // the step's MFMAs, one after every (TM * TN * 4) / NQ of them, instead of
+  // in one burst ahead of them.
+  auto compute = [&](auto ST, auto LD, int g, int stl) {
     constexpr int st = decltype(ST)::value;
     if constexpr (!SMFMAC) {
       i16x8 a[2][TM], bb[2][TN];
@@ -590,13 +630,20 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         wait_lds(a[ss & 1]);
         wait_lds(bb[ss & 1]);
         if constexpr (ss + 1 < 4) read_step(std::integral_constant<int, ss + 1>{});
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-#pragma unroll
-          for (int j = 0; j < TN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ss & 1][i]),
-                                                                __builtin_bit_cast(bf16x8, bb[ss & 1][j]),
-                                                                acc[i][j], 0, 0, 0);
+        constexpr int NMF = TM * TN * 4, STRIDE = NMF / NQ > 0 ? NMF / NQ : 1;
+        static_for<0, TM * TN>([&](auto KC) {
+          constexpr int k = decltype(KC)::value, i = k / TN, j = k % TN, kk = ss * TM * TN + k;
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ss & 1][i]),
+                                                              __builtin_bit_cast(bf16x8, bb[ss & 1][j]),
+                                                              acc[i][j], 0, 0, 0);
+          if constexpr (decltype(LD)::value && kk % STRIDE == 0 && kk / STRIDE < NQ) {
+            issue_one(std::integral_constant<int, kk / STRIDE>{}, g, stl);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        });
+        if constexpr (decltype(LD)::value && ss == 3)
+          static_for<(NMF + STRIDE - 1) / STRIDE < NQ ? (NMF + STRIDE - 1) / STRIDE : NQ, NQ>(
+              [&](auto Q) { issue_one(Q, g, stl); });
       });
     }
   };
@@ -641,14 +688,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     using QNQ = std::integral_constant<int, NQ>;
 #pragma unroll
     for (int g = 0; g < NSTAGE; ++g) {
-      load_kept(min(g, nk - 1), k_cur);
+      if constexpr (KG) {
+        // the prologue's own steps take their indices straight from the list
+        if (loader)
+#pragma unroll
+          for (int j = 0; j < C::X_DMA; ++j)
+            kv_cur[j / 4][j % 4] = kept_tile[(int64_t)min(g, nk - 1) * BK + x_r0 + j * X_ROW_STEP];
+      } else {
+        load_kept(min(g, nk - 1), k_cur);
+      }
       if (SPLIT && g == NSTAGE - 1) issue_range(I0{}, QP0{}, min(g, nk - 1), g);
       else issue_step(min(g, nk - 1), g);
     }
-    load_kept(min(NSTAGE, nk - 1), k_cur);
+    if constexpr (!KG) load_kept(min(NSTAGE, nk - 1), k_cur);
     constexpr int PRO_M = SPLIT ? (NSTAGE - 2) * C::DMA_M + P0 : (NSTAGE - 1) * C::DMA_M;
     constexpr int PRO_O = SPLIT ? (NSTAGE - 2) * C::DMA_O + P0 : (NSTAGE - 1) * C::DMA_O;
-    wait_vmcnt_by_wave<PRO_M, PRO_O>(meta_wave);
+    wait_vmcnt_by_wave<PRO_M, PRO_O>(extra_wave);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     // The fragment reads are asynchronous (results land at the lgkmcnt wait)
@@ -662,9 +717,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     rd_meta(I0{}, meta[0]);
     rd_a(I0{}, I0{}, a0);
     rd_b(I0{}, I0{}, b0);
+    rd_kept(I0{}, kv_cur);
     wait_lds(meta[0]);
     wait_lds(a0);
     wait_lds(b0);
+    if constexpr (KG) wait_lds(kv_cur);
     auto body = [&](auto ST, auto LD, int it) {
       constexpr int st = decltype(ST)::value;
       constexpr int nx = (st + 1) % NSTAGE;
@@ -679,11 +736,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       wait_lds(a1);
       wait_lds(b1);
-      wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(meta_wave);
+      wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(extra_wave);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
-      load_kept(min(it + NSTAGE + 1, nk - 1), k_nxt);
+      if constexpr (!KG) load_kept(min(it + NSTAGE + 1, nk - 1), k_nxt);
       if constexpr (!SPLIT) {
         if constexpr (decltype(LD)::value) issue_step(min(it + NSTAGE, nk - 1), st);
         asm volatile("" ::: "memory");
@@ -691,6 +748,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       rd_meta(std::integral_constant<int, nx>{}, meta[nx]);
       rd_a(std::integral_constant<int, nx>{}, I0{}, a0);
       rd_b(std::integral_constant<int, nx>{}, I0{}, b0);
+      rd_kept(std::integral_constant<int, nx>{}, kv_nxt);
       if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       if constexpr (SPLIT)
         mma_sparse_loads(LD, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st);
@@ -700,9 +758,10 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       wait_lds(meta[nx]);
       wait_lds(a0);
       wait_lds(b0);
-      if constexpr (GATHER) {
+      if constexpr (KG) {
+        wait_lds(kv_nxt);
 #pragma unroll
-        for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
+        for (int v = 0; v < KV; ++v) kv_cur[v] = kv_nxt[v];
       }
     };
     // loading and non-loading waves run separate copies of the loop (the
@@ -732,15 +791,19 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       issue_step(min(g, nk - 1), g);
     }
     load_kept(min(NSTAGE - 1, nk - 1), k_cur);
-    auto body = [&](auto ST, int it) {
+    // The expanded-tile path keeps its loads ahead of the expansion.
+    constexpr bool SPREAD = !DECOMP;
+    auto body = [&](auto ST, auto LD, int it) {
       constexpr int st = decltype(ST)::value;
       wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(meta_wave);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
-      const int gn = it + NSTAGE - 1;
-      load_kept(min(gn + 1, nk - 1), k_nxt);
-      issue_step(min(gn, nk - 1), (st + NSTAGE - 1) % NSTAGE);
-      asm volatile("" ::: "memory");
+      const int gn = min(it + NSTAGE - 1, nk - 1), sn = (st + NSTAGE - 1) % NSTAGE;
+      load_kept(min(it + NSTAGE, nk - 1), k_nxt);
+      if constexpr (!SPREAD) {
+        issue_step(gn, sn);
+        asm volatile("" ::: "memory");
+      }
       if constexpr (DECOMP) {
         // the dense tile is rewritten after the barrier above (every wave is past
         // its reads of the previous step) and read after this one
@@ -748,17 +811,23 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
       }
-      compute(ST);
+      compute(ST, std::integral_constant<bool, SPREAD && decltype(LD)::value>{}, gn, sn);
       if constexpr (GATHER) {
 #pragma unroll
         for (int j = 0; j < C::X_DMA; ++j) k_cur[j] = k_nxt[j];
       }
     };
-    for (int it = 0; it < nk; it += NSTAGE) {
-      static_for<0, NSTAGE>([&](auto ST) {
-        if (it + decltype(ST)::value < nk) body(ST, it + decltype(ST)::value);
-      });
-    }
+    // loading and non-loading waves run separate copies of the loop (no branch
+    // between a fragment read and its wait)
+    auto main_loop = [&](auto LD) {
+      for (int it = 0; it < nk; it += NSTAGE) {
+        static_for<0, NSTAGE>([&](auto ST) {
+          if (it + decltype(ST)::value < nk) body(ST, LD, it + decltype(ST)::value);
+        });
+      }
+    };
+    if (loader) main_loop(std::true_type{});
+    else main_loop(std::false_type{});
   }
 
   // The last NSTAGE-1 steps issued loads into stages that are never read; they

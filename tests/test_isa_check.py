@@ -50,6 +50,31 @@ def test_partial_wait_completes_older_reads():
     assert I.pending_lds_uses(asm) == {}
 
 
+def test_unconditional_branch_does_not_fall_through():
+    # the read before s_branch is waited on the taken path; the label after it is reached only by a
+    # jump from a point with nothing in flight
+    asm = _k("\ts_cbranch_scc1 .LBB0_2\n\tds_read_b32 v10, v1\n\ts_branch .LBB0_3\n"
+             ".LBB0_2:\n\tv_mov_b32_e32 v10, 0\n\ts_endpgm\n"
+             ".LBB0_3:\n\ts_waitcnt lgkmcnt(0)\n\tv_mov_b32_e32 v5, v10\n\ts_endpgm\n")
+    assert I.pending_lds_uses(asm) == {}
+
+
+def test_loop_back_edge_carries_pending_reads():
+    # a read issued at the end of the loop body is still in flight at the top of the next
+    # iteration, where a copy uses it (a program-order scan would see the copy first)
+    asm = _k(".LBB0_1:\n\tv_mov_b32_e32 v5, v10\n\ts_waitcnt lgkmcnt(0)\n\tds_read_b32 v10, v1\n"
+             "\ts_cbranch_scc1 .LBB0_1\n\ts_waitcnt lgkmcnt(0)\n\ts_endpgm\n")
+    found = list(I.pending_lds_uses(asm).values())
+    assert found == [["v_mov_b32_e32 v5, v10"]]
+
+
+def test_paths_merge_at_a_join():
+    # one path waits, the other does not: the join keeps the read pending
+    asm = _k("\tds_read_b32 v10, v1\n\ts_cbranch_scc1 .LBB0_2\n\ts_waitcnt lgkmcnt(0)\n"
+             ".LBB0_2:\n\tv_mov_b32_e32 v5, v10\n\ts_waitcnt lgkmcnt(0)\n\ts_endpgm\n")
+    assert list(I.pending_lds_uses(asm).values()) == [["v_mov_b32_e32 v5, v10"]]
+
+
 def test_flags_spills():
     assert I.spilling_kernels(_k("\tscratch_store_dword off, v0, off offset:384\n")) == [HEAD.split()[0][:-1]]
     assert I.spilling_kernels(_k("\tv_mov_b32_e32 v1, v2\n\tglobal_store_dword v[2:3], v1, off\n")) == []
