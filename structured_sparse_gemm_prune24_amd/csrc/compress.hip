@@ -335,6 +335,42 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
   scores[id] = canonical_score(acc);
 }
 
+// The same scores four columns per thread with 16-byte loads (K and the row
+// stride multiples of 4, W 16-byte aligned); each column's sum still runs
+// over its rows in order.
+__global__ __launch_bounds__(256) void k_tvw_scores4(const float* __restrict__ W, int64_t ldw, int64_t M,
+                                                     int64_t K, int64_t tile_m, double* __restrict__ scores) {
+  const int64_t T_ = (M + tile_m - 1) / tile_m, K4 = K / 4;
+  const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (id >= T_ * K4) return;
+  const int64_t t = id / K4, k = 4 * (id % K4);
+  const int64_t r1 = (t + 1) * tile_m < M ? (t + 1) * tile_m : M;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  int64_t m = t * tile_m;
+  for (; m + 8 <= r1; m += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = *reinterpret_cast<const float4*>(W + (m + u) * ldw + k);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      acc[0] = acc[0] + fabs((double)v[u].x);
+      acc[1] = acc[1] + fabs((double)v[u].y);
+      acc[2] = acc[2] + fabs((double)v[u].z);
+      acc[3] = acc[3] + fabs((double)v[u].w);
+    }
+  }
+  for (; m < r1; ++m) {
+    const float4 v = *reinterpret_cast<const float4*>(W + m * ldw + k);
+    acc[0] = acc[0] + fabs((double)v.x);
+    acc[1] = acc[1] + fabs((double)v.y);
+    acc[2] = acc[2] + fabs((double)v.z);
+    acc[3] = acc[3] + fabs((double)v.w);
+  }
+#pragma unroll
+  for (int c = 0; c < 4; ++c) scores[t * K + k + c] = canonical_score(acc[c]);
+}
+
+
 // --------------------------------------------------------------------------
 // TVW selection: one block per tile.  The kept set is the keep_k largest
 // scores, ties to the lower column.  Scores are non-negative fp64 sums with
@@ -347,6 +383,7 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
 // --------------------------------------------------------------------------
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int64_t SEL_LDS_KEYS = 8192;   // 64 KiB of fp64 keys per block
 
 // Exclusive block-wide prefix of per-thread counts in thread order (blocks of
 // SEL_THREADS); returns this thread's prefix and writes the block total.
@@ -410,9 +447,18 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
   __shared__ uint64_t sh_prefix;
   __shared__ int64_t sh_need;
   __shared__ uint32_t sh_whole;
+  __shared__ uint64_t skey[SEL_LDS_KEYS];
   const int64_t t = blockIdx.x;
-  const uint64_t* key = reinterpret_cast<const uint64_t*>(scores + t * K);
+  const uint64_t* gkey = reinterpret_cast<const uint64_t*>(scores + t * K);
   const int tid = threadIdx.x;
+  // A tile's keys are read from memory once into LDS when they fit (every
+  // pass below then reads LDS), else each pass reads them from memory.
+  const bool in_lds = K <= SEL_LDS_KEYS;
+  if (in_lds) {
+    for (int64_t k = tid; k < K; k += SEL_THREADS) skey[k] = gkey[k];
+    __syncthreads();
+  }
+  auto key = [&](int64_t k) -> uint64_t { return in_lds ? skey[k] : gkey[k]; };
   // per-tile keep counts: this tile's count and list position from the offsets
   int32_t* kept_out = kept + t * keep_k;
   if (offsets) {
@@ -425,9 +471,23 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
     for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0u;
     __syncthreads();
     const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-    for (int64_t k = tid; k < K; k += SEL_THREADS) {
-      const uint64_t x = key[k];
-      if ((x & hi_mask) == prefix) atomicAdd(&hist[(x >> shift) & 255u], 1u);
+    // A tile's keys mostly share their high digits: when every matching key
+    // of a wave has the same digit, one lane adds them all (one LDS address
+    // hit by each lane in turn would serialise the wave).
+    for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS) {
+      const int64_t k = k0 + tid;
+      const uint64_t x = k < K ? key(k) : 0ull;
+      const bool match = k < K && (x & hi_mask) == prefix;
+      const uint32_t d = (uint32_t)(x >> shift) & 255u;
+      const uint64_t mm = __ballot(match);
+      if (!mm) continue;                                    // wave-uniform
+      const int l0 = __builtin_ffsll((long long)mm) - 1;
+      const uint32_t d0 = (uint32_t)__shfl((int)d, l0);
+      if (__ballot(match && d == d0) == mm) {
+        if ((tid & 63) == l0) atomicAdd(&hist[d0], (uint32_t)__builtin_popcountll(mm));
+      } else if (match) {
+        atomicAdd(&hist[d], 1u);
+      }
     }
     __syncthreads();
     if (tid < 64) {
@@ -453,20 +513,29 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
       break;
     }
   }
-  // prefix is the threshold key; `need` columns equal to it are kept, lowest first
-  int64_t eq_base = 0, out_base = 0;
-  for (int64_t k0 = 0; k0 < K; k0 += SEL_THREADS) {
-    const int64_t k = k0 + tid;
-    const uint64_t x = k < K ? key[k] : 0ull;
-    const bool gt = k < K && x > prefix;
-    const bool eq = k < K && x == prefix;
-    int64_t eq_total, keep_total;
-    const int64_t eq_rank = eq_base + block_exclusive_scan<uint32_t>(eq ? 1u : 0u, &eq_total, wave_sums);
-    const bool keep = gt || (eq && eq_rank < need);
-    const int64_t pos = out_base + block_exclusive_scan<uint32_t>(keep ? 1u : 0u, &keep_total, wave_sums);
+  // prefix is the threshold key; `need` columns equal to it are kept, lowest
+  // first.  Thread tid takes the columns [tid * C, tid * C + C): a scan of the
+  // per-thread counts of keys equal to the threshold gives each thread the rank
+  // of its first such key, a second scan of the kept counts its first output
+  // position, and the thread then writes its kept columns in order.
+  const int64_t C = (K + SEL_THREADS - 1) / SEL_THREADS;
+  const int64_t k_lo = tid * C < K ? tid * C : K, k_hi = k_lo + C < K ? k_lo + C : K;
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int64_t k = k_lo; k < k_hi; ++k) {
+    const uint64_t x = key(k);
+    n_gt += x > prefix ? 1u : 0u;
+    n_eq += x == prefix ? 1u : 0u;
+  }
+  int64_t total;
+  const int64_t eq_rank0 = block_exclusive_scan<uint32_t>(n_eq, &total, wave_sums);
+  const int64_t eq_kept = need - eq_rank0 <= 0 ? 0 : (need - eq_rank0 < n_eq ? need - eq_rank0 : n_eq);
+  int64_t pos = block_exclusive_scan<uint32_t>(n_gt + (uint32_t)eq_kept, &total, wave_sums);
+  int64_t eq_left = eq_kept;
+  for (int64_t k = k_lo; k < k_hi; ++k) {
+    const uint64_t x = key(k);
+    const bool keep = x > prefix || (x == prefix && eq_left-- > 0);
     if (keep && pos < keep_k) kept_out[pos] = (int32_t)k;   // exactly keep_k keys are kept; the bound is a guard
-    eq_base += eq_total;
-    out_base += keep_total;
+    pos += keep ? 1 : 0;
   }
 }
 
@@ -850,6 +919,15 @@ using namespace p24;
 
 static inline unsigned grid1d(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
+static void launch_tvw_scores(const float* W, int64_t ldw, int64_t M, int64_t K, int64_t tile_m, double* scores,
+                              hipStream_t st) {
+  const int64_t T_ = (M + tile_m - 1) / tile_m;
+  if (K % 4 == 0 && ldw % 4 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
+    hipLaunchKernelGGL(k_tvw_scores4, dim3(grid1d(T_ * (K / 4), 256)), dim3(256), 0, st, W, ldw, M, K, tile_m, scores);
+  else
+    hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, W, ldw, M, K, tile_m, scores);
+}
+
 extern "C" P24_API size_t prune24_values_bytes(int64_t M, int64_t K, int32_t layout) {
   if (M < 0 || K < 0 || K % 4) return 0;
   if (layout == P24_LAYOUT_CANONICAL) return (size_t)M * (size_t)(K / 2) * 2;
@@ -1016,8 +1094,7 @@ static p24_status tvw_launch(const void* W, int32_t w_dtype, int64_t M, int64_t 
                              void* workspace, hipStream_t st) {
   const int64_t T_ = (M + tile_m - 1) / tile_m;
   double* scores = (double*)workspace;
-  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
-                     tile_m, scores);
+  launch_tvw_scores((const float*)W, ldw, M, K, tile_m, scores, st);
   p24_status s = launch_status();
   if (s != P24_OK) return s;
   hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
@@ -1116,8 +1193,7 @@ static p24_status launch_var_plan(const void* W, int64_t M, int64_t K, int64_t l
   int32_t* gt = (int32_t*)ws;
   int32_t* eq = gt + T_;
   const int64_t n = T_ * K;
-  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(n, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
-                     (int64_t)128, scores);
+  launch_tvw_scores((const float*)W, ldw, M, K, 128, scores, st);
   hipLaunchKernelGGL(k_var_init, dim3(1), dim3(VAR_THREADS), 0, st, vs, total_keep);
   const int64_t per_block = (int64_t)VAR_THREADS * 8;
   const unsigned radix_blocks = (unsigned)std::min<int64_t>((n + per_block - 1) / per_block, 1024);
@@ -1182,8 +1258,7 @@ extern "C" P24_API p24_status tw_compress(const void* W, int32_t w_dtype, int64_
   hipStream_t st = (hipStream_t)stream;
   const int64_t T_ = (M + tile_m - 1) / tile_m;
   double* scores = (double*)workspace;
-  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
-                     tile_m, scores);
+  launch_tvw_scores((const float*)W, ldw, M, K, tile_m, scores, st);
   hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
                      keep_k, (const int64_t*)nullptr, kept);
   const int64_t rows = (M + 31) / 32 * 32;
@@ -1235,8 +1310,7 @@ extern "C" P24_API p24_status bw_compress(const void* W, int32_t w_dtype, int64_
   double* scores = (double*)workspace;
   double* bscores = scores + T_ * K;
   int32_t* kept_blocks = (int32_t*)(bscores + T_ * nb);
-  hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, (const float*)W, ldw, M, K,
-                     (int64_t)128, scores);
+  launch_tvw_scores((const float*)W, ldw, M, K, 128, scores, st);
   hipLaunchKernelGGL(k_bw_block_scores, dim3(grid1d(T_ * nb, 256)), dim3(256), 0, st, (const double*)scores, T_, K,
                      bscores);
   hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)bscores, nb,
