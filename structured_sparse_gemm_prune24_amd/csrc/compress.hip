@@ -582,9 +582,22 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_radix(const uint64_t* __res
   h[tid] = 0u;
   __syncthreads();
   const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
-  for (int64_t i = (int64_t)blockIdx.x * VAR_THREADS + tid; i < n; i += (int64_t)gridDim.x * VAR_THREADS) {
-    const uint64_t x = keys[i];
-    if ((x & hi_mask) == prefix) atomicAdd(&h[(x >> shift) & 255u], 1u);
+  // as in the per-tile select: a wave whose matching keys share one digit adds
+  // them with one atomic
+  for (int64_t i0 = (int64_t)blockIdx.x * VAR_THREADS; i0 < n; i0 += (int64_t)gridDim.x * VAR_THREADS) {
+    const int64_t i = i0 + tid;
+    const uint64_t x = i < n ? keys[i] : 0ull;
+    const bool match = i < n && (x & hi_mask) == prefix;
+    const uint32_t d = (uint32_t)(x >> shift) & 255u;
+    const uint64_t mm = __ballot(match);
+    if (!mm) continue;                                      // wave-uniform
+    const int l0 = __builtin_ffsll((long long)mm) - 1;
+    const uint32_t d0 = (uint32_t)__shfl((int)d, l0);
+    if (__ballot(match && d == d0) == mm) {
+      if ((tid & 63) == l0) atomicAdd(&h[d0], (uint32_t)__builtin_popcountll(mm));
+    } else if (match) {
+      atomicAdd(&h[d], 1u);
+    }
   }
   __syncthreads();
   if (h[tid]) atomicAdd(&vs->hist[tid], h[tid]);
