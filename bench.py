@@ -324,17 +324,20 @@ def traffic_source(traffic):
 def spmm24_kernel(M, N, env=None):
     """The k_gemm instantiation spmm24 launches for an M x N output, by the library's tile rule:
     the first of 256x256, 128x256, 128x128, 64x128 that gives at least 160 blocks (else
-    64x128), or the tile P24_TILE forces."""
+    64x128), with 192x256 instead of 256x256 when that fills more of a single round of the
+    256 CUs; or the tile P24_TILE forces."""
     env = os.environ if env is None else env
-    waves = {"256x256": (2, 4), "128x256": (2, 4), "128x128": (2, 4), "64x128": (2, 2)}
+    waves = {"256x256": (2, 4), "192x256": (2, 4), "128x256": (2, 4), "128x128": (2, 4), "64x128": (2, 2)}
+    nblocks = lambda t: -(-M // int(t.split("x")[0])) * -(-N // int(t.split("x")[1]))
     tile = env.get("P24_TILE") if env.get("P24_TILE") in waves else None
     if tile is None:
         tile = "64x128"
         for t in ("256x256", "128x256", "128x128", "64x128"):
-            bm, bn = (int(v) for v in t.split("x"))
-            if -(-M // bm) * -(-N // bn) >= 160:
+            if nblocks(t) >= 160:
                 tile = t
                 break
+        if tile == "256x256" and nblocks("256x256") < 256 and nblocks("256x256") < nblocks("192x256") <= 256:
+            tile = "192x256"
     bm, bn = tile.split("x")
     wm, wn = waves[tile]
     return f"k_gemm<{bm},{bn},{wm},{wn},sparse,X_KN> (spmm24)"

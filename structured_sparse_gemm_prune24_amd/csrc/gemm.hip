@@ -76,8 +76,9 @@ struct TileCfg {
   static constexpr int X_BYTES = BK * ROWB;
   static constexpr int A_BYTES = RB * ASTEPS * 1024;
   // metadata: one 1 KiB load per group of four row blocks (a 64-row block
-  // loads its whole group and reads its half)
-  static constexpr int MG = SPARSE ? (RB >= 4 ? RB / 4 : 1) : 0;
+  // loads its whole group and reads its half; a 192-row block, which starts
+  // at a group boundary or in the middle of a group, loads two groups)
+  static constexpr int MG = SPARSE ? (RB % 4 == 0 ? RB / 4 : RB / 4 + 1) : 0;
   static constexpr int M_BYTES = MG * 1024;
   // gathered X on the sparse MFMA: the kept row indices of a later step (64 x 4 B)
   static constexpr int K_BYTES = GATHER_X && AM == A_SPARSE ? 256 : 0;
@@ -109,7 +110,7 @@ struct TileCfg {
   static_assert(BM % (32 * WGM) == 0 && BN % (32 * WGN) == 0, "wave tiles must be multiples of 32");
   static_assert(X_BYTES % (1024 * LW) == 0 && A_BYTES % (1024 * LW) == 0, "even load split");
   static_assert(AM != A_DECOMP || RB % NWAVES == 0, "the expansion splits row blocks evenly among waves");
-  static_assert(RB >= 4 ? RB % 4 == 0 : RB == 2, "row blocks come in whole metadata groups or one half");
+  static_assert(RB % 4 == 0 || RB == 2 || RB == 6, "row blocks: whole metadata groups, one half, or one and a half");
   static_assert(MG <= LW, "one metadata load per loading wave at most");
   static_assert(CPR >= 16, "the chunk swizzle needs at least 16 chunks per row");
   static_assert(2 * STAGE + D_BYTES <= LDS_LIMIT, "two stages must fit in LDS");
@@ -350,7 +351,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   const int g_end = ngroups < g0 + C::MG ? ngroups : g0 + C::MG;
   const __amdgpu_buffer_rsrc_t m_rsrc =
       SPARSE ? make_rsrc(Ameta + (int64_t)g0 * T_ * 256, (uint32_t)((g_end - g0) * T_ * 1024)) : a_rsrc;
-  const int m_in_group = C::RB < 4 ? (rb0 & 3) : 0;         // a 64-row block's row blocks inside its group
+  const int m_in_group = C::RB % 4 ? (rb0 & 3) : 0;        // first row block's place in its metadata group
   const int n_rows = N - n0 < BN ? N - n0 : BN;
   const __amdgpu_buffer_rsrc_t xt_rsrc =
       make_rsrc(args.X + (XT ? (int64_t)n0 * ldx : 0), (uint32_t)(XT ? (int64_t)n_rows * ldx * 2 : 0));
@@ -982,7 +983,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
 // ---------------------------------------------------------------------------
 // Host-side tile configuration and dispatch
 // ---------------------------------------------------------------------------
-enum class Tile { T256x256, T128x256, T128x128, T64x128 };
+enum class Tile { T256x256, T192x256, T128x256, T128x128, T64x128 };
 
 template <int BM, int BN, int WGM, int WGN, int AM, int XM, int EPI = 0>
 static p24_status launch_cfg(GemmArgs a, int32_t y_dtype, hipStream_t st) {
@@ -1000,6 +1001,7 @@ static int64_t nblocks_for(Tile t, int64_t M, int64_t N) {
   int bm = 256, bn = 256;
   switch (t) {
     case Tile::T256x256: bm = 256; bn = 256; break;
+    case Tile::T192x256: bm = 192; bn = 256; break;
     case Tile::T128x256: bm = 128; bn = 256; break;
     case Tile::T128x128: bm = 128; bn = 128; break;
     case Tile::T64x128: bm = 64; bn = 128; break;
@@ -1014,28 +1016,41 @@ static int64_t nblocks_for(Tile t, int64_t M, int64_t N) {
 // blocks per CU, win on parallelism.  Measured: 256x256 on the 8192^3 and
 // BERT FFN shapes, 128x256 on one GPU's share of 8192^3 split 8 ways (256
 // blocks; 7 % over 128x128), 128x128 and 64x128 on the ResNet-50 shapes.
-// P24_TILE=<256x256|128x256|128x128|64x128> overrides (measurement aid).
-static Tile choose_tile(int64_t M, int64_t N) {
+// When 256x256 leaves part of a single round of CUs idle and 192x256 fills
+// more of that round (the BERT FFN shape: 192 blocks become 256), the
+// sparse products take 192x256.
+// P24_TILE=<256x256|192x256|128x256|128x128|64x128> overrides (measurement aid).
+static Tile choose_tile(int64_t M, int64_t N, bool tall_ok) {
   if (const char* e = getenv("P24_TILE")) {
     const std::string s(e);
     if (s == "256x256") return Tile::T256x256;
+    if (s == "192x256" && tall_ok) return Tile::T192x256;
     if (s == "128x256") return Tile::T128x256;
     if (s == "128x128") return Tile::T128x128;
     if (s == "64x128") return Tile::T64x128;
   }
+  constexpr int64_t CUS = 256;
   const Tile order[] = {Tile::T256x256, Tile::T128x256, Tile::T128x128, Tile::T64x128};
   for (Tile t : order)
-    if (nblocks_for(t, M, N) >= 160) return t;
+    if (nblocks_for(t, M, N) >= 160) {
+      const int64_t n256 = nblocks_for(Tile::T256x256, M, N), n192 = nblocks_for(Tile::T192x256, M, N);
+      if (t == Tile::T256x256 && tall_ok && n256 < CUS && n192 <= CUS && n192 > n256) return Tile::T192x256;
+      return t;
+    }
   return Tile::T64x128;
 }
 
 template <int AM, int XM, int EPI = 0>
 static p24_status dispatch(const GemmArgs& a, int32_t y_dtype, hipStream_t st) {
-  switch (choose_tile(a.M, a.N)) {
+  switch (choose_tile(a.M, a.N, AM == A_SPARSE)) {
     // The 256 x 256 tile runs 8 waves (2 x 4, each 128 x 64), two per SIMD:
     // while one wave waits on LDS reads or the stage barrier the other issues
-    // MFMAs.  The 128 x 256 smfmac tile does the same with 64 x 64 per wave.
+    // MFMAs.  The 128 x 256 smfmac tile does the same with 64 x 64 per wave,
+    // the 192 x 256 one with 96 x 64.
     case Tile::T256x256: return launch_cfg<256, 256, 2, 4, AM, XM, EPI>(a, y_dtype, st);
+    case Tile::T192x256:
+      if constexpr (AM == A_SPARSE) return launch_cfg<192, 256, 2, 4, AM, XM, EPI>(a, y_dtype, st);
+      else return launch_cfg<256, 256, 2, 4, AM, XM, EPI>(a, y_dtype, st);
     case Tile::T128x256:
       if constexpr (AM == A_SPARSE) return launch_cfg<128, 256, 2, 4, AM, XM, EPI>(a, y_dtype, st);
       else return launch_cfg<128, 256, 2, 2, AM, XM, EPI>(a, y_dtype, st);

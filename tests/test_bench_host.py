@@ -90,7 +90,7 @@ def test_cpu_baseline_on_the_small_workload():
 def test_spmm24_kernel_label_follows_the_tile_rule():
     """The roofline's kernel name is the instantiation the library's tile rule picks."""
     import workloads
-    want = {"c1": "64x128", "c2": "256x256", "c3a": "128x128", "c3b": "64x128", "c4": "256x256",
+    want = {"c1": "64x128", "c2": "192x256", "c3a": "128x128", "c3b": "64x128", "c4": "256x256",
             "c4n8": "128x256", "c4m8": "128x256"}
     for key, tile in want.items():
         wl = workloads.WORKLOADS[key]
@@ -98,6 +98,7 @@ def test_spmm24_kernel_label_follows_the_tile_rule():
         assert bench.spmm24_kernel(wl.M, wl.N, env={}).startswith(f"k_gemm<{bm},{bn},"), key
     assert bench.spmm24_kernel(8192, 8192, env={}) == "k_gemm<256,256,2,4,sparse,X_KN> (spmm24)"
     assert bench.spmm24_kernel(8192, 8192, env={"P24_TILE": "128x128"}).startswith("k_gemm<128,128,2,4,")
+    assert bench.spmm24_kernel(8192, 8192, env={"P24_TILE": "192x256"}).startswith("k_gemm<192,256,2,4,")
     assert bench.spmm24_kernel(8192, 8192, env={"P24_TILE": "bogus"}).startswith("k_gemm<256,256,")
 
 

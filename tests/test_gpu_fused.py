@@ -76,7 +76,7 @@ def test_fused_noop_is_plain_product(order):
     assert torch.equal(Y1, Y2)
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x256", "128x128", "64x128"])
+@pytest.mark.parametrize("tile", ["256x256", "192x256", "128x256", "128x128", "64x128"])
 def test_fused_every_tile(tile, monkeypatch):
     need_gpu()
     monkeypatch.setenv("P24_TILE", tile)

@@ -19,7 +19,7 @@ from gpu_util import (DEV, bf16_dev, cached_ref, check_full, f32_dev, need_gpu, 
 p24 = pytest.importorskip("structured_sparse_gemm_prune24_amd")
 pytestmark = pytest.mark.gpu
 
-TILES = ["256x256", "128x256", "128x128", "64x128"]
+TILES = ["256x256", "192x256", "128x256", "128x128", "64x128"]
 
 
 def _run_sparse(W, Xb, out_dtype, x_pad=0):
@@ -66,6 +66,20 @@ def test_every_tile_config(tile, monkeypatch):
     Xb = workloads.random_bf16((K, N), seed=12)
     _, Y = _run_sparse(W, Xb, torch.float32)
     _check(Y, W, Xb, "f32")
+
+
+def test_192_row_tiles(monkeypatch):
+    """192-row blocks start on a metadata-group boundary (even block rows) or in the middle of
+    a group (odd ones); several of each, a ragged last block row, ragged N."""
+    need_gpu()
+    monkeypatch.setenv("P24_TILE", "192x256")
+    M, K, N = 1000, 384, 696
+    print(f"[spmm24] 192x256 tiles {M}x{K}x{N}", flush=True)
+    W = workloads.random_matrix((M, K), seed=21, sigma=0.05)
+    Xb = workloads.random_bf16((K, N), seed=22)
+    for out_dtype, out in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+        _, Y = _run_sparse(W, Xb, out_dtype)
+        _check(Y, W, Xb, out)
 
 
 def test_integer_exact_and_identity():

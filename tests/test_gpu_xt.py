@@ -55,7 +55,7 @@ def test_spmm24_xt_matches_kn_path_and_oracle(M, K, N, out):
     assert ok, worst
 
 
-@pytest.mark.parametrize("tile", ["256x256", "128x256", "128x128", "64x128"])
+@pytest.mark.parametrize("tile", ["256x256", "192x256", "128x256", "128x128", "64x128"])
 def test_spmm24_xt_every_tile(tile, monkeypatch):
     need_gpu()
     monkeypatch.setenv("P24_TILE", tile)
