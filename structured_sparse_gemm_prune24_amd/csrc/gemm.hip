@@ -574,6 +574,56 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // issued one after each MFMA, the rest after the last: spread out this way
   // a loading wave's vector-memory issue waits sit in the shadow of its
   // MFMAs instead of holding them back in one burst.
+  // Fragment reads one at a time: read r of a half's list (the metadata
+  // words, the A blocks, then the four 8-byte transposing pieces of each B
+  // fragment) from stage ST, half SS.
+  auto rd_one = [&](auto ST, auto SS, auto R, uint32_t (&meta)[TM], i16x8 (&a)[TM], i16x4 (&bq)[TN][4]) {
+    constexpr int st = decltype(ST)::value, ss = decltype(SS)::value;
+    constexpr int r = decltype(R)::value;
+    if constexpr (r < TM) {
+      meta[r] = lds_read_b32<r * 256>(m_off[st]);
+    } else if constexpr (r < 2 * TM) {
+      constexpr int i = r - TM;
+      a[i] = lds_read_b128<(i * ASTEPS + ss) * 1024>(a_off[st]);
+    } else {
+      constexpr int q = r - 2 * TM, j = q / 4, piece = q % 4;
+      constexpr int OFFS[4] = {0, 4 * C::ROWB, 16 * C::ROWB, 20 * C::ROWB};
+      bq[j][piece] = lds_read_tr<32 * ss * C::ROWB + OFFS[piece]>(b_off[st][j]);
+    }
+  };
+  auto assemble_b = [&](const i16x4 (&bq)[TN][4], i16x16 (&bf)[TN]) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const i16x8 lo = __builtin_shufflevector(bq[j][0], bq[j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+      const i16x8 hi = __builtin_shufflevector(bq[j][2], bq[j][3], 0, 1, 2, 3, 4, 5, 6, 7);
+      bf[j] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+    }
+  };
+  // The MFMAs of half SS with this wave's loads [Q0, Q1) (loading waves only)
+  // and the reads [R0, R1) of stage RST, half RSS, spread over them: after
+  // MFMA k go load Q0 + k and the k-th share of the reads, all of them within
+  // the first three quarters of the MFMAs so that the last ones still cover
+  // the reads' latency.
+  auto mma_io = [&](auto LD, auto SS, const i16x8 (&a)[TM], const i16x16 (&bf)[TN], const uint32_t (&meta)[TM],
+                    auto Q0, auto Q1, int g, int stl, auto RST, auto RSS, auto R0, auto R1,
+                    uint32_t (&rmeta)[TM], i16x8 (&ra)[TM], i16x4 (&rbq)[TN][4]) {
+    constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
+    constexpr int r0 = decltype(R0)::value, r1 = decltype(R1)::value, NR = r1 - r0;
+    constexpr int SPREAD = TM * TN * 3 / 4 > 0 ? TM * TN * 3 / 4 : 1;
+    static_for<0, TM * TN>([&](auto KC) {
+      constexpr int k = decltype(KC)::value, i = k / TN, j = k % TN;
+      acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
+                                                            __builtin_bit_cast(bf16x16, bf[j]), acc[i][j],
+                                                            (int)meta[i], 0, decltype(SS)::value);
+      if constexpr (decltype(LD)::value && q0 + k < q1) issue_one(std::integral_constant<int, q0 + k>{}, g, stl);
+      constexpr int lo = k < SPREAD ? r0 + (NR * k) / SPREAD : r1;
+      constexpr int hi = k < SPREAD ? r0 + (NR * (k + 1)) / SPREAD : r1;
+      static_for<lo, hi>([&](auto R) { rd_one(RST, RSS, R, rmeta, ra, rbq); });
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (decltype(LD)::value)
+      static_for<q0 + TM * TN < q1 ? q0 + TM * TN : q1, q1>([&](auto Q) { issue_one(Q, g, stl); });
+  };
   // LD (compile time) says whether this wave loads: a branch on it here,
   // between fragment reads and their wait, would let the compiler copy the
   // read registers at the join before they have arrived.
@@ -715,6 +765,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     uint32_t meta[NSTAGE][TM];
     i16x8 a0[TM], a1[TM];
     i16x16 b0[TN], b1[TN];
+    // Where the reads fit between the MFMAs (the fenced plain-X tiles with
+    // spread loads and at least four MFMAs per half), each half's fragment
+    // reads for the next half go out spread over its MFMAs too, a few after
+    // each, instead of all ahead of them: a wave that finds the LDS queue
+    // full then holds back one read, not its whole half of MFMAs.  8192^3:
+    // 461 -> 445 us and 497 -> 478 us in interleaved runs on two boxes.
+    constexpr bool IOL = PIN && SPLIT && !XT && TM * TN >= 4;
+    i16x4 b0q[TN][4], b1q[TN][4];
+    uint32_t meta_none[TM];
     rd_meta(I0{}, meta[0]);
     rd_a(I0{}, I0{}, a0);
     rd_b(I0{}, I0{}, b0);
@@ -723,9 +782,36 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     wait_lds(a0);
     wait_lds(b0);
     if constexpr (KG) wait_lds(kv_cur);
+    auto body_spread = [&](auto ST, auto LD, int it) {
+      constexpr int st = decltype(ST)::value;
+      constexpr int nx = (st + 1) % NSTAGE;
+      using NR = std::integral_constant<int, 2 * TM + 4 * TN>;   // reads of a half: metadata, A, B pieces
+      // first half on (a0, b0); this stage's second-half A and B reads spread over it
+      mma_io(LD, I0{}, a0, b0, meta[st], QP0{}, QNQ{}, min(it + NSTAGE - 1, nk - 1), (st + NSTAGE - 1) % NSTAGE,
+             ST, I1{}, std::integral_constant<int, TM>{}, NR{}, meta_none, a1, b1q);
+      wait_lds(a1);
+      static_for<0, TN>([&](auto J) { wait_lds(b1q[decltype(J)::value]); });
+      assemble_b(b1q, b1);
+      wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(extra_wave);
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      // second half on (a1, b1); the next stage's first-half reads spread over it
+      mma_io(LD, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st,
+             std::integral_constant<int, nx>{}, I0{}, I0{}, NR{}, meta[nx], a0, b0q);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_lds(meta[nx]);
+      wait_lds(a0);
+      static_for<0, TN>([&](auto J) { wait_lds(b0q[decltype(J)::value]); });
+      assemble_b(b0q, b0);
+    };
     auto body = [&](auto ST, auto LD, int it) {
       constexpr int st = decltype(ST)::value;
       constexpr int nx = (st + 1) % NSTAGE;
+      if constexpr (IOL) {
+        body_spread(ST, LD, it);
+        return;
+      }
       rd_a(ST, I1{}, a1);
       rd_b(ST, I1{}, b1);
       if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
