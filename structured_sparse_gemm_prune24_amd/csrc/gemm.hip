@@ -765,13 +765,15 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     uint32_t meta[NSTAGE][TM];
     i16x8 a0[TM], a1[TM];
     i16x16 b0[TN], b1[TN];
-    // Where the reads fit between the MFMAs (the fenced plain-X tiles with
-    // spread loads and at least four MFMAs per half), each half's fragment
-    // reads for the next half go out spread over its MFMAs too, a few after
-    // each, instead of all ahead of them: a wave that finds the LDS queue
-    // full then holds back one read, not its whole half of MFMAs.  8192^3:
-    // 461 -> 445 us and 497 -> 478 us in interleaved runs on two boxes.
-    constexpr bool IOL = PIN && SPLIT && !XT && TM * TN >= 4;
+    // Where the reads fit between the MFMAs (X given K x N, spread loads, at
+    // least four MFMAs per half, and on the widest tile a bf16 output: with
+    // fp32 output it would spill), each half's fragment reads for the next
+    // half go out spread over its MFMAs too, a few after each, instead of all
+    // ahead of them: a wave that finds the LDS queue full then holds back one
+    // read, not its whole half of MFMAs.  8192^3: 461 -> 445 us and
+    // 497 -> 478 us in interleaved runs on two boxes; with bias + GELU
+    // 519 -> 499 us.
+    constexpr bool IOL = SPLIT && !XT && TM * TN >= 4 && (!(BM == 256 && BN == 256) || sizeof(OutT) == 2);
     i16x4 b0q[TN][4], b1q[TN][4];
     uint32_t meta_none[TM];
     rd_meta(I0{}, meta[0]);
