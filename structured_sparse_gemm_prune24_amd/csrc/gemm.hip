@@ -675,22 +675,62 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
           }
         }
       };
+      // one read of sub-step SS: A block r (r < TM), then the B pieces (two
+      // transposing reads per fragment of X given K x N, one 16-byte read of X
+      // given N x K)
+      constexpr int DBP = XT ? 1 : 2;
+      i16x4 bq[2][TN][2];
+      auto read_one = [&](auto SS, auto R) {
+        constexpr int ss = decltype(SS)::value, r = decltype(R)::value;
+        if constexpr (r < TM) {
+          a[ss & 1][r] = lds_read_b128<(r * DSTEPS + ss) * 1024>(a_off[st]);
+        } else if constexpr (XT) {
+          bb[ss & 1][r - TM] = lds_read_b128<(r - TM) * 32 * 128>(xt_off[st][ss]);
+        } else {
+          constexpr int j = (r - TM) / 2, piece = (r - TM) % 2;
+          bq[ss & 1][j][piece] = lds_read_tr<16 * ss * C::ROWB + piece * 4 * C::ROWB>(b_off[st][j]);
+        }
+      };
+      auto finish_b = [&](auto SS) {
+        constexpr int ss = decltype(SS)::value;
+        if constexpr (!XT) {
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            bb[ss & 1][j] = __builtin_shufflevector(bq[ss & 1][j][0], bq[ss & 1][j][1], 0, 1, 2, 3, 4, 5, 6, 7);
+        }
+      };
+      // the plain dense tiles spread the next sub-step's reads over the
+      // current one's MFMAs (the first three quarters of them), as the sparse
+      // loop does
+      constexpr bool DIOL = !DECOMP && TM * TN >= 4;
+      constexpr int NRD = TM + DBP * TN;
       read_step(std::integral_constant<int, 0>{});
       static_for<0, 4>([&](auto SS) {
         constexpr int ss = decltype(SS)::value;
         wait_lds(a[ss & 1]);
-        wait_lds(bb[ss & 1]);
-        if constexpr (ss + 1 < 4) read_step(std::integral_constant<int, ss + 1>{});
+        if constexpr (DIOL && !XT && ss > 0) {
+          static_for<0, TN>([&](auto J) { wait_lds(bq[ss & 1][decltype(J)::value]); });
+          finish_b(SS);
+        } else {
+          wait_lds(bb[ss & 1]);
+        }
+        if constexpr (!DIOL && ss + 1 < 4) read_step(std::integral_constant<int, ss + 1>{});
         constexpr int NMF = TM * TN * 4, STRIDE = NMF / NQ > 0 ? NMF / NQ : 1;
+        constexpr int SPREAD = TM * TN * 3 / 4 > 0 ? TM * TN * 3 / 4 : 1;
         static_for<0, TM * TN>([&](auto KC) {
           constexpr int k = decltype(KC)::value, i = k / TN, j = k % TN, kk = ss * TM * TN + k;
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a[ss & 1][i]),
                                                               __builtin_bit_cast(bf16x8, bb[ss & 1][j]),
                                                               acc[i][j], 0, 0, 0);
-          if constexpr (decltype(LD)::value && kk % STRIDE == 0 && kk / STRIDE < NQ) {
+          if constexpr (decltype(LD)::value && kk % STRIDE == 0 && kk / STRIDE < NQ)
             issue_one(std::integral_constant<int, kk / STRIDE>{}, g, stl);
-            __builtin_amdgcn_sched_barrier(0);
+          if constexpr (DIOL && ss + 1 < 4) {
+            constexpr int lo = k < SPREAD ? (NRD * k) / SPREAD : NRD;
+            constexpr int hi = k < SPREAD ? (NRD * (k + 1)) / SPREAD : NRD;
+            static_for<lo, hi>([&](auto R) { read_one(std::integral_constant<int, ss + 1>{}, R); });
           }
+          if constexpr ((decltype(LD)::value && kk % STRIDE == 0 && kk / STRIDE < NQ) || DIOL)
+            __builtin_amdgcn_sched_barrier(0);
         });
         if constexpr (decltype(LD)::value && ss == 3)
           static_for<(NMF + STRIDE - 1) / STRIDE < NQ ? (NMF + STRIDE - 1) / STRIDE : NQ, NQ>(
