@@ -813,7 +813,9 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     // read, not its whole half of MFMAs.  8192^3: 461 -> 445 us and
     // 497 -> 478 us in interleaved runs on two boxes; with bias + GELU
     // 519 -> 499 us.
-    constexpr bool IOL = SPLIT && !XT && TM * TN >= 4 && (!(BM == 256 && BN == 256) || sizeof(OutT) == 2);
+    // The gathered products take the same schedule with every load of a step
+    // after the barrier (their stage count or kept indices rule out the split).
+    constexpr bool IOL = (SPLIT || KG) && !XT && TM * TN >= 4 && (!(BM == 256 && BN == 256) || sizeof(OutT) == 2);
     i16x4 b0q[TN][4], b1q[TN][4];
     uint32_t meta_none[TM];
     rd_meta(I0{}, meta[0]);
@@ -839,6 +841,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       // second half on (a1, b1); the next stage's first-half reads spread over it
+      rd_kept(std::integral_constant<int, nx>{}, kv_nxt);
       mma_io(LD, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st,
              std::integral_constant<int, nx>{}, I0{}, I0{}, NR{}, meta[nx], a0, b0q);
       __builtin_amdgcn_sched_barrier(0);
@@ -846,6 +849,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       wait_lds(a0);
       static_for<0, TN>([&](auto J) { wait_lds(b0q[decltype(J)::value]); });
       assemble_b(b0q, b0);
+      if constexpr (KG) {
+        wait_lds(kv_nxt);
+#pragma unroll
+        for (int v = 0; v < KV; ++v) kv_cur[v] = kv_nxt[v];
+      }
     };
     auto body = [&](auto ST, auto LD, int it) {
       constexpr int st = decltype(ST)::value;
