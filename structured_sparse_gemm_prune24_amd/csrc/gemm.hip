@@ -3,11 +3,15 @@
 // dense bf16 baseline on v_mfma_f32_32x32x16_bf16.
 //
 // Data flow per block (BM x BN outputs, K consumed 64 logical columns at a time):
-//   * Both operands stream global -> LDS with direct-to-LDS loads
-//     (global_load_lds_dwordx4 / _dword: lane l writes its 16 / 4 bytes at the
-//     wave's LDS base + l * size) into a ring of LDS stages, NSTAGE-1 K steps
-//     ahead of the compute.  No register holds data in flight, so the
-//     accumulators own the register file.
+//   * Both operands stream global -> LDS with direct-to-LDS buffer loads
+//     (buffer_load_dwordx4 / _dword with the LDS flag: lane l writes its 16 / 4
+//     bytes at the wave's LDS base + l * size) into a ring of LDS stages,
+//     NSTAGE-1 K steps ahead of the compute.  No register holds data in
+//     flight, so the accumulators own the register file.
+//   * On the sparse tiles both the loads of a later step and the fragment
+//     reads of the next half-step go out spread over the MFMAs, a few after
+//     each, so that a wave stalled on a full memory or LDS queue holds back
+//     one instruction rather than its MFMAs.
 //   * W operand: the compressed values / metadata (or the packed dense W) are
 //     stored in MFMA operand order, so one K step of one 32-row block is a
 //     contiguous 1 KiB (values) or 256 B (metadata) run in memory, in LDS, and
