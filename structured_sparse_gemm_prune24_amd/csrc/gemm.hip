@@ -388,14 +388,22 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // stage's fragments, so the loads of step g + NSTAGE, issued one step
   // later, find their rows in registers and never wait on a global load.
   constexpr bool KG = C::K_BYTES > 0;
-  static_assert(!KG || (C::X_DMA % 4 == 0 && C::MG < C::LW), "kept indices: whole 16-byte reads, a free loading wave");
-  constexpr int KV = KG ? C::X_DMA / 4 : 1;
+  // When one X load covers one whole row (512-wide blocks) a load's row is
+  // the same for the whole wave: each lane then holds one of the wave's
+  // indices (lane j those of load j) and a load takes its row offset as a
+  // scalar (readlane), instead of every lane holding all of them.
+  constexpr bool KU = KG && X_ROWS_PER_LOAD == 1;
+  static_assert(!KG || ((KU ? C::X_DMA <= 64 : C::X_DMA % 4 == 0) && C::MG < C::LW),
+                "kept indices: one per lane or whole 16-byte reads, a free loading wave");
+  constexpr int KV = KU ? 1 : (KG ? C::X_DMA / 4 : 1);
+  using KvT = typename std::conditional<KU, int, i32x4>::type;
+  const uint32_t ldx2 = (uint32_t)(ldx * 2);   // X row pitch in bytes (< 4 GiB for a gather)
   constexpr int K_OFF = C::X_BYTES + C::A_BYTES + C::M_BYTES;
   const __amdgpu_buffer_rsrc_t k_rsrc = make_rsrc(kept_tile, (uint32_t)(KG ? Kc * 4 : 0));
   const uint32_t k_voff = (uint32_t)((lane / C::X_DMA) + (lane % C::X_DMA) * X_ROW_STEP) * 4;
   const bool kept_wave = KG && wave == C::MG;
   extra_wave = extra_wave || kept_wave;
-  i32x4 kv_cur[KV], kv_nxt[KV];
+  KvT kv_cur[KV], kv_nxt[KV];
 
   // Load q of a loading wave's list for K step g into stage st: X loads
   // first (q < X_DMA), then A (q < X_DMA + A_DMA), then the metadata load of
@@ -407,7 +415,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     uint8_t* stage = lds + st * C::STAGE;
     if constexpr (q < C::X_DMA) {
       constexpr int j = q;
-      if constexpr (GATHER) {
+      if constexpr (KU) {
+        int k = __builtin_amdgcn_readlane(kv_cur[0], j);
+        k = k < 0 ? 0 : (k >= args.Kx ? args.Kx - 1 : k);
+        dma16_to_lds(xg_rsrc, stage + (j * C::LW + wave) * 1024, x_voff, (uint32_t)k * ldx2);
+      } else if constexpr (GATHER) {
         int k;
         if constexpr (KG) k = kv_cur[j / 4][j % 4];
         else k = k_cur[j];
@@ -439,6 +451,25 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // all direct-to-LDS loads of K step g into stage st (loading waves only)
   auto issue_step = [&](int g, int st) {
     issue_range(std::integral_constant<int, 0>{}, std::integral_constant<int, NQ>{}, g, st);
+  };
+  // The loads of a step split by the 32-k half of the stage they fill, for
+  // the two-stage gathered tiles (one row per X load): half 0 takes X rows
+  // 0..31 (loads j < X_DMA / 2) and the metadata and kept indices (both read
+  // along with half 0), half 1 X rows 32..63.  A load j of wave w fills A
+  // block j * LW + w, which is row block (j * LW + w) / 2 at k half w % 2 (LW
+  // even), so the even waves' A loads go with half 0 and the odd waves' with
+  // half 1.  Load k of half HC; NH0 and NH1 loads per half.
+  constexpr int XH = C::X_DMA / 2, NH0 = XH + C::A_DMA + 1, NH1 = XH + C::A_DMA;
+  auto issue_h = [&](auto HC, auto KC, int g, int st) {
+    constexpr int hf = decltype(HC)::value, k = decltype(KC)::value;
+    if constexpr (k < XH) {
+      issue_one(std::integral_constant<int, hf * XH + k>{}, g, st);
+    } else if constexpr (k < XH + C::A_DMA) {
+      if ((wave & 1) == hf) issue_one(std::integral_constant<int, C::X_DMA + k - XH>{}, g, st);
+    } else {
+      static_assert(hf == 0 && k == XH + C::A_DMA, "the extra load goes with half 0");
+      issue_one(std::integral_constant<int, C::X_DMA + C::A_DMA>{}, g, st);
+    }
   };
 
   // ---- LDS read addresses, one set per stage ----
@@ -524,8 +555,11 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     static_for<0, TM>([&](auto I) { meta[decltype(I)::value] = lds_read_b32<decltype(I)::value * 256>(m_off[st]); });
   };
   // this lane's kept indices from stage ST (those of the step NSTAGE after the stage's own)
-  auto rd_kept = [&](auto ST, i32x4 (&kv)[KV]) {
-    if constexpr (KG) {
+  auto rd_kept = [&](auto ST, KvT (&kv)[KV]) {
+    if constexpr (KU) {
+      constexpr int st = decltype(ST)::value;
+      kv[0] = (int)lds_read_b32<0>(lds_base + st * C::STAGE + K_OFF + (uint32_t)(x_r0 * C::X_DMA + lane % C::X_DMA) * 4);
+    } else if constexpr (KG) {
       constexpr int st = decltype(ST)::value;
       const uint32_t ad = lds_base + st * C::STAGE + K_OFF + (uint32_t)x_r0 * C::X_DMA * 4;
       static_for<0, KV>([&](auto V) {
@@ -608,25 +642,31 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
   // MFMA k go load Q0 + k and the k-th share of the reads, all of them within
   // the first three quarters of the MFMAs so that the last ones still cover
   // the reads' latency.
-  auto mma_io = [&](auto LD, auto SS, const i16x8 (&a)[TM], const i16x16 (&bf)[TN], const uint32_t (&meta)[TM],
-                    auto Q0, auto Q1, int g, int stl, auto RST, auto RSS, auto R0, auto R1,
-                    uint32_t (&rmeta)[TM], i16x8 (&ra)[TM], i16x4 (&rbq)[TN][4]) {
-    constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value;
+  // HL: the loads are those of the step's list (HL < 0) or of its half HL
+  // (issue_h).
+  auto mma_io = [&](auto LD, auto HL, auto SS, const i16x8 (&a)[TM], const i16x16 (&bf)[TN],
+                    const uint32_t (&meta)[TM], auto Q0, auto Q1, int g, int stl, auto RST, auto RSS, auto R0,
+                    auto R1, uint32_t (&rmeta)[TM], i16x8 (&ra)[TM], i16x4 (&rbq)[TN][4]) {
+    constexpr int q0 = decltype(Q0)::value, q1 = decltype(Q1)::value, hl = decltype(HL)::value;
     constexpr int r0 = decltype(R0)::value, r1 = decltype(R1)::value, NR = r1 - r0;
     constexpr int SPREAD = TM * TN * 3 / 4 > 0 ? TM * TN * 3 / 4 : 1;
+    auto issue_q = [&](auto Q) {
+      if constexpr (hl < 0) issue_one(Q, g, stl);
+      else issue_h(std::integral_constant<int, hl>{}, Q, g, stl);
+    };
     static_for<0, TM * TN>([&](auto KC) {
       constexpr int k = decltype(KC)::value, i = k / TN, j = k % TN;
       acc[i][j] = __builtin_amdgcn_smfmac_f32_32x32x32_bf16(__builtin_bit_cast(bf16x8, a[i]),
                                                             __builtin_bit_cast(bf16x16, bf[j]), acc[i][j],
                                                             (int)meta[i], 0, decltype(SS)::value);
-      if constexpr (decltype(LD)::value && q0 + k < q1) issue_one(std::integral_constant<int, q0 + k>{}, g, stl);
+      if constexpr (decltype(LD)::value && q0 + k < q1) issue_q(std::integral_constant<int, q0 + k>{});
       constexpr int lo = k < SPREAD ? r0 + (NR * k) / SPREAD : r1;
       constexpr int hi = k < SPREAD ? r0 + (NR * (k + 1)) / SPREAD : r1;
       static_for<lo, hi>([&](auto R) { rd_one(RST, RSS, R, rmeta, ra, rbq); });
       __builtin_amdgcn_sched_barrier(0);
     });
     if constexpr (decltype(LD)::value)
-      static_for<q0 + TM * TN < q1 ? q0 + TM * TN : q1, q1>([&](auto Q) { issue_one(Q, g, stl); });
+      static_for<q0 + TM * TN < q1 ? q0 + TM * TN : q1, q1>([&](auto Q) { issue_q(Q); });
   };
   // LD (compile time) says whether this wave loads: a branch on it here,
   // between fragment reads and their wait, would let the compiler copy the
@@ -781,19 +821,57 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     constexpr bool PIN = !(BM == 256 && BN == 256) || (XM == X_KN && EPI == 0 && sizeof(OutT) == 2);
     using QP0 = std::integral_constant<int, P0>;
     using QNQ = std::integral_constant<int, NQ>;
+    // Where the reads fit between the MFMAs (X given K x N, spread loads, at
+    // least four MFMAs per half, and on the widest tile a bf16 output: with
+    // fp32 output it would spill), each half's fragment reads for the next
+    // half go out spread over its MFMAs too, a few after each, instead of all
+    // ahead of them: a wave that finds the LDS queue full then holds back one
+    // read, not its whole half of MFMAs.  8192^3: 461 -> 445 us and
+    // 497 -> 478 us in interleaved runs on two boxes; with bias + GELU
+    // 519 -> 499 us.
+    // The gathered products take the same schedule with every load of a step
+    // after a barrier (their stage count or kept indices rule out the split).
+    constexpr bool IOL = (SPLIT || KG) && !XT && TM * TN >= 4 && (!(BM == 256 && BN == 256) || sizeof(OutT) == 2);
+    // Half-stage refill (HS), for the two-stage gathered tiles: a second
+    // barrier at the end of each step, after which every wave is done with
+    // the first half of stage it (read during the previous step) and the
+    // metadata and kept indices read with it.  The loads of step it+2 for that
+    // half go out with the first-half multiplies of step it, those for the
+    // second half after the middle barrier as before, so each has a step and
+    // a half to land instead of one: half 0 of step it+2 is read after the
+    // middle barrier of step it+1, half 1 after its end barrier.  Each barrier
+    // waits for the half issued one and a half steps earlier, with the next
+    // two halves (one step's loads) still in flight.
+    constexpr bool HS = KG && NSTAGE == 2 && IOL;
+    static_assert(!HS || (C::LW % 2 == 0 && ASTEPS == 2 && X_ROWS_PER_LOAD == 1 && XH * X_ROW_STEP == BK / 2),
+                  "half-stage refill: A halves by wave parity, X loads j < X_DMA / 2 cover k 0..31");
 #pragma unroll
     for (int g = 0; g < NSTAGE; ++g) {
       if constexpr (KG) {
         // the prologue's own steps take their indices straight from the list
-        if (loader)
+        if (loader) {
+          if constexpr (KU) {
+            kv_cur[0] = kept_tile[(int64_t)min(g, nk - 1) * BK + x_r0 + (lane % C::X_DMA) * X_ROW_STEP];
+          } else {
 #pragma unroll
-          for (int j = 0; j < C::X_DMA; ++j)
-            kv_cur[j / 4][j % 4] = kept_tile[(int64_t)min(g, nk - 1) * BK + x_r0 + j * X_ROW_STEP];
+            for (int j = 0; j < C::X_DMA; ++j)
+              kv_cur[j / 4][j % 4] = kept_tile[(int64_t)min(g, nk - 1) * BK + x_r0 + j * X_ROW_STEP];
+          }
+        }
       } else {
         load_kept(min(g, nk - 1), k_cur);
       }
-      if (SPLIT && g == NSTAGE - 1) issue_range(I0{}, QP0{}, min(g, nk - 1), g);
-      else issue_step(min(g, nk - 1), g);
+      if (SPLIT && g == NSTAGE - 1) {
+        issue_range(I0{}, QP0{}, min(g, nk - 1), g);
+      } else if constexpr (HS) {
+        // half 0 then half 1, the order the loop's counts assume
+        if (loader) {
+          static_for<0, NH0>([&](auto Q) { issue_h(I0{}, Q, min(g, nk - 1), g); });
+          static_for<0, NH1>([&](auto Q) { issue_h(I1{}, Q, min(g, nk - 1), g); });
+        }
+      } else {
+        issue_step(min(g, nk - 1), g);
+      }
     }
     if constexpr (!KG) load_kept(min(NSTAGE, nk - 1), k_cur);
     constexpr int PRO_M = SPLIT ? (NSTAGE - 2) * C::DMA_M + P0 : (NSTAGE - 1) * C::DMA_M;
@@ -809,54 +887,72 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
     uint32_t meta[NSTAGE][TM];
     i16x8 a0[TM], a1[TM];
     i16x16 b0[TN], b1[TN];
-    // Where the reads fit between the MFMAs (X given K x N, spread loads, at
-    // least four MFMAs per half, and on the widest tile a bf16 output: with
-    // fp32 output it would spill), each half's fragment reads for the next
-    // half go out spread over its MFMAs too, a few after each, instead of all
-    // ahead of them: a wave that finds the LDS queue full then holds back one
-    // read, not its whole half of MFMAs.  8192^3: 461 -> 445 us and
-    // 497 -> 478 us in interleaved runs on two boxes; with bias + GELU
-    // 519 -> 499 us.
-    // The gathered products take the same schedule with every load of a step
-    // after the barrier (their stage count or kept indices rule out the split).
-    constexpr bool IOL = (SPLIT || KG) && !XT && TM * TN >= 4 && (!(BM == 256 && BN == 256) || sizeof(OutT) == 2);
     i16x4 b0q[TN][4], b1q[TN][4];
     uint32_t meta_none[TM];
     rd_meta(I0{}, meta[0]);
     rd_a(I0{}, I0{}, a0);
     rd_b(I0{}, I0{}, b0);
-    rd_kept(I0{}, kv_cur);
     wait_lds(meta[0]);
     wait_lds(a0);
     wait_lds(b0);
-    if constexpr (KG) wait_lds(kv_cur);
+    // only the loading waves read kept indices (theirs are the stage's 64)
+    if constexpr (KG) {
+      if (loader) {
+        rd_kept(I0{}, kv_cur);
+        wait_lds(kv_cur);
+      }
+    }
+    if constexpr (HS) {
+      // the end barrier of "step -1": every wave is done with half 0 of stage 0
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+    }
+    // wait at a barrier: with HS one step's loads stay in flight, else NSTAGE - 2 steps'
+    constexpr int BW_M = HS ? C::DMA_M : (NSTAGE - 2) * C::DMA_M;
+    constexpr int BW_O = HS ? C::DMA_O : (NSTAGE - 2) * C::DMA_O;
+    using HL0 = std::integral_constant<int, HS ? 0 : -1>;
+    using HL1 = std::integral_constant<int, HS ? 1 : -1>;
     auto body_spread = [&](auto ST, auto LD, int it) {
       constexpr int st = decltype(ST)::value;
       constexpr int nx = (st + 1) % NSTAGE;
       using NR = std::integral_constant<int, 2 * TM + 4 * TN>;   // reads of a half: metadata, A, B pieces
-      // first half on (a0, b0); this stage's second-half A and B reads spread over it
-      mma_io(LD, I0{}, a0, b0, meta[st], QP0{}, QNQ{}, min(it + NSTAGE - 1, nk - 1), (st + NSTAGE - 1) % NSTAGE,
-             ST, I1{}, std::integral_constant<int, TM>{}, NR{}, meta_none, a1, b1q);
+      // first half on (a0, b0); this stage's second-half A and B reads spread
+      // over it, and with HS the loads of half 0 of step it+2 into this stage
+      if constexpr (HS)
+        mma_io(LD, HL0{}, I0{}, a0, b0, meta[st], I0{}, std::integral_constant<int, NH0>{},
+               min(it + NSTAGE, nk - 1), st, ST, I1{}, std::integral_constant<int, TM>{}, NR{}, meta_none, a1, b1q);
+      else
+        mma_io(LD, HL0{}, I0{}, a0, b0, meta[st], QP0{}, QNQ{}, min(it + NSTAGE - 1, nk - 1),
+               (st + NSTAGE - 1) % NSTAGE, ST, I1{}, std::integral_constant<int, TM>{}, NR{}, meta_none, a1, b1q);
       wait_lds(a1);
       static_for<0, TN>([&](auto J) { wait_lds(b1q[decltype(J)::value]); });
       assemble_b(b1q, b1);
-      wait_vmcnt_by_wave<(NSTAGE - 2) * C::DMA_M, (NSTAGE - 2) * C::DMA_O>(extra_wave);
+      wait_vmcnt_by_wave<BW_M, BW_O>(extra_wave);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       // second half on (a1, b1); the next stage's first-half reads spread over it
-      rd_kept(std::integral_constant<int, nx>{}, kv_nxt);
-      mma_io(LD, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st,
-             std::integral_constant<int, nx>{}, I0{}, I0{}, NR{}, meta[nx], a0, b0q);
+      if constexpr (decltype(LD)::value) rd_kept(std::integral_constant<int, nx>{}, kv_nxt);
+      if constexpr (HS)
+        mma_io(LD, HL1{}, I1{}, a1, b1, meta[st], I0{}, std::integral_constant<int, NH1>{},
+               min(it + NSTAGE, nk - 1), st, std::integral_constant<int, nx>{}, I0{}, I0{}, NR{}, meta[nx], a0, b0q);
+      else
+        mma_io(LD, HL1{}, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st,
+               std::integral_constant<int, nx>{}, I0{}, I0{}, NR{}, meta[nx], a0, b0q);
       __builtin_amdgcn_sched_barrier(0);
       wait_lds(meta[nx]);
       wait_lds(a0);
       static_for<0, TN>([&](auto J) { wait_lds(b0q[decltype(J)::value]); });
       assemble_b(b0q, b0);
-      if constexpr (KG) {
+      if constexpr (KG && decltype(LD)::value) {
         wait_lds(kv_nxt);
 #pragma unroll
         for (int v = 0; v < KV; ++v) kv_cur[v] = kv_nxt[v];
+      }
+      if constexpr (HS) {
+        wait_vmcnt_by_wave<BW_M, BW_O>(extra_wave);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
       }
     };
     auto body = [&](auto ST, auto LD, int it) {
@@ -889,7 +985,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       rd_meta(std::integral_constant<int, nx>{}, meta[nx]);
       rd_a(std::integral_constant<int, nx>{}, I0{}, a0);
       rd_b(std::integral_constant<int, nx>{}, I0{}, b0);
-      rd_kept(std::integral_constant<int, nx>{}, kv_nxt);
+      if constexpr (decltype(LD)::value) rd_kept(std::integral_constant<int, nx>{}, kv_nxt);
       if constexpr (PIN) __builtin_amdgcn_sched_barrier(0);
       if constexpr (SPLIT)
         mma_sparse_loads(LD, I1{}, a1, b1, meta[st], I0{}, QP0{}, min(it + NSTAGE, nk - 1), st);
@@ -899,7 +995,7 @@ __global__ __launch_bounds__(WGM * WGN * 64) void k_gemm(const GemmArgs args) {
       wait_lds(meta[nx]);
       wait_lds(a0);
       wait_lds(b0);
-      if constexpr (KG) {
+      if constexpr (KG && decltype(LD)::value) {
         wait_lds(kv_nxt);
 #pragma unroll
         for (int v = 0; v < KV; ++v) kv_cur[v] = kv_nxt[v];

@@ -106,11 +106,12 @@ def test_c5_full():
 
 
 @pytest.mark.parametrize("M,K,N,keep", [(256, 256, 200, 128), (384, 512, 1000, 256), (300, 256, 72, 128),
-                                         (256, 256, 1096, 128)])
+                                         (256, 256, 1096, 128), (384, 1024, 1000, 448), (256, 256, 520, 64)])
 @pytest.mark.parametrize("tile", ["128x256", "128x512"])
 def test_spmm_tvw_small(M, K, N, keep, tile, monkeypatch):
     """Both block widths of the fixed-keep gathered product (the width is forced; by default
-    only grids of at least 160 wide blocks take 128 x 512), ragged N included."""
+    only grids of at least 160 wide blocks take 128 x 512), ragged N included, with one K
+    step (keep 64) and an odd number of them (keep 448: seven)."""
     need_gpu()
     monkeypatch.setenv("P24_GATHER_TILE", tile)
     print(f"[tvw] spmm M={M} K={K} N={N} keep={keep} tile={tile}", flush=True)
