@@ -1361,8 +1361,8 @@ extern "C" P24_API p24_status spmm24(const void* values, const void* meta, int32
 }
 
 // Gathered products (TVW on the sparse MFMA, TW alone on the dense MFMA): one
-// block row = one 128-row slice of a tile, 8 waves (2 x 4); the fused variants
-// add the bias + activation epilogue.
+// block row = one 128-row slice of a tile, 8 waves; the fused variants add
+// the bias + activation epilogue.
 //
 // Block width.  With one keep count for every tile the block is 128 x 512 when
 // that grid still gives at least 160 blocks (five eighths of the CUs), else
@@ -1383,11 +1383,16 @@ static bool wide_gather(int64_t M, int64_t N) {
   return ((M + 127) / 128) * ((N + 511) / 512) >= 160;
 }
 
+// Wave layout: 2 x 4 waves of 64 x (BN / 4), except the 512-wide sparse block,
+// which takes 1 x 8 waves of 128 x 64 (the 8192^3 product's wave tile: a
+// fifth fewer LDS fragment bytes per MFMA than 64 x 128); 4096^3 TVW keep
+// 2048 measured 46.1 -> 45.2 us.
 template <int AM, int XM, int BN>
 static p24_status launch_gather_bn(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
-  if (!fused) return launch_cfg<128, BN, 2, 4, AM, XM, 0>(a, y_dtype, st);
-  if (act == P24_ACT_GELU) return launch_cfg<128, BN, 2, 4, AM, XM, 2>(a, y_dtype, st);
-  return launch_cfg<128, BN, 2, 4, AM, XM, 1>(a, y_dtype, st);
+  constexpr int WM = BN == 512 && AM == A_SPARSE ? 1 : 2, WN = 8 / WM;
+  if (!fused) return launch_cfg<128, BN, WM, WN, AM, XM, 0>(a, y_dtype, st);
+  if (act == P24_ACT_GELU) return launch_cfg<128, BN, WM, WN, AM, XM, 2>(a, y_dtype, st);
+  return launch_cfg<128, BN, WM, WN, AM, XM, 1>(a, y_dtype, st);
 }
 
 template <int AM, int XM>
