@@ -1383,13 +1383,15 @@ static bool wide_gather(int64_t M, int64_t N) {
   return ((M + 127) / 128) * ((N + 511) / 512) >= 160;
 }
 
-// Wave layout: 2 x 4 waves of 64 x (BN / 4), except the 512-wide sparse block,
-// which takes 1 x 8 waves of 128 x 64 (the 8192^3 product's wave tile: a
-// fifth fewer LDS fragment bytes per MFMA than 64 x 128); 4096^3 TVW keep
-// 2048 measured 46.1 -> 45.2 us.
+// Wave layout: the sparse blocks take 1 x 8 waves of 128 x (BN / 8).  At 512
+// wide that is the 8192^3 product's wave tile, with a fifth fewer LDS
+// fragment bytes per MFMA than 2 x 4 waves of 64 x 128 (4096^3 TVW keep 2048:
+// 46.1 -> 45.2 us); at 256 wide the bytes are equal but half of the B reads
+// become A reads, which do not transpose (per-tile keep: 55.6 -> 54.4 us).
+// The dense (TW) blocks keep 2 x 4.
 template <int AM, int XM, int BN>
 static p24_status launch_gather_bn(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
-  constexpr int WM = BN == 512 && AM == A_SPARSE ? 1 : 2, WN = 8 / WM;
+  constexpr int WM = AM == A_SPARSE ? 1 : 2, WN = 8 / WM;
   if (!fused) return launch_cfg<128, BN, WM, WN, AM, XM, 0>(a, y_dtype, st);
   if (act == P24_ACT_GELU) return launch_cfg<128, BN, WM, WN, AM, XM, 2>(a, y_dtype, st);
   return launch_cfg<128, BN, WM, WN, AM, XM, 1>(a, y_dtype, st);
