@@ -545,25 +545,34 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
 // ascending, and the top total_keep are taken; tile t keeps its number of
 // those rounded to a multiple of 64 (halves up), clamped to [64, K].
 //   * the global cut: the same MSB-first radix select as above, over all T*K
-//     keys; one launch per 8-bit digit, each block adds its LDS histogram to
-//     a global one and the last block to finish picks the digit;
+//     keys, with 11-bit digits; one launch per digit (six), each block adds
+//     its LDS histogram to a global one and the last block to finish picks
+//     the digit;
 //   * per tile: keys above the cut and keys equal to it; the equal keys are
 //     taken in flat order, so tile t gets min(eq_t, need - (eq of tiles < t));
 //   * keep counts, their running sum (the tiles' column offsets in the
 //     concatenated storage) and the order of the tiles by count, heaviest first.
 // --------------------------------------------------------------------------
-struct VarSelect {
+template <int BINS>
+struct VarSel {
   uint64_t prefix;        // the cut's digits found so far
   int64_t need;           // rank of the cut among the keys matching the prefix
   uint32_t ticket;        // blocks done in the current pass
   uint32_t pad;
-  uint32_t hist[256];     // digit histogram of the current pass
+  uint32_t hist[BINS];    // digit histogram of the current pass
 };
+// 8-bit digits (the unstructured plan's four passes over 32-bit keys) and
+// 11-bit digits (the per-tile-keep cut over 64-bit scores: six passes of
+// 11, 11, 11, 11, 11 and 9 bits instead of eight of 8; each pass is one launch)
+using VarSelect = VarSel<256>;
+constexpr int VAR_DIGIT = 11;
+using VarSelectW = VarSel<1 << VAR_DIGIT>;
 constexpr int VAR_THREADS = 256;
 constexpr int64_t VAR_STEP = 64;
 
-__global__ __launch_bounds__(VAR_THREADS) void k_var_init(VarSelect* __restrict__ vs, int64_t total_keep) {
-  vs->hist[threadIdx.x] = 0u;
+template <int BINS>
+__global__ __launch_bounds__(VAR_THREADS) void k_var_init(VarSel<BINS>* __restrict__ vs, int64_t total_keep) {
+  for (int i = threadIdx.x; i < BINS; i += VAR_THREADS) vs->hist[i] = 0u;
   if (threadIdx.x == 0) {
     vs->prefix = 0ull;
     vs->need = total_keep;
@@ -572,63 +581,96 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_init(VarSelect* __restrict_
   }
 }
 
+// One digit pass of the global cut: digit (x >> shift) & (2^width - 1) of the
+// keys whose higher digits equal the prefix found so far.
 __global__ __launch_bounds__(VAR_THREADS) void k_var_radix(const uint64_t* __restrict__ keys, int64_t n, int shift,
-                                                           VarSelect* __restrict__ vs) {
-  __shared__ uint32_t h[256];
+                                                           int width, VarSelectW* __restrict__ vs) {
+  constexpr int BINS = 1 << VAR_DIGIT, PER = BINS / VAR_THREADS, NW = VAR_THREADS / 64;
+  __shared__ uint32_t h[BINS];
+  __shared__ uint32_t wsum[NW];
   __shared__ uint32_t last;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t prefix = vs->prefix;
   const int64_t need = vs->need;
-  h[tid] = 0u;
+  for (int i = tid; i < BINS; i += VAR_THREADS) h[i] = 0u;
   __syncthreads();
-  const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+  const uint64_t hi_mask = shift + width >= 64 ? 0ull : (~0ull << (shift + width));
+  const uint32_t dmask = (1u << width) - 1u;
   // as in the per-tile select: a wave whose matching keys share one digit adds
   // them with one atomic
   for (int64_t i0 = (int64_t)blockIdx.x * VAR_THREADS; i0 < n; i0 += (int64_t)gridDim.x * VAR_THREADS) {
     const int64_t i = i0 + tid;
     const uint64_t x = i < n ? keys[i] : 0ull;
     const bool match = i < n && (x & hi_mask) == prefix;
-    const uint32_t d = (uint32_t)(x >> shift) & 255u;
+    const uint32_t d = (uint32_t)(x >> shift) & dmask;
     const uint64_t mm = __ballot(match);
     if (!mm) continue;                                      // wave-uniform
     const int l0 = __builtin_ffsll((long long)mm) - 1;
     const uint32_t d0 = (uint32_t)__shfl((int)d, l0);
     if (__ballot(match && d == d0) == mm) {
-      if ((tid & 63) == l0) atomicAdd(&h[d0], (uint32_t)__builtin_popcountll(mm));
+      if (lane == l0) atomicAdd(&h[d0], (uint32_t)__builtin_popcountll(mm));
     } else if (match) {
       atomicAdd(&h[d], 1u);
     }
   }
   __syncthreads();
-  if (h[tid]) atomicAdd(&vs->hist[tid], h[tid]);
+  for (int i = tid; i < BINS; i += VAR_THREADS)
+    if (h[i]) atomicAdd(&vs->hist[i], h[i]);
   __threadfence();
   __syncthreads();
   if (tid == 0) last = atomicAdd(&vs->ticket, 1u) == gridDim.x - 1 ? 1u : 0u;
   __syncthreads();
   if (!last) return;
-  // the last block sees every block's histogram: pick the digit, then clear
-  // the histogram and the ticket for the next pass
+  // The last block sees every block's histogram.  Thread tid holds the
+  // digits [PER tid, PER tid + PER); a suffix sum over the threads (higher
+  // digits first) gives the count above each thread's digits, and the one
+  // thread whose digits hold the rank `need` walks them from the highest.
+  // Then the histogram and the ticket are cleared for the next pass.
   __threadfence();
-  if (tid < 64) {
-    uint32_t hb[4];
+  uint32_t hb[PER];
+  uint32_t own = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      hb[i] = __hip_atomic_load(&vs->hist[4 * tid + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    int d;
-    int64_t rest;
-    if (find_cut(hb, need, tid, &d, &rest)) {
-      vs->prefix = prefix | ((uint64_t)d << shift);
-      vs->need = rest;
+  for (int i = 0; i < PER; ++i) {
+    hb[i] = __hip_atomic_load(&vs->hist[PER * tid + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    own += hb[i];
+  }
+  uint32_t incl = own;                  // inclusive suffix sum over the wave's lanes lane .. 63
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint32_t o = __shfl_down(incl, d);
+    if (lane + d < 64) incl += o;
+  }
+  if (lane == 0) wsum[wave] = incl;     // the wave's total
+  __syncthreads();
+  int64_t above = (int64_t)incl - own;
+  for (int w = wave + 1; w < NW; ++w) above += wsum[w];
+  if (above < need && above + own >= need) {
+    int64_t a = above;
+    int dsel = PER * tid;
+    bool found = false;
+#pragma unroll
+    for (int i = PER - 1; i >= 0; --i) {
+      if (!found) {
+        if (a + hb[i] >= need) {
+          dsel = PER * tid + i;
+          found = true;
+        } else {
+          a += hb[i];
+        }
+      }
     }
+    vs->prefix = prefix | ((uint64_t)dsel << shift);
+    vs->need = need - a;
   }
   __syncthreads();
-  vs->hist[tid] = 0u;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) vs->hist[PER * tid + i] = 0u;
   if (tid == 0) vs->ticket = 0u;
 }
 
 // keys of tile t above the cut and equal to it; one block per tile
 __global__ __launch_bounds__(VAR_THREADS) void k_var_tile_counts(const uint64_t* __restrict__ keys, int64_t K,
-                                                                 const VarSelect* __restrict__ vs,
+                                                                 const VarSelectW* __restrict__ vs,
                                                                  int32_t* __restrict__ gt, int32_t* __restrict__ eq) {
   __shared__ uint32_t sg[VAR_THREADS / 64], se[VAR_THREADS / 64];
   const int64_t t = blockIdx.x;
@@ -662,7 +704,7 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_tile_counts(const uint64_t*
 }
 
 // keep counts and their offsets; one block of SEL_THREADS
-__global__ __launch_bounds__(SEL_THREADS) void k_var_plan(int64_t T, int64_t K, const VarSelect* __restrict__ vs,
+__global__ __launch_bounds__(SEL_THREADS) void k_var_plan(int64_t T, int64_t K, const VarSelectW* __restrict__ vs,
                                                           const int32_t* __restrict__ gt,
                                                           const int32_t* __restrict__ eq,
                                                           int64_t* __restrict__ offsets) {
@@ -1188,7 +1230,7 @@ extern "C" P24_API size_t tvw_var_workspace_bytes(int64_t M, int64_t K) {
   if (M < 0 || K <= 0) return 0;
   const int64_t T_ = var_tiles(M);
   const size_t scores = ((size_t)T_ * (size_t)K * sizeof(double) + 255) & ~(size_t)255;
-  const size_t sel = (sizeof(VarSelect) + 255) & ~(size_t)255;
+  const size_t sel = (sizeof(VarSelectW) + 255) & ~(size_t)255;
   return scores + sel + 2 * (size_t)T_ * sizeof(int32_t);
 }
 
@@ -1201,21 +1243,25 @@ static p24_status launch_var_plan(const void* W, int64_t M, int64_t K, int64_t l
   uint8_t* ws = (uint8_t*)workspace;
   double* scores = (double*)ws;
   ws += ((size_t)T_ * (size_t)K * sizeof(double) + 255) & ~(size_t)255;
-  VarSelect* vs = (VarSelect*)ws;
-  ws += (sizeof(VarSelect) + 255) & ~(size_t)255;
+  VarSelectW* vs = (VarSelectW*)ws;
+  ws += (sizeof(VarSelectW) + 255) & ~(size_t)255;
   int32_t* gt = (int32_t*)ws;
   int32_t* eq = gt + T_;
   const int64_t n = T_ * K;
   launch_tvw_scores((const float*)W, ldw, M, K, 128, scores, st);
-  hipLaunchKernelGGL(k_var_init, dim3(1), dim3(VAR_THREADS), 0, st, vs, total_keep);
+  hipLaunchKernelGGL(k_var_init<1 << VAR_DIGIT>, dim3(1), dim3(VAR_THREADS), 0, st, vs, total_keep);
   const int64_t per_block = (int64_t)VAR_THREADS * 8;
   const unsigned radix_blocks = (unsigned)std::min<int64_t>((n + per_block - 1) / per_block, 1024);
-  for (int shift = 56; shift >= 0; shift -= 8)
+  // digits of 11 bits from the top (bits 53..63, 42..52, ...), the last one
+  // the 9 bits left
+  for (int top = 64; top > 0; top -= VAR_DIGIT) {
+    const int width = top < VAR_DIGIT ? top : VAR_DIGIT;
     hipLaunchKernelGGL(k_var_radix, dim3(radix_blocks), dim3(VAR_THREADS), 0, st, (const uint64_t*)scores, n,
-                       shift, vs);
+                       top - width, width, vs);
+  }
   hipLaunchKernelGGL(k_var_tile_counts, dim3((unsigned)T_), dim3(VAR_THREADS), 0, st, (const uint64_t*)scores, K,
-                     (const VarSelect*)vs, gt, eq);
-  hipLaunchKernelGGL(k_var_plan, dim3(1), dim3(SEL_THREADS), 0, st, T_, K, (const VarSelect*)vs,
+                     (const VarSelectW*)vs, gt, eq);
+  hipLaunchKernelGGL(k_var_plan, dim3(1), dim3(SEL_THREADS), 0, st, T_, K, (const VarSelectW*)vs,
                      (const int32_t*)gt, (const int32_t*)eq, offsets);
   hipLaunchKernelGGL(k_var_order, dim3(grid1d(T_, VAR_THREADS)), dim3(VAR_THREADS), 0, st,
                      (const int64_t*)offsets, T_, order);
@@ -1359,7 +1405,7 @@ extern "C" P24_API p24_status ew_compress(const void* W, int32_t w_dtype, int64_
   ws += (sizeof(VarSelect) + 255) & ~(size_t)255;
   int32_t* gt = (int32_t*)ws;
   int32_t* eq = gt + M;
-  hipLaunchKernelGGL(k_var_init, dim3(1), dim3(VAR_THREADS), 0, st, vs, keep_total);
+  hipLaunchKernelGGL(k_var_init<256>, dim3(1), dim3(VAR_THREADS), 0, st, vs, keep_total);
   const int64_t n = M * K, per_block = (int64_t)VAR_THREADS * 16;
   const unsigned blocks = (unsigned)std::min<int64_t>((n + per_block - 1) / per_block, 2048);
   for (int shift = 24; shift >= 0; shift -= 8)

@@ -176,9 +176,10 @@ def test_tvw_validation(L):
 
 
 def test_tvw_var_validation(L):
-    # T = ceil(M / 128) tiles: scores (T*K fp64, 256 B rounded) + selection state + 2 counts per tile
-    assert L.tvw_var_workspace_bytes(4096, 4096) == 32 * 4096 * 8 + 1280 + 2 * 32 * 4
-    assert L.tvw_var_workspace_bytes(300, 64) == 3 * 64 * 8 + 1280 + 2 * 3 * 4   # 1536 B of scores
+    # T = ceil(M / 128) tiles: scores (T*K fp64, 256 B rounded) + selection state (a 2048-bin
+    # histogram and the cut, 8216 B, rounded to 8448) + 2 counts per tile
+    assert L.tvw_var_workspace_bytes(4096, 4096) == 32 * 4096 * 8 + 8448 + 2 * 32 * 4
+    assert L.tvw_var_workspace_bytes(300, 64) == 3 * 64 * 8 + 8448 + 2 * 3 * 4   # 1536 B of scores
     f = L.tvw_var_compress
     base = dict(W=FAKE, wd=0, M=256, K=256, ldw=256, total=256, off=FAKE, order=FAKE, kept=FAKE, v=FAKE, m=FAKE,
                 ws=FAKE, wsb=1 << 30)
