@@ -7,7 +7,9 @@
 //     (buffer_load_dwordx4 / _dword with the LDS flag: lane l writes its 16 / 4
 //     bytes at the wave's LDS base + l * size) into a ring of LDS stages,
 //     NSTAGE-1 K steps ahead of the compute.  No register holds data in
-//     flight, so the accumulators own the register file.
+//     flight, so the accumulators own the register file.  The two-stage
+//     gathered tiles refill each stage by 32-k halves, each half as soon as
+//     every wave is done with it, which gives a load a step and a half.
 //   * On the sparse tiles both the loads of a later step and the fragment
 //     reads of the next half-step go out spread over the MFMAs, a few after
 //     each, so that a wave stalled on a full memory or LDS queue holds back
