@@ -126,13 +126,15 @@ constexpr int CMP_META_PITCH = 65;
 // offsets[t] of the concatenation, its compacted K is offsets[t+1] - offsets[t]).
 enum GatherMode { G_NONE = 0, G_FIXED = 1, G_VAR = 2 };
 
+// rq: waves per (row block, chunk); each takes 32 / rq of the block's rows
+// (1, or 4 when there are too few (row block, chunk) pairs to fill the chip).
 template <typename T, int GM, bool WB = false>
 __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, int64_t ldw, int64_t M,
                                                                     int64_t K, uint16_t* __restrict__ dvals,
                                                                     uint32_t* __restrict__ dmeta,
                                                                     const int32_t* __restrict__ kept,
                                                                     const int64_t* __restrict__ offsets,
-                                                                    int64_t tile_m, int64_t kmax, T* Wout) {
+                                                                    int64_t tile_m, int64_t kmax, T* Wout, int rq) {
   constexpr bool GATHER = GM != G_NONE;
   static_assert(!WB || GM == G_NONE, "re-prune in place works on the whole matrix");
   __shared__ uint32_t sv[CMP_WAVES][8 * CMP_BLK_WORDS];
@@ -140,9 +142,10 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, 
   const int64_t RB = device_row_blocks(M);
   const int64_t NC = (K + 255) / 256;    // K: the widest compacted row
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t wid = (int64_t)blockIdx.x * CMP_WAVES + wv;
-  if (wid >= RB * NC) return;            // wave-uniform
-  const int64_t rb = wid / NC, c = wid % NC;
+  const int64_t wq = (int64_t)blockIdx.x * CMP_WAVES + wv;
+  if (wq >= RB * NC * rq) return;        // wave-uniform
+  const int64_t wid = wq / rq, rb = wid / NC, c = wid % NC;
+  const int r_begin = (int)(wq % rq) * (32 / rq), r_end = r_begin + 32 / rq;
   int64_t Kc = K, rbl = rb;              // compacted K, row block inside the storage
   const int32_t* kept_tile = nullptr;
   if constexpr (GM == G_VAR) {
@@ -179,7 +182,7 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, 
       kcol[i] = k < 0 ? 0 : (k >= kmax ? kmax - 1 : k);
     }
   }
-  for (int r0 = 0; r0 < 32; r0 += 8) {
+  for (int r0 = r_begin; r0 < r_end; r0 += 8) {
 #pragma unroll
     for (int rr = 0; rr < 8; ++rr) {
       const int r = r0 + rr;
@@ -224,8 +227,10 @@ __global__ __launch_bounds__(64 * CMP_WAVES) void k_compress_device(const T* W, 
       }
     }
   }
+  // the metadata words of this wave's rows: lanes r and r + 32 for its rows r
   uint32_t* mout = dmeta + (((rbl >> 2) * T_ + 4 * c) * 4 + (rbl & 3)) * 64;
-  for (int j = 0; j < ns / 2; ++j) __builtin_nontemporal_store(mst[j * CMP_META_PITCH + lane], &mout[j * 256 + lane]);
+  if ((lane & 31) >= r_begin && (lane & 31) < r_end)
+    for (int j = 0; j < ns / 2; ++j) __builtin_nontemporal_store(mst[j * CMP_META_PITCH + lane], &mout[j * 256 + lane]);
 }
 
 // --------------------------------------------------------------------------
@@ -1035,15 +1040,20 @@ static p24_status launch_compress(const void* W, int32_t w_dtype, int64_t M, int
                          (const uint16_t*)W, ldw, M, K, (uint16_t*)values, (uint32_t*)meta, kept, tile_m, kmax,
                          WB ? (uint16_t*)W : nullptr);
   } else {
-    const int64_t waves = device_row_blocks(M) * ((K + 255) / 256);
-    const dim3 grid(grid1d(waves, CMP_WAVES)), block(64 * CMP_WAVES);
+    // A (row block, 256-column chunk) pair is one wave, or four of 8 rows
+    // each when the pairs would give fewer than 16 waves per CU (the gathered
+    // compression of 4096 x 4096, keep 2048: 1024 pairs).
+    const int64_t pairs = device_row_blocks(M) * ((K + 255) / 256);
+    const int rq = pairs < 4096 ? 4 : 1;
+    const dim3 grid(grid1d(pairs * rq, CMP_WAVES)), block(64 * CMP_WAVES);
     if (w_dtype == P24_F32)
       hipLaunchKernelGGL((k_compress_device<float, GM, WB>), grid, block, 0, st, (const float*)W, ldw, M, K,
-                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax, WB ? (float*)W : nullptr);
+                         (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax, WB ? (float*)W : nullptr,
+                         rq);
     else
       hipLaunchKernelGGL((k_compress_device<uint16_t, GM, WB>), grid, block, 0, st, (const uint16_t*)W, ldw, M, K,
                          (uint16_t*)values, (uint32_t*)meta, kept, offsets, tile_m, kmax,
-                         WB ? (uint16_t*)W : nullptr);
+                         WB ? (uint16_t*)W : nullptr, rq);
   }
   return launch_status();
 }
