@@ -982,8 +982,11 @@ static inline unsigned grid1d(int64_t n, int threads) { return (unsigned)((n + t
 static void launch_tvw_scores(const float* W, int64_t ldw, int64_t M, int64_t K, int64_t tile_m, double* scores,
                               hipStream_t st) {
   const int64_t T_ = (M + tile_m - 1) / tile_m;
+  // blocks of 128 threads: on 4096 x 4096 (tile 128) that is 256 blocks, one
+  // per CU; measured 14.2 -> 12.0 us against 128 blocks of 256 threads (512
+  // blocks of 64 threads: 18.8 us)
   if (K % 4 == 0 && ldw % 4 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
-    hipLaunchKernelGGL(k_tvw_scores4, dim3(grid1d(T_ * (K / 4), 256)), dim3(256), 0, st, W, ldw, M, K, tile_m, scores);
+    hipLaunchKernelGGL(k_tvw_scores4, dim3(grid1d(T_ * (K / 4), 128)), dim3(128), 0, st, W, ldw, M, K, tile_m, scores);
   else
     hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, W, ldw, M, K, tile_m, scores);
 }
