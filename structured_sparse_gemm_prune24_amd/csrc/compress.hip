@@ -380,14 +380,15 @@ __global__ __launch_bounds__(256) void k_tvw_scores4(const float* __restrict__ W
 // TVW selection: one block per tile.  The kept set is the keep_k largest
 // scores, ties to the lower column.  Scores are non-negative fp64 sums with
 // one NaN pattern, so their bit patterns order like the values (NaN above
-// +Inf).  An MSB-first radix select (8
-// passes of 8 bits, a 256-bin histogram over the keys that still match the
-// prefix found so far) finds the keep_k-th largest key v and how many of the
+// +Inf).  An MSB-first radix select (up
+// to six passes of 11-bit digits, a 2048-bin histogram over the keys that
+// still match the prefix found so far) finds the keep_k-th largest key v and how many of the
 // keys equal to v are kept; a block-wide scan in column order then writes
 // every column with key > v and the first `need` columns with key == v.
 // --------------------------------------------------------------------------
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
+constexpr int SEL_DIGIT = 11;            // select digits: 11, 11, 11, 11, 11 and 9 bits from the top
 constexpr int64_t SEL_LDS_KEYS = 8192;   // 64 KiB of fp64 keys per block
 
 // Exclusive block-wide prefix of per-thread counts in thread order (blocks of
@@ -447,7 +448,8 @@ __device__ __forceinline__ bool find_cut(const uint32_t (&hb)[4], int64_t need, 
 __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __restrict__ scores, int64_t K,
                                                             int64_t keep_k, const int64_t* __restrict__ offsets,
                                                             int32_t* __restrict__ kept) {
-  __shared__ uint32_t hist[256];
+  constexpr int BINS = 1 << SEL_DIGIT, PER = BINS / SEL_THREADS;
+  __shared__ uint32_t hist[BINS];
   __shared__ uint32_t wave_sums[SEL_WAVES];
   __shared__ uint64_t sh_prefix;
   __shared__ int64_t sh_need;
@@ -472,10 +474,12 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
   }
   uint64_t prefix = 0;        // digits of the threshold found so far (high bits)
   int64_t need = keep_k;      // rank of the threshold among keys matching the prefix
-  for (int shift = 56; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += SEL_THREADS) hist[i] = 0u;
+  for (int top = 64; top > 0; top -= SEL_DIGIT) {
+    const int width = top < SEL_DIGIT ? top : SEL_DIGIT, shift = top - width;
+    for (int i = tid; i < BINS; i += SEL_THREADS) hist[i] = 0u;
     __syncthreads();
-    const uint64_t hi_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
+    const uint64_t hi_mask = top == 64 ? 0ull : (~0ull << top);
+    const uint32_t dmask = (1u << width) - 1u;
     // A tile's keys mostly share their high digits: when every matching key
     // of a wave has the same digit, one lane adds them all (one LDS address
     // hit by each lane in turn would serialise the wave).
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
       const int64_t k = k0 + tid;
       const uint64_t x = k < K ? key(k) : 0ull;
       const bool match = k < K && (x & hi_mask) == prefix;
-      const uint32_t d = (uint32_t)(x >> shift) & 255u;
+      const uint32_t d = (uint32_t)(x >> shift) & dmask;
       const uint64_t mm = __ballot(match);
       if (!mm) continue;                                    // wave-uniform
       const int l0 = __builtin_ffsll((long long)mm) - 1;
@@ -495,16 +499,47 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
       }
     }
     __syncthreads();
-    if (tid < 64) {
-      const uint32_t hb[4] = {hist[4 * tid], hist[4 * tid + 1], hist[4 * tid + 2], hist[4 * tid + 3]};
-      int d;
-      int64_t rest;
-      uint32_t bin;
-      if (find_cut(hb, need, tid, &d, &rest, &bin)) {
-        sh_prefix = prefix | ((uint64_t)d << shift);
-        sh_need = rest;
-        sh_whole = rest == (int64_t)bin ? 1u : 0u;
+    // Thread tid holds the digits [PER tid, PER tid + PER): a suffix sum over
+    // the threads (higher digits first: the lanes of a wave, then the waves)
+    // gives the count above them; the one thread whose digits hold the rank
+    // `need` walks them from the highest.
+    uint32_t hb[PER], own = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      hb[i] = hist[PER * tid + i];
+      own += hb[i];
+    }
+    const int lane = tid & 63, wv = tid >> 6;
+    uint32_t incl = own;
+#pragma unroll
+    for (int dd = 1; dd < 64; dd <<= 1) {
+      const uint32_t o = __shfl_down(incl, dd);
+      if (lane + dd < 64) incl += o;
+    }
+    if (lane == 0) wave_sums[wv] = incl;
+    __syncthreads();
+    int64_t above = (int64_t)incl - own;
+    for (int w = wv + 1; w < SEL_WAVES; ++w) above += wave_sums[w];
+    if (above < need && above + own >= need) {
+      int64_t a = above;
+      int dsel = PER * tid;
+      uint32_t bin = hb[0];
+      bool found = false;
+#pragma unroll
+      for (int i = PER - 1; i >= 0; --i) {
+        if (!found) {
+          if (a + hb[i] >= need) {
+            dsel = PER * tid + i;
+            bin = hb[i];
+            found = true;
+          } else {
+            a += hb[i];
+          }
+        }
       }
+      sh_prefix = prefix | ((uint64_t)dsel << shift);
+      sh_need = need - a;
+      sh_whole = need - a == (int64_t)bin ? 1u : 0u;
     }
     __syncthreads();
     prefix = sh_prefix;
