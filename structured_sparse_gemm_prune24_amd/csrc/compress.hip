@@ -598,7 +598,7 @@ struct VarSel {
   uint64_t prefix;        // the cut's digits found so far
   int64_t need;           // rank of the cut among the keys matching the prefix
   uint32_t ticket;        // blocks done in the current pass
-  uint32_t pad;
+  uint32_t done;          // a pass found the cut's bin kept whole: later passes do nothing
   uint32_t hist[BINS];    // digit histogram of the current pass
 };
 // 8-bit digits (the unstructured plan's four passes over 32-bit keys) and
@@ -617,7 +617,7 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_init(VarSel<BINS>* __restri
     vs->prefix = 0ull;
     vs->need = total_keep;
     vs->ticket = 0u;
-    vs->pad = 0u;
+    vs->done = 0u;
   }
 }
 
@@ -629,6 +629,9 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_radix(const uint64_t* __res
   __shared__ uint32_t h[BINS];
   __shared__ uint32_t wsum[NW];
   __shared__ uint32_t last;
+  // An earlier pass kept the cut's whole bin: the prefix found so far already
+  // separates the kept keys (every key >= it), so no digit is left to pick.
+  if (vs->done) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t prefix = vs->prefix;
   const int64_t need = vs->need;
@@ -687,12 +690,14 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_radix(const uint64_t* __res
   if (above < need && above + own >= need) {
     int64_t a = above;
     int dsel = PER * tid;
+    uint32_t bin = hb[0];
     bool found = false;
 #pragma unroll
     for (int i = PER - 1; i >= 0; --i) {
       if (!found) {
         if (a + hb[i] >= need) {
           dsel = PER * tid + i;
+          bin = hb[i];
           found = true;
         } else {
           a += hb[i];
@@ -700,7 +705,12 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_radix(const uint64_t* __res
       }
     }
     vs->prefix = prefix | ((uint64_t)dsel << shift);
-    vs->need = need - a;
+    // Every key of the cut's bin is kept: the kept keys are then those >= the
+    // bin's lowest value (the prefix, lower bits zero), i.e. the keys above it
+    // and all keys equal to it (need = n takes every equal key).
+    const bool whole = need - a == (int64_t)bin;
+    vs->need = whole ? n : need - a;
+    if (whole) vs->done = 1u;
   }
   __syncthreads();
 #pragma unroll
