@@ -1390,10 +1390,12 @@ static bool wide_gather(int64_t M, int64_t N) {
 // fragment bytes per MFMA than 2 x 4 waves of 64 x 128 (4096^3 TVW keep 2048:
 // 46.1 -> 45.2 us); at 256 wide the bytes are equal but half of the B reads
 // become A reads, which do not transpose (per-tile keep: 55.6 -> 54.4 us).
-// The dense (TW) blocks keep 2 x 4.
+// The dense (TW) blocks take 1 x 8 at 512 wide (TW keep 2048 63.2 -> 62.5 us,
+// keep 1024 37.8 -> 36.1 us) and keep 2 x 4 at 256 wide (per-tile keep TW
+// measured 2-3 % slower with 1 x 8).
 template <int AM, int XM, int BN>
 static p24_status launch_gather_bn(const GemmArgs& a, int32_t y_dtype, bool fused, int32_t act, hipStream_t st) {
-  constexpr int WM = AM == A_SPARSE ? 1 : 2, WN = 8 / WM;
+  constexpr int WM = AM == A_SPARSE || BN == 512 ? 1 : 2, WN = 8 / WM;
   if (!fused) return launch_cfg<128, BN, WM, WN, AM, XM, 0>(a, y_dtype, st);
   if (act == P24_ACT_GELU) return launch_cfg<128, BN, WM, WN, AM, XM, 2>(a, y_dtype, st);
   return launch_cfg<128, BN, WM, WN, AM, XM, 1>(a, y_dtype, st);
