@@ -753,14 +753,17 @@ __global__ __launch_bounds__(VAR_THREADS) void k_var_tile_counts(const uint64_t*
   }
 }
 
-// keep counts and their offsets; one block of SEL_THREADS
+// keep counts and their offsets; one block of SEL_THREADS.  With order given
+// (T <= SEL_THREADS: one tile per thread) also the order of the tiles, as
+// k_var_order computes it.
 __global__ __launch_bounds__(SEL_THREADS) void k_var_plan(int64_t T, int64_t K, const VarSelectW* __restrict__ vs,
                                                           const int32_t* __restrict__ gt,
                                                           const int32_t* __restrict__ eq,
-                                                          int64_t* __restrict__ offsets) {
+                                                          int64_t* __restrict__ offsets, int32_t* __restrict__ order) {
   __shared__ int64_t wave_sums[SEL_WAVES];
+  __shared__ int64_t sk[SEL_THREADS];
   const int64_t need = vs->need;
-  int64_t eq_base = 0, off_base = 0;
+  int64_t eq_base = 0, off_base = 0, my_keep = 0;
   for (int64_t t0 = 0; t0 < T; t0 += SEL_THREADS) {
     const int64_t t = t0 + threadIdx.x;
     const bool live = t < T;
@@ -777,8 +780,23 @@ __global__ __launch_bounds__(SEL_THREADS) void k_var_plan(int64_t T, int64_t K, 
     if (live) offsets[t] = off;
     eq_base += eq_total;
     off_base += keep_total;
+    my_keep = keep;
   }
   if (threadIdx.x == 0) offsets[T] = off_base;
+  if (order != nullptr) {
+    // rank r = the tiles with a larger count, or an equal count and a lower index
+    sk[threadIdx.x] = my_keep;
+    __syncthreads();
+    const int64_t t = threadIdx.x;
+    if (t < T) {
+      int64_t rank = 0;
+      for (int64_t u = 0; u < T; ++u) {
+        const int64_t cu = sk[u];
+        rank += (cu > my_keep || (cu == my_keep && u < t)) ? 1 : 0;
+      }
+      order[rank] = (int32_t)t;
+    }
+  }
 }
 
 // order[r] = the tile of rank r by keep count descending, then tile ascending
@@ -1319,10 +1337,13 @@ static p24_status launch_var_plan(const void* W, int64_t M, int64_t K, int64_t l
   }
   hipLaunchKernelGGL(k_var_tile_counts, dim3((unsigned)T_), dim3(VAR_THREADS), 0, st, (const uint64_t*)scores, K,
                      (const VarSelectW*)vs, gt, eq);
+  // up to SEL_THREADS tiles the plan kernel also orders them (one launch less)
+  const bool plan_orders = T_ <= SEL_THREADS;
   hipLaunchKernelGGL(k_var_plan, dim3(1), dim3(SEL_THREADS), 0, st, T_, K, (const VarSelectW*)vs,
-                     (const int32_t*)gt, (const int32_t*)eq, offsets);
-  hipLaunchKernelGGL(k_var_order, dim3(grid1d(T_, VAR_THREADS)), dim3(VAR_THREADS), 0, st,
-                     (const int64_t*)offsets, T_, order);
+                     (const int32_t*)gt, (const int32_t*)eq, offsets, plan_orders ? order : nullptr);
+  if (!plan_orders)
+    hipLaunchKernelGGL(k_var_order, dim3(grid1d(T_, VAR_THREADS)), dim3(VAR_THREADS), 0, st,
+                       (const int64_t*)offsets, T_, order);
   hipLaunchKernelGGL(k_tvw_select, dim3((unsigned)T_), dim3(SEL_THREADS), 0, st, (const double*)scores, K,
                      (int64_t)0, (const int64_t*)offsets, kept);
   return launch_status();
