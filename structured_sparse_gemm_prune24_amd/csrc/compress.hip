@@ -316,12 +316,47 @@ __global__ __launch_bounds__(256) void k_pack_dense(const uint16_t* __restrict__
 // their bit patterns, so every NaN score must carry the same bits (above
 // +Inf; NaN columns then tie and go to the lower index).
 // --------------------------------------------------------------------------
+// The state of a global radix select (the per-tile-keep cut, the
+// unstructured plan), kept in the caller's workspace between its launches.
+template <int BINS>
+struct VarSel {
+  uint64_t prefix;        // the cut's digits found so far
+  int64_t need;           // rank of the cut among the keys matching the prefix
+  uint32_t ticket;        // blocks done in the current pass
+  uint32_t done;          // a pass found the cut's bin kept whole: later passes do nothing
+  uint32_t hist[BINS];    // digit histogram of the current pass
+};
+// 8-bit digits (the unstructured plan's four passes over 32-bit keys) and
+// 11-bit digits (the per-tile-keep cut over 64-bit scores: six passes of
+// 11, 11, 11, 11, 11 and 9 bits instead of eight of 8; each pass is one launch)
+using VarSelect = VarSel<256>;
+constexpr int VAR_DIGIT = 11;
+using VarSelectW = VarSel<1 << VAR_DIGIT>;
+constexpr int VAR_THREADS = 256;
+constexpr int64_t VAR_STEP = 64;
+
+// A fresh select state, by the threads tid = 0 .. nthreads-1 of one block.
+template <int BINS>
+__device__ __forceinline__ void var_init(VarSel<BINS>* vs, int64_t total_keep, int tid, int nthreads) {
+  for (int i = tid; i < BINS; i += nthreads) vs->hist[i] = 0u;
+  if (tid == 0) {
+    vs->prefix = 0ull;
+    vs->need = total_keep;
+    vs->ticket = 0u;
+    vs->done = 0u;
+  }
+}
+
 __device__ __forceinline__ double canonical_score(double s) {
   return s != s ? __longlong_as_double(0x7FF8000000000000ll) : s;
 }
 
+// vs (optional): a per-tile-keep select state that block 0 initialises for the
+// digit passes that follow (one launch less).
 __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W, int64_t ldw, int64_t M,
-                                                    int64_t K, int64_t tile_m, double* __restrict__ scores) {
+                                                    int64_t K, int64_t tile_m, double* __restrict__ scores,
+                                                    VarSelectW* __restrict__ vs, int64_t total_keep) {
+  if (vs != nullptr && blockIdx.x == 0) var_init(vs, total_keep, (int)threadIdx.x, (int)blockDim.x);
   const int64_t T_ = (M + tile_m - 1) / tile_m;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= T_ * K) return;
@@ -344,7 +379,9 @@ __global__ __launch_bounds__(256) void k_tvw_scores(const float* __restrict__ W,
 // stride multiples of 4, W 16-byte aligned); each column's sum still runs
 // over its rows in order.
 __global__ __launch_bounds__(256) void k_tvw_scores4(const float* __restrict__ W, int64_t ldw, int64_t M,
-                                                     int64_t K, int64_t tile_m, double* __restrict__ scores) {
+                                                     int64_t K, int64_t tile_m, double* __restrict__ scores,
+                                                     VarSelectW* __restrict__ vs, int64_t total_keep) {
+  if (vs != nullptr && blockIdx.x == 0) var_init(vs, total_keep, (int)threadIdx.x, (int)blockDim.x);
   const int64_t T_ = (M + tile_m - 1) / tile_m, K4 = K / 4;
   const int64_t id = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (id >= T_ * K4) return;
@@ -594,31 +631,8 @@ __global__ __launch_bounds__(SEL_THREADS) void k_tvw_select(const double* __rest
 //     concatenated storage) and the order of the tiles by count, heaviest first.
 // --------------------------------------------------------------------------
 template <int BINS>
-struct VarSel {
-  uint64_t prefix;        // the cut's digits found so far
-  int64_t need;           // rank of the cut among the keys matching the prefix
-  uint32_t ticket;        // blocks done in the current pass
-  uint32_t done;          // a pass found the cut's bin kept whole: later passes do nothing
-  uint32_t hist[BINS];    // digit histogram of the current pass
-};
-// 8-bit digits (the unstructured plan's four passes over 32-bit keys) and
-// 11-bit digits (the per-tile-keep cut over 64-bit scores: six passes of
-// 11, 11, 11, 11, 11 and 9 bits instead of eight of 8; each pass is one launch)
-using VarSelect = VarSel<256>;
-constexpr int VAR_DIGIT = 11;
-using VarSelectW = VarSel<1 << VAR_DIGIT>;
-constexpr int VAR_THREADS = 256;
-constexpr int64_t VAR_STEP = 64;
-
-template <int BINS>
 __global__ __launch_bounds__(VAR_THREADS) void k_var_init(VarSel<BINS>* __restrict__ vs, int64_t total_keep) {
-  for (int i = threadIdx.x; i < BINS; i += VAR_THREADS) vs->hist[i] = 0u;
-  if (threadIdx.x == 0) {
-    vs->prefix = 0ull;
-    vs->need = total_keep;
-    vs->ticket = 0u;
-    vs->done = 0u;
-  }
+  var_init(vs, total_keep, (int)threadIdx.x, VAR_THREADS);
 }
 
 // One digit pass of the global cut: digit (x >> shift) & (2^width - 1) of the
@@ -1042,16 +1056,20 @@ using namespace p24;
 
 static inline unsigned grid1d(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
+// vs (optional): a per-tile-keep select state to initialise with need =
+// total_keep (the scores launch has at least one block).
 static void launch_tvw_scores(const float* W, int64_t ldw, int64_t M, int64_t K, int64_t tile_m, double* scores,
-                              hipStream_t st) {
+                              hipStream_t st, VarSelectW* vs = nullptr, int64_t total_keep = 0) {
   const int64_t T_ = (M + tile_m - 1) / tile_m;
   // blocks of 128 threads: on 4096 x 4096 (tile 128) that is 256 blocks, one
   // per CU; measured 14.2 -> 12.0 us against 128 blocks of 256 threads (512
   // blocks of 64 threads: 18.8 us)
   if (K % 4 == 0 && ldw % 4 == 0 && (reinterpret_cast<uintptr_t>(W) & 15) == 0)
-    hipLaunchKernelGGL(k_tvw_scores4, dim3(grid1d(T_ * (K / 4), 128)), dim3(128), 0, st, W, ldw, M, K, tile_m, scores);
+    hipLaunchKernelGGL(k_tvw_scores4, dim3(grid1d(T_ * (K / 4), 128)), dim3(128), 0, st, W, ldw, M, K, tile_m, scores,
+                       vs, total_keep);
   else
-    hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, W, ldw, M, K, tile_m, scores);
+    hipLaunchKernelGGL(k_tvw_scores, dim3(grid1d(T_ * K, 256)), dim3(256), 0, st, W, ldw, M, K, tile_m, scores, vs,
+                       total_keep);
 }
 
 extern "C" P24_API size_t prune24_values_bytes(int64_t M, int64_t K, int32_t layout) {
@@ -1324,8 +1342,7 @@ static p24_status launch_var_plan(const void* W, int64_t M, int64_t K, int64_t l
   int32_t* gt = (int32_t*)ws;
   int32_t* eq = gt + T_;
   const int64_t n = T_ * K;
-  launch_tvw_scores((const float*)W, ldw, M, K, 128, scores, st);
-  hipLaunchKernelGGL(k_var_init<1 << VAR_DIGIT>, dim3(1), dim3(VAR_THREADS), 0, st, vs, total_keep);
+  launch_tvw_scores((const float*)W, ldw, M, K, 128, scores, st, vs, total_keep);   // also initialises vs
   const int64_t per_block = (int64_t)VAR_THREADS * 8;
   const unsigned radix_blocks = (unsigned)std::min<int64_t>((n + per_block - 1) / per_block, 1024);
   // digits of 11 bits from the top (bits 53..63, 42..52, ...), the last one
