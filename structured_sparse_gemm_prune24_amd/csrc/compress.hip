@@ -417,11 +417,11 @@ __global__ __launch_bounds__(256) void k_tvw_scores4(const float* __restrict__ W
 // TVW selection: one block per tile.  The kept set is the keep_k largest
 // scores, ties to the lower column.  Scores are non-negative fp64 sums with
 // one NaN pattern, so their bit patterns order like the values (NaN above
-// +Inf).  An MSB-first radix select (up
-// to six passes of 11-bit digits, a 2048-bin histogram over the keys that
-// still match the prefix found so far) finds the keep_k-th largest key v and how many of the
-// keys equal to v are kept; a block-wide scan in column order then writes
-// every column with key > v and the first `need` columns with key == v.
+// +Inf).  An MSB-first radix select (up to six passes of 11-bit digits, a
+// 2048-bin histogram over the keys that still match the prefix found so far)
+// finds the keep_k-th largest key v and how many of the keys equal to v are
+// kept; a block-wide scan in column order then writes every column with
+// key > v and the first `need` columns with key == v.
 // --------------------------------------------------------------------------
 constexpr int SEL_THREADS = 1024;
 constexpr int SEL_WAVES = SEL_THREADS / 64;
